@@ -1,0 +1,211 @@
+"""Benchmark of the sparse / lazy Adam step on one MI355X.
+
+One step is the whole hot path over one batch of raw lookups:
+  coo_from_lookups  (radix sort, dedupe, duplicate sums)
+  csr_from_coo      (row_offsets over every table row, col_indices, touched rows)
+  sparse_adam_step  (DormancyDecay update of the touched coordinates)
+on the 10M x 128 float32 table (65,536 Zipf(1.05) lookups per step, last_step
+int32 per coordinate).  Inputs for every step are generated up front and are
+resident in HBM before the timed region starts.
+
+Prints one JSON line:  value = touched coordinates updated per second over the
+whole timed region (G/s); roofline = the update kernel's algorithmic bytes per
+launch / its mean duration (HIP events on the launch stream) against 8 TB/s;
+cpu_baseline = the CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "touched coords updated/sec (G/s) + achieved HBM GB/s % of peak, 10M x 128 table"
+HBM_PEAK_GBS = 8000.0
+# Algorithmic bytes of the DormancyDecay update: per touched coordinate read p, m, v,
+# last_step, g (20 B) and write p, m, v, last_step (16 B); per touched row read its id
+# (8 B) and two row offsets (8 B).
+BYTES_PER_COORD = 36
+BYTES_PER_ROW = 16
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="budget of the CPU-oracle sample (0 disables it)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB device copy (for scaling HBM counters)")
+    return ap.parse_args()
+
+
+def copy_probe(steps: int) -> None:
+    import torch
+
+    n = 1 << 28  # 1 GiB of float32
+    a = torch.ones(n, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": 4 * n, "copy_probe_bytes_written": 4 * n,
+                      "launches": steps}), flush=True)
+
+
+def cpu_baseline(w, host_p0, batches, budget_s: float):
+    """The oracle, as it stands, on the first steps of the same workload until the
+    time budget is spent (at least 2 steps); single thread."""
+    import numpy as np
+
+    import oracle
+
+    h = w.hyper
+    m = np.zeros((w.rows, w.cols), np.float32)       # zero pages are mapped lazily
+    v = np.zeros((w.rows, w.cols), np.float32)
+    ls = np.zeros((w.rows, w.cols), np.int32)
+    opt = oracle.Adam(host_p0, lr=h["lr"], beta1=h["beta1"], beta2=h["beta2"], eps=h["eps"],
+                      mode=w.mode, m=m, v=v, last_step=ls)
+    coords = 0
+    steps = 0
+    t0 = time.perf_counter()
+    for ids, grads in batches:
+        keys, sums, _ = oracle.coo_from_lookups(ids, grads, w.rows)
+        ro, ci, cv = oracle.csr_from_coo(keys, sums, w.rows, w.cols, w.rows, w.cols)
+        opt.step_csr(ro, ci, cv)
+        coords += keys.size * w.cols
+        steps += 1
+        if steps >= 2 and time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": coords / dt / 1e9, "unit": "G touched coords/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"first {steps} steps of the same workload (whole step: canonicalise, CSR, "
+                      f"update; {coords} touched coords in {dt:.2f} s, one thread)"}
+
+
+def main() -> int:
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the sparse step is built and timed on a single "
+              "MI355X; run it with --gpus 1", file=sys.stderr, flush=True)
+        return 2
+
+    import numpy as np
+    import torch
+
+    if args.copy_probe:
+        copy_probe(args.warmup + args.steps)
+        return 0
+
+    import lazy_optimizer_step_amd as L
+    import synth
+
+    torch.cuda.set_device(0)
+    w = synth.WORKLOADS[3]
+    R, Cc, n = w.rows, w.cols, w.n_lookups
+    K, W = args.steps, args.warmup
+    h = w.hyper
+
+    log(f"initial table {R}x{Cc} float32 (N(0, {w.init_std}))")
+    host_p0 = synth.init_params(w)
+    params = torch.from_numpy(host_p0).to("cuda")
+    opt = L.SparseAdam(params, lr=h["lr"], beta1=h["beta1"], beta2=h["beta2"], eps=h["eps"],
+                       mode=w.mode)
+    log(f"inputs of {W + K} steps ({n} lookups each)")
+    batches = synth.lookups_many(w, range(W + K))
+    ids_d = [torch.from_numpy(i).to("cuda") for i, _ in batches]
+    grads_d = [torch.from_numpy(g).to("cuda") for _, g in batches]
+
+    keys = torch.empty(n, dtype=torch.int64, device="cuda")
+    sums = torch.empty((n, Cc), dtype=torch.float32, device="cuda")
+    counts = torch.empty(n, dtype=torch.int32, device="cuda")
+    nuniq = torch.zeros(W + K, dtype=torch.int64, device="cuda")
+    ws = torch.empty(L.sparse_opt_workspace_size(n, Cc, R), dtype=torch.uint8, device="cuda")
+    row_offsets = torch.empty(R + 1, dtype=torch.int32, device="cuda")
+    col_indices = torch.empty(n * Cc, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(W + K)]
+
+    def step(s: int) -> None:
+        e = ev[s]
+        e[0].record(stream)
+        L.coo_from_lookups(ids_d[s], grads_d[s], R, out_keys=keys, out_vals=sums,
+                           out_counts=counts, d_nunique=nuniq[s:s + 1], workspace=ws,
+                           stream=stream)
+        e[1].record(stream)
+        coo = L.CooGradient(keys, sums, dim=R, width=Cc, nnz=n, d_nnz=nuniq[s:s + 1])
+        csr = L.csr_from_coo(coo, R, Cc, row_offsets=row_offsets, col_indices=col_indices,
+                             copy_values=False, stream=stream)
+        e[2].record(stream)
+        opt.step(csr, stream=stream)
+        e[3].record(stream)
+
+    log(f"warmup {W} steps")
+    for s in range(W):
+        step(s)
+    torch.cuda.synchronize()
+    log(f"timed {K} steps")
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for s in range(W, W + K):
+        step(s)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+
+    U = nuniq.cpu().numpy()[W:]
+    coords = int(U.sum()) * Cc
+    canon = np.array([ev[s][0].elapsed_time(ev[s][1]) for s in range(W, W + K)])
+    csr_t = np.array([ev[s][1].elapsed_time(ev[s][2]) for s in range(W, W + K)])
+    upd = np.array([ev[s][2].elapsed_time(ev[s][3]) for s in range(W, W + K)])
+    upd_bytes = BYTES_PER_COORD * U * Cc + BYTES_PER_ROW * U
+    achieved = float((upd_bytes / (upd * 1e-3)).mean() / 1e9)
+
+    result = {
+        "metric": METRIC,
+        "value": coords / (total_ms * 1e-3) / 1e9,
+        "unit": "G touched coords/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": total_ms / K,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "rows": R, "cols": Cc, "lookups_per_step": n,
+                   "zipf_s": w.zipf_s, "mode": w.mode, "state": "p,m,v float32 + last_step int32",
+                   "mean_unique_rows": float(U.mean())},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "k_update_rows<AdamOp<DormancyDecay>, SrcCsrTouched, 32>",
+                     "mean_us": float(upd.mean() * 1e3),
+                     "coords_per_s_G": float((U * Cc / (upd * 1e-3)).mean() / 1e9)},
+        "breakdown_us": {"coo_from_lookups": float(np.median(canon) * 1e3),
+                         "csr_from_coo": float(np.median(csr_t) * 1e3),
+                         "sparse_adam_step": float(np.median(upd) * 1e3)},
+    }
+    if args.cpu_seconds > 0:
+        log("cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline(w, host_p0, batches, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

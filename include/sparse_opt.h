@@ -1,0 +1,259 @@
+/*
+ * sparse_opt.h - C ABI of the MI355X (gfx950) sparse / lazy optimizer step.
+ *
+ * What the library computes (page "optirs_gpu::sparse_optimizer", docs.rs):
+ *   - section "Sparse gradient representations": a COO gradient keeps its
+ *     indices strictly ascending; a CSR gradient keeps row_offsets, and
+ *     strictly ascending col_indices within each row, with the dense shape;
+ *     CSR of shape (r, c) and COO over dim = r*c convert losslessly through
+ *     linear = row*c + col;
+ *   - section "Sparse SGD": params[i] -= lr * grad[i] on touched coordinates
+ *     only, with optional coupled weight decay and momentum applied lazily;
+ *   - sections "LazyAdamMode::Lazy" and "LazyAdamMode::DormancyDecay": per
+ *     coordinate m, v and last_step; Lazy decays once per touch, DormancyDecay
+ *     by beta^gap with gap = t - last_step; both bias-correct with the global
+ *     step t (the number of step calls so far) and apply
+ *     p -= lr * m_hat / (sqrt(v_hat) + eps).
+ * Untouched coordinates are never read or written, so they stay bit-identical.
+ * From the DiskSparseAdam README (page 2), where page 1 is silent: duplicate
+ * lookups are summed and emitted in ascending order ("Safe Duplicate
+ * Aggregation & Sorted I/O"); out-of-range indices, wrong shapes and
+ * non-finite gradients are errors ("Validated Inputs"; step() method).
+ *
+ * Conventions for every entry point:
+ *   - Pointers named d_* or documented as "device" are HIP device pointers
+ *     (e.g. torch tensor data_ptr()); the caller allocates and owns all of
+ *     them, including state, outputs and workspace.  The library's only
+ *     device allocation is a 256-byte status block per device, made by the
+ *     first SPOPT_VALIDATE call on that device and kept until the process
+ *     ends; validated calls are serialised process-wide around it.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream) on
+ *     the calling thread's current device.  All device work is enqueued on
+ *     it; calls return before it finishes unless SPOPT_VALIDATE is set, in
+ *     which case they synchronise on `stream` once.
+ *   - Return value: SPOPT_OK (0) or a negative spopt_status.  No exception
+ *     crosses the ABI.  sparse_opt_last_error() gives a message for the
+ *     calling thread's most recent failure.
+ *   - A call that returns an error has enqueued no kernel that writes an
+ *     output or state array, with one documented exception: in trusted mode
+ *     coo_from_lookups cannot see device-side errors, so it marks its result
+ *     empty instead (see there).
+ *   - Layouts are row-major and contiguous; float arrays whose width is a
+ *     multiple of 4 take 16-byte vector loads when their base is 16-byte
+ *     aligned (torch allocations are), and a scalar path otherwise.
+ */
+#ifndef SPARSE_OPT_H
+#define SPARSE_OPT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Only the entry points below are exported from the shared library. */
+#define SPOPT_API __attribute__((visibility("default")))
+
+/* ---- status codes ------------------------------------------------------- */
+typedef enum spopt_status {
+    SPOPT_OK = 0,
+    SPOPT_EINVAL = -1,      /* bad argument: NULL pointer, size, hyper-parameter, step */
+    SPOPT_ERANGE = -2,      /* an index outside its range */
+    SPOPT_ENOTCANON = -3,   /* indices not strictly ascending / CSR not canonical */
+    SPOPT_ESHAPE = -4,      /* gradient shape does not match the state */
+    SPOPT_ENONFINITE = -5,  /* a gradient value is NaN or infinite (SPOPT_VALIDATE) */
+    SPOPT_EOVERFLOW = -6,   /* a count does not fit its index type */
+    SPOPT_EWORKSPACE = -7,  /* workspace missing or too small */
+    SPOPT_EDEVICE = -8      /* a HIP runtime call failed */
+} spopt_status;
+
+/* ---- flags -------------------------------------------------------------- */
+#define SPOPT_TRUSTED 0u   /* no checks beyond bounds guards, no host synchronisation */
+#define SPOPT_VALIDATE 1u  /* full input checks on the device, one synchronisation,
+                              and a rejected call writes nothing */
+
+/* ---- optimizer kinds and configuration ---------------------------------- */
+#define SPOPT_KIND_ADAM 0
+#define SPOPT_KIND_SGD 1
+
+#define SPOPT_MODE_LAZY 0      /* LazyAdamMode::Lazy */
+#define SPOPT_MODE_DORMANCY 1  /* LazyAdamMode::DormancyDecay */
+
+/* Sparse / lazy Adam.  lr >= 0, beta1 and beta2 in [0, 1), eps > 0 (ranges of
+ * the DiskSparseAdam API reference; lr >= 0 is this library's own rule).
+ * Doubles: every derived scalar (1 - beta, bias corrections, log2 beta) is
+ * formed in double on the host and rounded once. */
+typedef struct spopt_adam_config {
+    double lr, beta1, beta2, eps;
+    int32_t mode; /* SPOPT_MODE_LAZY or SPOPT_MODE_DORMANCY */
+} spopt_adam_config;
+
+/* Sparse SGD.  lr >= 0, momentum in [0, 1), weight_decay >= 0.  Coupled weight
+ * decay: g' = g + weight_decay * p.  momentum != 0: b = momentum * b + g',
+ * p -= lr * b (heavy ball, no dampening); momentum == 0: p -= lr * g'. */
+typedef struct spopt_sgd_config {
+    double lr, momentum, weight_decay;
+} spopt_sgd_config;
+
+/* ---- gradients ---------------------------------------------------------- */
+
+/* COO gradient over a dense (dim x width) object: entry k covers coordinates
+ * indices[k]*width + j for j < width, with values[k*width + j].
+ *   width == 1: P1's CooGradient (a 1-D vector, or the rows*cols flattened
+ *               view of a table);
+ *   width == cols of a table: indices are row ids and every entry is a full
+ *               row (the compact form of a CSR whose touched rows are full).
+ * indices strictly ascending in [0, dim).
+ * The entry count is nnz, or, when d_nnz != NULL, the device value *d_nnz
+ * (which must be <= nnz; nnz is then the upper bound used to size launches).
+ */
+typedef struct spopt_coo {
+    int64_t dim;
+    int64_t width;
+    int64_t nnz;
+    const int64_t* d_nnz;   /* device, optional */
+    const int64_t* indices; /* device [nnz] */
+    const float* values;    /* device [nnz * width] */
+} spopt_coo;
+
+/* CSR gradient of shape rows x cols: row r holds entries
+ * [row_offsets[r], row_offsets[r+1]) with columns col_indices[..] strictly
+ * ascending in [0, cols); row_offsets[0] == 0, nondecreasing.
+ * col_indices may be NULL when every non-empty row is full (its columns are
+ * then 0..cols-1 in order, which is the only canonical full row).
+ * touched_rows (optional): the ascending ids of all rows with at least one
+ * entry, n_touched of them (or *d_n_touched when that is given, <= n_touched).
+ * Without it the update scans row_offsets over all rows. */
+typedef struct spopt_csr {
+    int64_t rows, cols;
+    const int32_t* row_offsets;  /* device [rows + 1] */
+    const int32_t* col_indices;  /* device [nnz] or NULL (full rows) */
+    const float* values;         /* device [nnz] */
+    const int64_t* touched_rows; /* device [n_touched], optional */
+    int64_t n_touched;
+    const int64_t* d_n_touched;  /* device, optional */
+} spopt_csr;
+
+#define SPOPT_FORMAT_COO 0
+#define SPOPT_FORMAT_CSR 1
+
+typedef struct spopt_grad {
+    int32_t format; /* SPOPT_FORMAT_COO or SPOPT_FORMAT_CSR */
+    spopt_coo coo;
+    spopt_csr csr;
+} spopt_grad;
+
+/* ---- optimizer handle --------------------------------------------------- */
+typedef struct spopt_optimizer* spopt_t;
+
+/* Create an optimizer over caller-owned device state of shape rows x cols
+ * (cols == 1 for a 1-D vector), all contiguous:
+ *   params        float [rows*cols]
+ *   m_or_momentum float [rows*cols] (Adam m; SGD momentum buffer, may be NULL
+ *                 when momentum == 0)
+ *   v             float [rows*cols] (Adam only; NULL for SGD)
+ *   last_step     int32 [rows*cols] (Adam only; NULL for SGD)
+ * The caller initialises m = v = momentum = 0 and last_step = 0 before the
+ * first step (the reading that makes the first touch at global step t a gap
+ * of t).  config points at spopt_adam_config or spopt_sgd_config (copied).
+ * The handle owns the config and the global step counter t, starting at 0.
+ * Errors: SPOPT_EINVAL (NULL, bad kind, rows*cols <= 0, hyper-parameter out of
+ * range), SPOPT_EDEVICE. */
+SPOPT_API int sparse_opt_create(spopt_t* out, int32_t kind, const void* config, int64_t rows, int64_t cols,
+                      float* params, float* m_or_momentum, float* v, int32_t* last_step);
+SPOPT_API void sparse_opt_destroy(spopt_t h);
+
+/* Global step counter (number of successful step calls so far). */
+SPOPT_API int64_t sparse_opt_get_step(spopt_t h);
+/* Set t, e.g. to resume from a checkpoint of the state arrays.  0 <= t <
+ * 2^31 (last_step is int32).  SPOPT_EINVAL otherwise. */
+SPOPT_API int sparse_opt_set_step(spopt_t h, int64_t t);
+
+/* Message of the calling thread's last failure ("" if none). */
+SPOPT_API const char* sparse_opt_last_error(void);
+
+/* ---- canonicalisation --------------------------------------------------- */
+
+/* Bytes of device workspace coo_from_lookups needs for n lookups of `width`
+ * values over keys in [0, key_space).  SPOPT_EINVAL for n < 0, width < 1,
+ * key_space < 1, or key and position bits together above 64. */
+SPOPT_API int sparse_opt_workspace_size(int64_t n, int64_t width, int64_t key_space, size_t* bytes);
+
+/* Raw lookups -> canonical COO (DiskSparseAdam "Safe Duplicate Aggregation &
+ * Sorted I/O"; P1 canonical COO).
+ *   ids        device int64 [n], each in [0, key_space)
+ *   vals       device float [n * width], row i belongs to ids[i]
+ *   out_keys   device int64 [n]: the U distinct ids, strictly ascending
+ *   out_vals   device float [n * width]: row k = sum of the rows of all
+ *              lookups of out_keys[k]; summation in float32 in a fixed order
+ *              (deterministic run to run), not necessarily lookup order
+ *   out_counts device int32 [n]: multiplicity of out_keys[k]
+ *   d_nunique  device int64 [1]: U
+ * Entries k >= U of the outputs are unspecified.  A key whose values sum to
+ * zero is kept (present means touched).
+ * width == 1 gives a 1-D CooGradient; width == cols with key_space == rows
+ * gives full table rows.
+ * Workspace: device, at least sparse_opt_workspace_size(n, width, key_space).
+ * Errors: SPOPT_EINVAL, SPOPT_EWORKSPACE, SPOPT_EOVERFLOW (n >= 2^31);
+ * with SPOPT_VALIDATE also SPOPT_ERANGE (an id outside [0, key_space)) and
+ * SPOPT_ENONFINITE.  In trusted mode an out-of-range id is still detected on
+ * the device; the call then sets *d_nunique = 0 (an empty gradient) and
+ * writes no other output. */
+SPOPT_API int coo_from_lookups(const int64_t* ids, const float* vals, int64_t n, int64_t width,
+                     int64_t key_space, int64_t* out_keys, float* out_vals, int32_t* out_counts,
+                     int64_t* d_nunique, void* workspace, size_t workspace_bytes, void* stream,
+                     uint32_t flags);
+
+/* ---- COO <-> CSR (P1 CsrGradient::from_coo / to_coo) -------------------- */
+
+/* Canonical COO -> CSR of shape rows x cols.
+ *   in->width == 1:    in->dim must be rows*cols; row = idx / cols,
+ *                      col = idx % cols.
+ *   in->width == cols: in->dim must be rows; entries are full rows.
+ *   row_offsets device int32 [rows + 1] (required)
+ *   col_indices device int32 [nnz*width] or NULL (only for width == cols:
+ *               full rows, columns implicit)
+ *   values      device float [nnz*width] or NULL to skip the copy (the CSR
+ *               values then ARE in->values, which has the same layout)
+ *   touched_rows device int64 [nnz] or NULL; width == cols only: the touched
+ *               row ids (a copy of in->indices); d_n_touched (device int64,
+ *               or NULL) receives their count.
+ * nnz is read on the device from in->d_nnz when given.
+ * Errors: SPOPT_EINVAL, SPOPT_ESHAPE, SPOPT_EOVERFLOW (nnz*width >= 2^31);
+ * with SPOPT_VALIDATE also SPOPT_ERANGE and SPOPT_ENOTCANON. */
+SPOPT_API int csr_from_coo(const spopt_coo* in, int64_t rows, int64_t cols, int32_t* row_offsets,
+                 int32_t* col_indices, float* values, int64_t* touched_rows,
+                 int64_t* d_n_touched, void* stream, uint32_t flags);
+
+/* CSR -> COO over the flattened rows*cols view: idx[j] = row*cols + col[j],
+ * values copied (already ascending, so canonical).
+ *   out_indices device int64 [nnz], out_values device float [nnz] or NULL.
+ * Errors: SPOPT_EINVAL; with SPOPT_VALIDATE also SPOPT_ENOTCANON, SPOPT_ERANGE. */
+SPOPT_API int csr_to_coo(const spopt_csr* in, int64_t* out_indices, float* out_values, void* stream,
+               uint32_t flags);
+
+/* ---- optimizer steps ---------------------------------------------------- */
+
+/* One sparse / lazy Adam step: t += 1, then every touched coordinate i is
+ * updated (Lazy or DormancyDecay per the handle's config) and
+ * last_step[i] = t.  Nothing else is read or written.  An empty gradient
+ * still advances t (t counts step calls).
+ * COO gradients: width == 1 with dim == rows*cols, or width == cols with
+ * dim == rows.  CSR gradients: rows and cols equal the handle's.
+ * Errors: SPOPT_EINVAL (NULL, wrong kind, t would reach 2^31), SPOPT_ESHAPE;
+ * with SPOPT_VALIDATE also SPOPT_ERANGE, SPOPT_ENOTCANON, SPOPT_ENONFINITE,
+ * and SPOPT_EINVAL when a touched coordinate has last_step >= t.  A rejected
+ * step writes nothing and leaves t unchanged.  In trusted mode indices outside
+ * the state are skipped, never dereferenced. */
+SPOPT_API int sparse_adam_step(spopt_t h, const spopt_grad* g, void* stream, uint32_t flags);
+
+/* One sparse SGD step on the touched coordinates (same gradient forms and
+ * error rules as sparse_adam_step).  t advances as well. */
+SPOPT_API int sparse_sgd_step(spopt_t h, const spopt_grad* g, void* stream, uint32_t flags);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_OPT_H */

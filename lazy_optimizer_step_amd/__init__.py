@@ -1,0 +1,306 @@
+"""MI355X-native sparse / lazy optimizer step (Python binding of libsparseopt.so).
+
+The functions below carry the C ABI's names (include/sparse_opt.h) and only
+marshal arguments: they check dtypes, devices and contiguity, allocate
+outputs with torch when none are given, and call the library on torch's
+current stream.  All arithmetic runs in the library's HIP kernels.
+
+Pages followed (see the header for the full contract): the optirs_gpu
+sparse_optimizer module page (COO/CSR gradients, sparse SGD, Lazy and
+DormancyDecay Adam with global-step bias correction) and, where it is silent,
+the DiskSparseAdam README (duplicates summed and sorted, validated inputs).
+"""
+from __future__ import annotations
+
+import ctypes as C
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+from ._lib import (FORMAT_COO, FORMAT_CSR, KIND_ADAM, KIND_SGD, MODE_DORMANCY, MODE_LAZY, TRUSTED,
+                   VALIDATE, SparseOptError, check)
+
+__all__ = ["coo_from_lookups", "csr_from_coo", "csr_to_coo", "sparse_opt_workspace_size",
+           "sparse_opt_create", "sparse_adam_step", "sparse_sgd_step", "CooGradient",
+           "CsrGradient", "SparseAdam", "SparseSgd", "SparseOptError", "TRUSTED", "VALIDATE"]
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _need(t, dtype, name, numel=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a ROCm device")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs {numel}")
+    return t
+
+
+def _flags(validate: bool) -> int:
+    return VALIDATE if validate else TRUSTED
+
+
+# ---------------------------------------------------------------------------
+# Gradients
+# ---------------------------------------------------------------------------
+
+@dataclass
+class CooGradient:
+    """COO gradient over a dense (dim x width) object; see spopt_coo.
+
+    nnz is the entry count, or an upper bound when d_nnz (a device int64[1])
+    holds the count."""
+    indices: torch.Tensor
+    values: torch.Tensor
+    dim: int
+    width: int = 1
+    nnz: int | None = None
+    d_nnz: torch.Tensor | None = None
+
+    def _c(self) -> _lib.Coo:
+        nnz = self.indices.numel() if self.nnz is None else self.nnz
+        _need(self.indices, torch.int64, "indices", nnz)
+        _need(self.values, torch.float32, "values", nnz * self.width)
+        if self.d_nnz is not None:
+            _need(self.d_nnz, torch.int64, "d_nnz", 1)
+        return _lib.Coo(self.dim, self.width, nnz, _ptr(self.d_nnz), _ptr(self.indices),
+                        _ptr(self.values))
+
+
+@dataclass
+class CsrGradient:
+    """CSR gradient of shape rows x cols; see spopt_csr."""
+    row_offsets: torch.Tensor
+    col_indices: torch.Tensor | None
+    values: torch.Tensor
+    rows: int
+    cols: int
+    touched_rows: torch.Tensor | None = None
+    n_touched: int | None = None
+    d_n_touched: torch.Tensor | None = None
+
+    def _c(self) -> _lib.Csr:
+        _need(self.row_offsets, torch.int32, "row_offsets", self.rows + 1)
+        if self.col_indices is not None:
+            _need(self.col_indices, torch.int32, "col_indices")
+        _need(self.values, torch.float32, "values")
+        n_touched = 0
+        if self.touched_rows is not None:
+            _need(self.touched_rows, torch.int64, "touched_rows")
+            n_touched = self.touched_rows.numel() if self.n_touched is None else self.n_touched
+        if self.d_n_touched is not None:
+            _need(self.d_n_touched, torch.int64, "d_n_touched", 1)
+        return _lib.Csr(self.rows, self.cols, _ptr(self.row_offsets), _ptr(self.col_indices),
+                        _ptr(self.values), _ptr(self.touched_rows), n_touched,
+                        _ptr(self.d_n_touched))
+
+
+def _grad(g) -> _lib.Grad:
+    if isinstance(g, CooGradient):
+        return _lib.Grad(FORMAT_COO, g._c(), _lib.Csr())
+    if isinstance(g, CsrGradient):
+        return _lib.Grad(FORMAT_CSR, _lib.Coo(), g._c())
+    raise TypeError("gradient must be a CooGradient or a CsrGradient")
+
+
+# ---------------------------------------------------------------------------
+# Canonicalisation and conversions
+# ---------------------------------------------------------------------------
+
+def sparse_opt_workspace_size(n: int, width: int, key_space: int) -> int:
+    out = C.c_size_t(0)
+    check(_lib.lib().sparse_opt_workspace_size(n, width, key_space, C.byref(out)))
+    return out.value
+
+
+def coo_from_lookups(ids: torch.Tensor, vals: torch.Tensor, key_space: int, *, out_keys=None,
+                     out_vals=None, out_counts=None, d_nunique=None, workspace=None,
+                     stream=None, validate: bool = False):
+    """Raw lookups -> canonical COO.  Returns (keys, vals, counts, d_nunique), all
+    sized by the lookup count n; the first U = d_nunique entries are the result."""
+    n = ids.numel()
+    width = vals.numel() // n if n else (vals.shape[1] if vals.dim() == 2 else 1)
+    dev = ids.device
+    _need(ids, torch.int64, "ids")
+    _need(vals, torch.float32, "vals", n * width)
+    if out_keys is None:
+        out_keys = torch.empty(max(n, 1), dtype=torch.int64, device=dev)
+    if out_vals is None:
+        out_vals = torch.empty((max(n, 1), width), dtype=torch.float32, device=dev)
+    if out_counts is None:
+        out_counts = torch.empty(max(n, 1), dtype=torch.int32, device=dev)
+    if d_nunique is None:
+        d_nunique = torch.empty(1, dtype=torch.int64, device=dev)
+    need = sparse_opt_workspace_size(n, width, key_space)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _need(out_keys, torch.int64, "out_keys", n)
+    _need(out_vals, torch.float32, "out_vals", n * width)
+    _need(out_counts, torch.int32, "out_counts", n)
+    _need(d_nunique, torch.int64, "d_nunique", 1)
+    _need(workspace, torch.uint8, "workspace")
+    check(_lib.lib().coo_from_lookups(_ptr(ids), _ptr(vals), n, width, key_space, _ptr(out_keys),
+                                      _ptr(out_vals), _ptr(out_counts), _ptr(d_nunique),
+                                      _ptr(workspace), workspace.numel(), _stream(stream),
+                                      _flags(validate)))
+    return out_keys, out_vals, out_counts, d_nunique
+
+
+def csr_from_coo(coo: CooGradient, rows: int, cols: int, *, row_offsets=None, col_indices=None,
+                 values=None, touched_rows=None, d_n_touched=None, want_col_indices=True,
+                 copy_values=True, stream=None, validate: bool = False):
+    """Canonical COO -> CSR.  Returns a CsrGradient.  For a full-row COO the touched
+    rows are the COO's keys (no copy unless touched_rows is given), and values may
+    alias the COO's (copy_values=False)."""
+    c = coo._c()
+    dev = coo.indices.device
+    total = c.nnz * coo.width
+    if row_offsets is None:
+        row_offsets = torch.empty(rows + 1, dtype=torch.int32, device=dev)
+    _need(row_offsets, torch.int32, "row_offsets", rows + 1)
+    full = coo.width == cols and coo.width > 1
+    if col_indices is None and (want_col_indices or not full):
+        col_indices = torch.empty(max(total, 1), dtype=torch.int32, device=dev)
+    if col_indices is not None:
+        _need(col_indices, torch.int32, "col_indices", total)
+    if values is None:
+        values = torch.empty(max(total, 1), dtype=torch.float32, device=dev) if copy_values \
+            else coo.values
+    _need(values, torch.float32, "values", total)
+    tr, dn = touched_rows, d_n_touched
+    if full:
+        if tr is None:
+            tr = coo.indices
+        if dn is None and coo.d_nnz is not None:
+            dn = coo.d_nnz
+    check(_lib.lib().csr_from_coo(C.byref(c), rows, cols, _ptr(row_offsets), _ptr(col_indices),
+                                  _ptr(values), _ptr(tr) if full else None,
+                                  _ptr(dn) if full else None, _stream(stream), _flags(validate)))
+    return CsrGradient(row_offsets, col_indices, values, rows, cols,
+                       touched_rows=tr if full else None,
+                       n_touched=c.nnz if full else None, d_n_touched=dn if full else None)
+
+
+def csr_to_coo(csr: CsrGradient, *, out_indices=None, out_values=None, nnz: int | None = None,
+               stream=None, validate: bool = False) -> CooGradient:
+    """CSR -> COO over the flattened rows*cols view.  nnz (the entry count) is read
+    from row_offsets with a host copy when not given."""
+    c = csr._c()
+    dev = csr.row_offsets.device
+    if nnz is None:
+        nnz = int(csr.row_offsets[csr.rows].item())
+    if out_indices is None:
+        out_indices = torch.empty(max(nnz, 1), dtype=torch.int64, device=dev)
+    if out_values is None:
+        out_values = torch.empty(max(nnz, 1), dtype=torch.float32, device=dev)
+    _need(out_indices, torch.int64, "out_indices", nnz)
+    _need(out_values, torch.float32, "out_values", nnz)
+    check(_lib.lib().csr_to_coo(C.byref(c), _ptr(out_indices), _ptr(out_values), _stream(stream),
+                                _flags(validate)))
+    return CooGradient(out_indices, out_values, csr.rows * csr.cols, 1, nnz)
+
+
+# ---------------------------------------------------------------------------
+# Optimizer handles
+# ---------------------------------------------------------------------------
+
+class _Handle:
+    def __init__(self, kind, cfg, rows, cols, p, m, v, ls):
+        self._h = C.c_void_p()
+        check(_lib.lib().sparse_opt_create(C.byref(self._h), kind, C.byref(cfg), rows, cols,
+                                           _ptr(p), _ptr(m), _ptr(v), _ptr(ls)))
+        self._L = _lib.lib()
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            self._L.sparse_opt_destroy(h)
+            self._h = None
+
+    @property
+    def step_count(self) -> int:
+        return int(self._L.sparse_opt_get_step(self._h))
+
+    def set_step(self, t: int) -> None:
+        check(self._L.sparse_opt_set_step(self._h, t))
+
+
+def sparse_opt_create(kind: int, config, rows: int, cols: int, params, m_or_momentum=None, v=None,
+                      last_step=None) -> _Handle:
+    n = rows * cols
+    _need(params, torch.float32, "params", n)
+    for t, name, dt in ((m_or_momentum, "m_or_momentum", torch.float32), (v, "v", torch.float32),
+                        (last_step, "last_step", torch.int32)):
+        if t is not None:
+            _need(t, dt, name, n)
+    return _Handle(kind, config, rows, cols, params, m_or_momentum, v, last_step)
+
+
+def sparse_adam_step(h: _Handle, grad, *, stream=None, validate: bool = False) -> None:
+    g = _grad(grad)
+    check(h._L.sparse_adam_step(h._h, C.byref(g), _stream(stream), _flags(validate)))
+
+
+def sparse_sgd_step(h: _Handle, grad, *, stream=None, validate: bool = False) -> None:
+    g = _grad(grad)
+    check(h._L.sparse_sgd_step(h._h, C.byref(g), _stream(stream), _flags(validate)))
+
+
+class SparseAdam:
+    """Sparse / lazy Adam over a (rows x cols) float32 table that this object
+    allocates on the device (m = v = 0, last_step = 0)."""
+
+    def __init__(self, params: torch.Tensor, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8,
+                 mode="dormancy"):
+        self.params = params
+        self.rows = params.shape[0]
+        self.cols = params.shape[1] if params.dim() == 2 else 1
+        self.m = torch.zeros_like(params)
+        self.v = torch.zeros_like(params)
+        self.last_step = torch.zeros(params.shape, dtype=torch.int32, device=params.device)
+        cfg = _lib.AdamConfig(lr, beta1, beta2, eps, MODE_DORMANCY if mode == "dormancy" else MODE_LAZY)
+        self.handle = sparse_opt_create(KIND_ADAM, cfg, self.rows, self.cols, params, self.m, self.v,
+                                        self.last_step)
+
+    @property
+    def t(self) -> int:
+        return self.handle.step_count
+
+    def step(self, grad, *, stream=None, validate=False) -> None:
+        sparse_adam_step(self.handle, grad, stream=stream, validate=validate)
+
+
+class SparseSgd:
+    """Sparse SGD (coupled weight decay, lazy momentum) over a float32 table."""
+
+    def __init__(self, params: torch.Tensor, lr, momentum=0.0, weight_decay=0.0):
+        self.params = params
+        self.rows = params.shape[0]
+        self.cols = params.shape[1] if params.dim() == 2 else 1
+        self.momentum_buf = torch.zeros_like(params) if momentum != 0.0 else None
+        cfg = _lib.SgdConfig(lr, momentum, weight_decay)
+        self.handle = sparse_opt_create(KIND_SGD, cfg, self.rows, self.cols, params,
+                                        self.momentum_buf)
+
+    @property
+    def t(self) -> int:
+        return self.handle.step_count
+
+    def step(self, grad, *, stream=None, validate=False) -> None:
+        sparse_sgd_step(self.handle, grad, stream=stream, validate=validate)

@@ -1,0 +1,259 @@
+// abi.cpp - the optimizer handle, error reporting and the step entry points of
+// the C ABI declared in sparse_opt.h.
+//
+// The handle holds the configuration and the global step t (optirs_gpu
+// sparse_optimizer page: bias correction uses the number of step calls so
+// far, never a per-coordinate count).  Each step computes, in double, the
+// scalars that depend only on t and the hyper-parameters and rounds each once
+// to float for the kernels.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <vector>
+
+#include "common.hpp"
+
+namespace spopt {
+
+
+static thread_local char g_err[512];
+
+void set_error(const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+}
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int status_to_code(uint32_t bits, const char* what) {
+    if (bits & kStatusRange) return fail(SPOPT_ERANGE, "%s: index out of range", what);
+    if (bits & (kStatusNotCanon | kStatusTouched))
+        return fail(SPOPT_ENOTCANON, "%s: gradient is not in canonical form", what);
+    if (bits & kStatusNonFinite) return fail(SPOPT_ENONFINITE, "%s: non-finite gradient", what);
+    if (bits & kStatusStep)
+        return fail(SPOPT_EINVAL, "%s: a touched coordinate has last_step >= t", what);
+    return fail(SPOPT_EINVAL, "%s: status 0x%x", what, bits);
+}
+
+std::mutex& validation_mutex() {
+    static std::mutex m;
+    return m;
+}
+
+// One 4-word status block per device, allocated on first use and kept.
+uint32_t* device_status_block() {
+    static std::vector<uint32_t*> blocks;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return nullptr;
+    if ((size_t)dev >= blocks.size()) blocks.resize((size_t)dev + 1, nullptr);
+    if (blocks[(size_t)dev] == nullptr) {
+        void* p = nullptr;
+        if (hipMalloc(&p, 256) != hipSuccess) return nullptr;
+        blocks[(size_t)dev] = (uint32_t*)p;
+    }
+    return blocks[(size_t)dev];
+}
+
+int device_status_check(uint32_t* d_status, hipStream_t s, bool check_touched,
+                        const char* what) {
+    uint32_t h[4] = {0, 0, 0, 0};
+    SPOPT_HIP(hipMemcpyAsync(h, d_status, sizeof h, hipMemcpyDeviceToHost, s));
+    SPOPT_HIP(hipStreamSynchronize(s));
+    if (h[0] != 0u) return status_to_code(h[0], what);
+    if (check_touched && h[1] != h[2])
+        return fail(SPOPT_ENOTCANON, "%s: touched-row list has %u rows, row_offsets %u", what,
+                    h[2], h[1]);
+    return SPOPT_OK;
+}
+
+}  // namespace spopt
+
+using namespace spopt;
+
+struct spopt_optimizer {
+    int32_t kind;
+    spopt_adam_config adam;
+    spopt_sgd_config sgd;
+    int64_t rows, cols;
+    float* p;
+    float* m;  // Adam m, or SGD momentum buffer
+    float* v;
+    int32_t* ls;
+    int64_t t;
+};
+
+static int check_adam_config(const spopt_adam_config* c) {
+    if (!(c->lr >= 0.0) || !isfinite(c->lr))
+        return fail(SPOPT_EINVAL, "adam config: lr must be finite and >= 0");
+    if (!(c->beta1 >= 0.0 && c->beta1 < 1.0) || !(c->beta2 >= 0.0 && c->beta2 < 1.0))
+        return fail(SPOPT_EINVAL, "adam config: beta1 and beta2 must lie in [0, 1)");
+    if (!(c->eps > 0.0) || !isfinite(c->eps))
+        return fail(SPOPT_EINVAL, "adam config: eps must be finite and > 0");
+    if (c->mode != SPOPT_MODE_LAZY && c->mode != SPOPT_MODE_DORMANCY)
+        return fail(SPOPT_EINVAL, "adam config: unknown mode %d", c->mode);
+    return SPOPT_OK;
+}
+
+static int check_sgd_config(const spopt_sgd_config* c) {
+    if (!(c->lr >= 0.0) || !isfinite(c->lr))
+        return fail(SPOPT_EINVAL, "sgd config: lr must be finite and >= 0");
+    if (!(c->momentum >= 0.0 && c->momentum < 1.0))
+        return fail(SPOPT_EINVAL, "sgd config: momentum must lie in [0, 1)");
+    if (!(c->weight_decay >= 0.0) || !isfinite(c->weight_decay))
+        return fail(SPOPT_EINVAL, "sgd config: weight_decay must be finite and >= 0");
+    return SPOPT_OK;
+}
+
+extern "C" const char* sparse_opt_last_error(void) { return g_err; }
+
+extern "C" int sparse_opt_create(spopt_t* out, int32_t kind, const void* config, int64_t rows,
+                                 int64_t cols, float* params, float* m_or_momentum, float* v,
+                                 int32_t* last_step) {
+    if (out == nullptr || config == nullptr || params == nullptr)
+        return fail(SPOPT_EINVAL, "create: NULL argument");
+    *out = nullptr;
+    if (rows < 1 || cols < 1 || rows > INT64_MAX / cols)
+        return fail(SPOPT_EINVAL, "create: bad shape %lld x %lld", (long long)rows,
+                    (long long)cols);
+    spopt_optimizer h{};
+    h.kind = kind;
+    h.rows = rows;
+    h.cols = cols;
+    h.p = params;
+    h.m = m_or_momentum;
+    h.v = v;
+    h.ls = last_step;
+    h.t = 0;
+    if (kind == SPOPT_KIND_ADAM) {
+        h.adam = *(const spopt_adam_config*)config;
+        int rc = check_adam_config(&h.adam);
+        if (rc) return rc;
+        if (m_or_momentum == nullptr || v == nullptr || last_step == nullptr)
+            return fail(SPOPT_EINVAL, "create: Adam needs m, v and last_step");
+    } else if (kind == SPOPT_KIND_SGD) {
+        h.sgd = *(const spopt_sgd_config*)config;
+        int rc = check_sgd_config(&h.sgd);
+        if (rc) return rc;
+        if (h.sgd.momentum != 0.0 && m_or_momentum == nullptr)
+            return fail(SPOPT_EINVAL, "create: SGD with momentum needs a momentum buffer");
+    } else {
+        return fail(SPOPT_EINVAL, "create: unknown kind %d", kind);
+    }
+    spopt_optimizer* p = new (std::nothrow) spopt_optimizer(h);
+    if (p == nullptr) return fail(SPOPT_EINVAL, "create: out of host memory");
+    *out = p;
+    return SPOPT_OK;
+}
+
+extern "C" void sparse_opt_destroy(spopt_t h) { delete h; }
+
+extern "C" int64_t sparse_opt_get_step(spopt_t h) { return h ? h->t : -1; }
+
+extern "C" int sparse_opt_set_step(spopt_t h, int64_t t) {
+    if (h == nullptr) return fail(SPOPT_EINVAL, "set_step: NULL handle");
+    if (t < 0 || t >= INT32_MAX) return fail(SPOPT_EINVAL, "set_step: t=%lld out of range",
+                                             (long long)t);
+    h->t = t;
+    return SPOPT_OK;
+}
+
+// Shape checks of a gradient against the state (host side, no device access).
+static int check_grad_shape(const spopt_optimizer* h, const spopt_grad* g, const char* what) {
+    if (g == nullptr) return fail(SPOPT_EINVAL, "%s: NULL gradient", what);
+    if (g->format == SPOPT_FORMAT_COO) {
+        const spopt_coo& c = g->coo;
+        if (c.nnz < 0) return fail(SPOPT_EINVAL, "%s: nnz < 0", what);
+        if (c.nnz > 0 && (c.indices == nullptr || c.values == nullptr))
+            return fail(SPOPT_EINVAL, "%s: NULL COO arrays", what);
+        const bool flat = c.width == 1 && c.dim == h->rows * h->cols;
+        const bool full = c.width == h->cols && c.dim == h->rows;
+        if (!flat && !full)
+            return fail(SPOPT_ESHAPE,
+                        "%s: COO dim %lld width %lld matches neither %lld x 1 nor %lld x %lld",
+                        what, (long long)c.dim, (long long)c.width,
+                        (long long)(h->rows * h->cols), (long long)h->rows, (long long)h->cols);
+        return SPOPT_OK;
+    }
+    if (g->format == SPOPT_FORMAT_CSR) {
+        const spopt_csr& c = g->csr;
+        if (c.rows != h->rows || c.cols != h->cols)
+            return fail(SPOPT_ESHAPE, "%s: CSR shape %lld x %lld != state %lld x %lld", what,
+                        (long long)c.rows, (long long)c.cols, (long long)h->rows,
+                        (long long)h->cols);
+        if (c.row_offsets == nullptr) return fail(SPOPT_EINVAL, "%s: NULL row_offsets", what);
+        if (c.touched_rows && c.n_touched < 0) return fail(SPOPT_EINVAL, "%s: n_touched < 0", what);
+        return SPOPT_OK;
+    }
+    return fail(SPOPT_EINVAL, "%s: unknown gradient format %d", what, g->format);
+}
+
+static int validate_grad(const spopt_optimizer* h, const spopt_grad* g, const int32_t* ls,
+                         int32_t t, hipStream_t s, const char* what) {
+    const bool touched = g->format == SPOPT_FORMAT_CSR && g->csr.touched_rows != nullptr;
+    return validate_on_device(s, touched, what, [&](uint32_t* status) {
+        if (g->format == SPOPT_FORMAT_COO) return launch_check_coo(&g->coo, 1, ls, t, status, s);
+        return launch_check_csr(&g->csr, 1, ls, t, status, s);
+    });
+}
+
+extern "C" int sparse_adam_step(spopt_t h, const spopt_grad* g, void* stream, uint32_t flags) {
+    hipStream_t s = (hipStream_t)stream;
+    if (h == nullptr) return fail(SPOPT_EINVAL, "sparse_adam_step: NULL handle");
+    if (h->kind != SPOPT_KIND_ADAM) return fail(SPOPT_EINVAL, "sparse_adam_step: not an Adam handle");
+    int rc = check_grad_shape(h, g, "sparse_adam_step");
+    if (rc) return rc;
+    const int64_t t = h->t + 1;
+    if (t >= INT32_MAX) return fail(SPOPT_EINVAL, "sparse_adam_step: t would reach 2^31");
+    if (flags & SPOPT_VALIDATE) {
+        rc = validate_grad(h, g, h->ls, (int32_t)t, s, "sparse_adam_step");
+        if (rc) return rc;
+    }
+    const spopt_adam_config& c = h->adam;
+    AdamScalars a;
+    a.lr = (float)c.lr;
+    a.c1 = (float)(1.0 - c.beta1);
+    a.c2 = (float)(1.0 - c.beta2);
+    a.inv_bc1 = (float)(1.0 / (1.0 - pow(c.beta1, (double)t)));
+    a.inv_bc2 = (float)(1.0 / (1.0 - pow(c.beta2, (double)t)));
+    a.eps = (float)c.eps;
+    a.beta1 = (float)c.beta1;
+    a.beta2 = (float)c.beta2;
+    a.l2b1 = (float)log2(c.beta1);
+    a.l2b2 = (float)log2(c.beta2);
+    a.t = (int32_t)t;
+    rc = launch_adam(h->p, h->m, h->v, h->ls, a, c.mode, g, h->rows, h->cols, s);
+    if (rc) return rc;
+    h->t = t;
+    return SPOPT_OK;
+}
+
+extern "C" int sparse_sgd_step(spopt_t h, const spopt_grad* g, void* stream, uint32_t flags) {
+    hipStream_t s = (hipStream_t)stream;
+    if (h == nullptr) return fail(SPOPT_EINVAL, "sparse_sgd_step: NULL handle");
+    if (h->kind != SPOPT_KIND_SGD) return fail(SPOPT_EINVAL, "sparse_sgd_step: not an SGD handle");
+    int rc = check_grad_shape(h, g, "sparse_sgd_step");
+    if (rc) return rc;
+    const int64_t t = h->t + 1;
+    if (t >= INT32_MAX) return fail(SPOPT_EINVAL, "sparse_sgd_step: t would reach 2^31");
+    if (flags & SPOPT_VALIDATE) {
+        rc = validate_grad(h, g, nullptr, 0, s, "sparse_sgd_step");
+        if (rc) return rc;
+    }
+    const spopt_sgd_config& c = h->sgd;
+    rc = launch_sgd(h->p, h->m, (float)c.lr, (float)c.momentum, (float)c.weight_decay, g,
+                    h->rows, h->cols, s);
+    if (rc) return rc;
+    h->t = t;
+    return SPOPT_OK;
+}

@@ -1,0 +1,172 @@
+// common.hpp - device helpers and host plumbing shared by the HIP sources of
+// the sparse / lazy optimizer library (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <mutex>
+
+#include "sparse_opt.h"
+
+namespace spopt {
+
+constexpr int kWave = 64;
+
+// Device-side status bits, OR-ed into a status word by checking kernels.
+enum : uint32_t {
+    kStatusRange = 1u,     // index outside its range
+    kStatusNotCanon = 2u,  // not strictly ascending / CSR not canonical
+    kStatusNonFinite = 4u, // NaN or inf gradient value
+    kStatusStep = 8u,      // last_step >= t on a touched coordinate
+    kStatusTouched = 16u   // touched-row list inconsistent with row_offsets
+};
+
+// ---------------------------------------------------------------- device ---
+
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return (uint64_t)__ballot(p); }
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+    const int l = lane_id();
+    return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+__device__ __forceinline__ int popc64(uint64_t x) { return __popcll(x); }
+
+template <class T>
+__device__ __forceinline__ T read_lane(T v, int lane);
+
+template <>
+__device__ __forceinline__ int read_lane<int>(int v, int lane) {
+    return __builtin_amdgcn_readlane(v, lane);
+}
+template <>
+__device__ __forceinline__ uint32_t read_lane<uint32_t>(uint32_t v, int lane) {
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, lane);
+}
+
+// Inclusive prefix sum across the 64 lanes of a wave.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+    const int l = lane_id();
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        uint32_t y = __shfl_up(x, off, kWave);
+        if (l >= off) x += y;
+    }
+    return x;
+}
+
+// Exclusive prefix sum over a block; `warp_tot` is LDS scratch with one slot
+// per wave of the block.  Returns the exclusive prefix; *total gets the sum.
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, uint32_t* warp_tot,
+                                                    uint32_t* total) {
+    const int w = (int)(threadIdx.x >> 6);
+    const int nw = (int)((blockDim.x + kWave - 1) >> 6);
+    uint32_t inc = wave_incl_scan(x);
+    if (lane_id() == kWave - 1) warp_tot[w] = inc;
+    __syncthreads();
+    uint32_t before = 0, all = 0;
+    for (int i = 0; i < nw; ++i) {
+        uint32_t t = warp_tot[i];
+        if (i < w) before += t;
+        all += t;
+    }
+    __syncthreads();
+    *total = all;
+    return before + inc - x;
+}
+
+// Wave-cooperative lower bound: first index i in [0, n) with a[i] >= x (n if
+// none), for ascending a.  Each round probes 64 evenly spaced positions, so a
+// search over 2^18 keys takes 3 dependent loads.  All lanes return the result.
+__device__ __forceinline__ int64_t wave_lower_bound(const int64_t* a, int64_t n, int64_t x) {
+    const int l = lane_id();
+    int64_t lo = 0, hi = n;  // answer in [lo, hi]
+    while (hi - lo > kWave) {
+        const int64_t step = (hi - lo + kWave - 1) / kWave;
+        const int64_t q = lo + (int64_t)(l + 1) * step - 1;
+        const bool valid = q < hi;
+        const bool less = valid && a[q] < x;
+        const int cnt = popc64(ballot(less));
+        const int nvalid = popc64(ballot(valid));
+        const int64_t new_lo = lo + (int64_t)cnt * step;
+        if (cnt < nvalid) hi = lo + (int64_t)(cnt + 1) * step - 1;
+        lo = new_lo;
+        if (hi > n) hi = n;
+    }
+    const int64_t q = lo + l;
+    const bool less = (q < hi) && a[q] < x;
+    return lo + popc64(ballot(less));
+}
+
+__device__ __forceinline__ bool finite_f(float x) { return __builtin_isfinite(x); }
+
+// ------------------------------------------------------------------ host ---
+
+void set_error(const char* fmt, ...);
+int fail(int code, const char* fmt, ...);
+
+#define SPOPT_HIP(call)                                                                   \
+    do {                                                                                  \
+        hipError_t e_ = (call);                                                           \
+        if (e_ != hipSuccess)                                                             \
+            return ::spopt::fail(SPOPT_EDEVICE, "%s failed: %s", #call,                   \
+                                 hipGetErrorString(e_));                                  \
+    } while (0)
+
+#define SPOPT_LAUNCHED()                                                                  \
+    do {                                                                                  \
+        hipError_t e_ = hipGetLastError();                                                \
+        if (e_ != hipSuccess)                                                             \
+            return ::spopt::fail(SPOPT_EDEVICE, "kernel launch failed: %s",               \
+                                 hipGetErrorString(e_));                                  \
+    } while (0)
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+__host__ __device__ inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Status-word helpers implemented in abi.cpp.
+int status_to_code(uint32_t bits, const char* what);
+std::mutex& validation_mutex();
+uint32_t* device_status_block();  // 4 words per device, allocated on first use
+int device_status_check(uint32_t* d_status, hipStream_t s, bool check_touched,
+                        const char* what);
+
+// Launchers shared between the sources.
+int launch_status_clear(uint32_t* d_status, int nwords, hipStream_t s);
+int launch_check_coo(const spopt_coo* c, int check_finite, const int32_t* ls, int32_t t,
+                     uint32_t* status, hipStream_t s);
+int launch_check_csr(const spopt_csr* c, int check_finite, const int32_t* ls, int32_t t,
+                     uint32_t* status, hipStream_t s);
+
+// Per-step scalars of Adam, each formed in double on the host and rounded once.
+struct AdamScalars {
+    float lr, c1, c2, inv_bc1, inv_bc2, eps, beta1, beta2, l2b1, l2b2;
+    int32_t t;
+};
+int launch_adam(float* p, float* m, float* v, int32_t* ls, const AdamScalars& a, int mode,
+                const spopt_grad* gr, int64_t rows, int64_t cols, hipStream_t s);
+int launch_sgd(float* p, float* b, float lr, float mu, float wd, const spopt_grad* gr,
+               int64_t rows, int64_t cols, hipStream_t s);
+
+// A validated call: serialised with every other validated call of the
+// process, it clears the device's status block, lets `launch` enqueue its
+// checks into it, and reads it back (one synchronisation of `s`).
+template <class F>
+int validate_on_device(hipStream_t s, bool check_touched, const char* what, F&& launch) {
+    std::lock_guard<std::mutex> guard(validation_mutex());
+    uint32_t* status = device_status_block();
+    if (status == nullptr) return fail(SPOPT_EDEVICE, "%s: no device status block", what);
+    int rc = launch_status_clear(status, 4, s);
+    if (rc) return rc;
+    rc = launch(status);
+    if (rc) return rc;
+    return device_status_check(status, s, check_touched, what);
+}
+
+}  // namespace spopt

@@ -1,0 +1,370 @@
+// csr.hip - COO <-> CSR on the GPU and the canonical-form checks.
+//
+// Follows the optirs_gpu sparse_optimizer page, section "Sparse gradient
+// representations": a CsrGradient of shape (r, c) and a CooGradient over
+// dim = r*c correspond through linear index row*c + col (CsrGradient::to_coo
+// and ::from_coo), columns strictly ascending within every row.
+//
+// row_offsets is built without a global scan: a block owns 4096 consecutive
+// entries of row_offsets, finds the range of COO entries that fall into its
+// rows with two wave-parallel lower-bound searches over the sorted indices,
+// counts entries per row in LDS and scans the counts locally.
+#include "common.hpp"
+
+namespace spopt {
+
+constexpr int kRoRows = 4096;  // row_offsets entries per block
+constexpr int kRoThreads = 256;
+constexpr int kRoPer = kRoRows / kRoThreads;
+
+__global__ __launch_bounds__(kRoThreads) void k_row_offsets(
+    const int64_t* __restrict__ idx, const int64_t* d_nnz, int64_t nnz_host, int64_t rows,
+    int64_t cols, int64_t width, int32_t* __restrict__ row_offsets) {
+    __shared__ int64_t bounds[2];
+    __shared__ uint32_t cnt[kRoRows];
+    __shared__ uint32_t wt[kRoThreads / kWave];
+    const int64_t nnz = d_nnz ? (*d_nnz < nnz_host ? *d_nnz : nnz_host) : nnz_host;
+    const int64_t r0 = (int64_t)blockIdx.x * kRoRows;
+    const int64_t r1 = (r0 + kRoRows < rows + 1) ? r0 + kRoRows : rows + 1;
+    const int64_t scale = (width == 1) ? cols : 1;  // entries of row r have keys < (r+1)*scale
+    const int w = (int)(threadIdx.x >> 6);
+    if (w < 2) {
+        const int64_t lb = wave_lower_bound(idx, nnz, (w == 0 ? r0 : r1) * scale);
+        if (lane_id() == 0) bounds[w] = lb;
+    }
+    for (int i = threadIdx.x; i < kRoRows; i += kRoThreads) cnt[i] = 0;
+    __syncthreads();
+    const int64_t ka = bounds[0], kb = bounds[1];
+    // For canonical input every entry in [ka, kb) lies in rows [r0, r1); the
+    // bound test only keeps malformed trusted input inside the LDS array.
+    if (scale == 1) {
+        for (int64_t k = ka + threadIdx.x; k < kb; k += kRoThreads) {
+            const int64_t o = idx[k] - r0;
+            if ((uint64_t)o < (uint64_t)kRoRows) cnt[o] = 1u;
+        }
+    } else {
+        for (int64_t k = ka + threadIdx.x; k < kb; k += kRoThreads) {
+            const int64_t x = idx[k];
+            const int64_t o = (x < 0 ? -1 : x / scale - r0);
+            if ((uint64_t)o < (uint64_t)kRoRows) atomicAdd(&cnt[o], 1u);
+        }
+    }
+    __syncthreads();
+    uint32_t loc[kRoPer];
+    uint32_t sum = 0;
+#pragma unroll
+    for (int j = 0; j < kRoPer; ++j) {
+        loc[j] = cnt[threadIdx.x * kRoPer + j];
+        sum += loc[j];
+    }
+    uint32_t total;
+    uint32_t run = block_excl_scan(sum, wt, &total);
+#pragma unroll
+    for (int j = 0; j < kRoPer; ++j) {
+        cnt[threadIdx.x * kRoPer + j] = run;
+        run += loc[j];
+    }
+    __syncthreads();
+    const int64_t per_entry = (width == 1) ? 1 : cols;
+    for (int64_t r = r0 + threadIdx.x; r < r1; r += kRoThreads)
+        row_offsets[r] = (int32_t)((ka + (int64_t)cnt[r - r0]) * per_entry);
+}
+
+// col_indices of full rows: 0..cols-1 repeated for every touched row.
+__global__ void k_full_cols(int32_t* __restrict__ ci, const int64_t* d_nnz, int64_t nnz_host,
+                            int64_t cols) {
+    const int64_t nnz = d_nnz ? (*d_nnz < nnz_host ? *d_nnz : nnz_host) : nnz_host;
+    const int64_t total = nnz * cols;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    if ((cols & 3) == 0 && aligned16(ci)) {
+        for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total / 4; q += stride) {
+            const int32_t c = (int32_t)((q * 4) % cols);
+            reinterpret_cast<int4*>(ci)[q] = make_int4(c, c + 1, c + 2, c + 3);
+        }
+    } else {
+        for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total; q += stride)
+            ci[q] = (int32_t)(q % cols);
+    }
+}
+
+// Scalar COO over the flattened view: column of every entry, values copied.
+__global__ void k_scalar_cols(const int64_t* __restrict__ idx, const float* __restrict__ vin,
+                              const int64_t* d_nnz, int64_t nnz_host, int64_t cols,
+                              int32_t* __restrict__ ci, float* __restrict__ vout) {
+    const int64_t nnz = d_nnz ? (*d_nnz < nnz_host ? *d_nnz : nnz_host) : nnz_host;
+    for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < nnz;
+         k += (int64_t)gridDim.x * blockDim.x) {
+        if (ci) ci[k] = (int32_t)(idx[k] % cols);
+        if (vout) vout[k] = vin[k];
+    }
+}
+
+__global__ void k_copy_f32(const float* __restrict__ in, float* __restrict__ out,
+                           const int64_t* d_nnz, int64_t nnz_host, int64_t width) {
+    const int64_t nnz = d_nnz ? (*d_nnz < nnz_host ? *d_nnz : nnz_host) : nnz_host;
+    const int64_t total = nnz * width;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    if ((total & 3) == 0 && aligned16(in) && aligned16(out)) {
+        for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total / 4; q += stride)
+            reinterpret_cast<float4*>(out)[q] = reinterpret_cast<const float4*>(in)[q];
+    } else {
+        for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total; q += stride)
+            out[q] = in[q];
+    }
+}
+
+__global__ void k_copy_rows(const int64_t* __restrict__ in, int64_t* __restrict__ out,
+                            const int64_t* d_nnz, int64_t nnz_host, int64_t* d_count) {
+    const int64_t nnz = d_nnz ? (*d_nnz < nnz_host ? *d_nnz : nnz_host) : nnz_host;
+    const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (out && out != in)
+        for (int64_t k = g; k < nnz; k += (int64_t)gridDim.x * blockDim.x) out[k] = in[k];
+    if (d_count && g == 0) *d_count = nnz;
+}
+
+// CSR -> linear COO indices, one wave per 64 rows.
+__global__ __launch_bounds__(256) void k_csr_to_coo(const int32_t* __restrict__ ro,
+                                                    const int32_t* __restrict__ ci,
+                                                    const float* __restrict__ vin, int64_t rows,
+                                                    int64_t cols, int64_t* __restrict__ out_idx,
+                                                    float* __restrict__ vout) {
+    const int lane = lane_id();
+    const int64_t nw = ((int64_t)gridDim.x * blockDim.x) >> 6;
+    const int nnz = ro[rows];  // entries stay inside [0, nnz) even for malformed offsets
+    for (int64_t tile = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+         tile * kWave < rows; tile += nw) {
+        const int64_t r = tile * kWave + lane;
+        int a = 0, b = 0;
+        if (r < rows) {
+            a = ro[r];
+            b = ro[r + 1];
+        }
+        uint64_t mask = ballot(b > a && a >= 0 && b <= nnz);
+        while (mask) {
+            const int bit = __builtin_ctzll(mask);
+            mask &= mask - 1;
+            const int st = read_lane(a, bit), en = read_lane(b, bit);
+            const int64_t row = tile * kWave + bit;
+            for (int j = st + lane; j < en; j += kWave) {
+                const int64_t c = ci ? (int64_t)ci[j] : (int64_t)(j - st);
+                out_idx[j] = row * cols + c;
+                if (vout) vout[j] = vin[j];
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------- checks ---
+
+// COO canonical form, ranges, finiteness, and (for Adam) last_step < t.
+__global__ void k_check_coo(const int64_t* __restrict__ idx, const float* __restrict__ vals,
+                            const int64_t* d_nnz, int64_t nnz_host, int64_t dim, int64_t width,
+                            int check_finite, const int32_t* __restrict__ ls, int32_t t,
+                            uint32_t* status) {
+    const int64_t nnz = d_nnz ? (*d_nnz < nnz_host ? *d_nnz : nnz_host) : nnz_host;
+    uint32_t bad = 0;
+    for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < nnz;
+         k += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t i = idx[k];
+        if (i < 0 || i >= dim) {
+            bad |= kStatusRange;
+            continue;
+        }
+        if (k > 0 && idx[k - 1] >= i) bad |= kStatusNotCanon;
+        for (int64_t c = 0; c < width; ++c) {
+            if (check_finite && !finite_f(vals[k * width + c])) bad |= kStatusNonFinite;
+            if (ls && ls[i * width + c] >= t) bad |= kStatusStep;
+        }
+    }
+    if (bad) atomicOr(status, bad);
+}
+
+// CSR canonical form (one wave per 64 rows), finiteness, last_step < t, and a
+// count of non-empty rows in status[1].
+__global__ __launch_bounds__(256) void k_check_csr(const int32_t* __restrict__ ro,
+                                                   const int32_t* __restrict__ ci,
+                                                   const float* __restrict__ vals, int64_t rows,
+                                                   int64_t cols, int check_finite,
+                                                   const int32_t* __restrict__ ls, int32_t t,
+                                                   uint32_t* status) {
+    const int lane = lane_id();
+    const int64_t nw = ((int64_t)gridDim.x * blockDim.x) >> 6;
+    uint32_t bad = 0;
+    uint32_t nonempty = 0;
+    const int nnz = ro[rows];
+    if (blockIdx.x == 0 && threadIdx.x == 0 && (ro[0] != 0 || nnz < 0)) bad |= kStatusNotCanon;
+    for (int64_t tile = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+         tile * kWave < rows; tile += nw) {
+        const int64_t r = tile * kWave + lane;
+        int a = 0, b = 0;
+        if (r < rows) {
+            a = ro[r];
+            b = ro[r + 1];
+            if (b < a || a < 0 || b > nnz) {
+                bad |= kStatusNotCanon;
+                b = a;  // no entry of a malformed row is read
+            }
+        }
+        uint64_t mask = ballot(b > a);
+        if (lane == 0) nonempty += (uint32_t)popc64(mask);
+        while (mask) {
+            const int bit = __builtin_ctzll(mask);
+            mask &= mask - 1;
+            const int st = read_lane(a, bit), en = read_lane(b, bit);
+            const int64_t row = tile * kWave + bit;
+            if (ci == nullptr && en - st != cols) bad |= kStatusNotCanon;
+            for (int j = st + lane; j < en; j += kWave) {
+                const int64_t c = ci ? (int64_t)ci[j] : (int64_t)(j - st);
+                if (c < 0 || c >= cols) {
+                    bad |= kStatusRange;
+                    continue;
+                }
+                if (ci && j > st && ci[j - 1] >= c) bad |= kStatusNotCanon;
+                if (check_finite && !finite_f(vals[j])) bad |= kStatusNonFinite;
+                if (ls && ls[row * cols + c] >= t) bad |= kStatusStep;
+            }
+        }
+    }
+    if (bad) atomicOr(status, bad);
+    if (lane == 0 && nonempty) atomicAdd(status + 1, nonempty);
+}
+
+// Touched-row list: ascending, in range, every listed row non-empty.
+__global__ void k_check_touched(const int64_t* __restrict__ tr, const int64_t* d_n,
+                                int64_t n_host, const int32_t* __restrict__ ro, int64_t rows,
+                                uint32_t* status) {
+    const int64_t n = d_n ? (*d_n < n_host ? *d_n : n_host) : n_host;
+    uint32_t bad = 0;
+    for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < n;
+         k += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t r = tr[k];
+        if (r < 0 || r >= rows) {
+            bad |= kStatusTouched;
+            continue;
+        }
+        if (k > 0 && tr[k - 1] >= r) bad |= kStatusTouched;
+        if (ro[r + 1] <= ro[r]) bad |= kStatusTouched;
+    }
+    if (bad) atomicOr(status, bad);
+    if (blockIdx.x == 0 && threadIdx.x == 0) status[2] = (uint32_t)n;
+}
+
+static unsigned grid_for(int64_t work, int64_t per_block, int64_t cap = 4096) {
+    int64_t g = ceil_div(work, per_block);
+    if (g < 1) g = 1;
+    return (unsigned)(g < cap ? g : cap);
+}
+
+int launch_check_coo(const spopt_coo* c, int check_finite, const int32_t* ls, int32_t t,
+                     uint32_t* status, hipStream_t s) {
+    k_check_coo<<<grid_for(c->nnz, 256), 256, 0, s>>>(c->indices, c->values, c->d_nnz, c->nnz,
+                                                      c->dim, c->width, check_finite, ls, t,
+                                                      status);
+    SPOPT_LAUNCHED();
+    return SPOPT_OK;
+}
+
+int launch_check_csr(const spopt_csr* c, int check_finite, const int32_t* ls, int32_t t,
+                     uint32_t* status, hipStream_t s) {
+    k_check_csr<<<grid_for(ceil_div(c->rows, kWave), 4), 256, 0, s>>>(
+        c->row_offsets, c->col_indices, c->values, c->rows, c->cols, check_finite, ls, t,
+        status);
+    SPOPT_LAUNCHED();
+    if (c->touched_rows) {
+        k_check_touched<<<grid_for(c->n_touched, 256), 256, 0, s>>>(
+            c->touched_rows, c->d_n_touched, c->n_touched, c->row_offsets, c->rows, status);
+        SPOPT_LAUNCHED();
+    }
+    return SPOPT_OK;
+}
+
+}  // namespace spopt
+
+using namespace spopt;
+
+extern "C" int csr_from_coo(const spopt_coo* in, int64_t rows, int64_t cols,
+                            int32_t* row_offsets, int32_t* col_indices, float* values,
+                            int64_t* touched_rows, int64_t* d_n_touched, void* stream,
+                            uint32_t flags) {
+    hipStream_t st = (hipStream_t)stream;
+    if (in == nullptr || row_offsets == nullptr || rows < 1 || cols < 1 || in->nnz < 0)
+        return fail(SPOPT_EINVAL, "csr_from_coo: NULL argument or bad size");
+    if (in->nnz > 0 && (in->indices == nullptr || in->values == nullptr))
+        return fail(SPOPT_EINVAL, "csr_from_coo: NULL COO arrays");
+    const bool full = in->width == cols && in->width > 1;
+    if (in->width == 1) {
+        if (in->dim != rows * cols)
+            return fail(SPOPT_ESHAPE, "csr_from_coo: dim %lld != rows*cols %lld",
+                        (long long)in->dim, (long long)(rows * cols));
+        if (col_indices == nullptr)
+            return fail(SPOPT_EINVAL, "csr_from_coo: col_indices required for scalar entries");
+        if (touched_rows != nullptr || d_n_touched != nullptr)
+            return fail(SPOPT_EINVAL,
+                        "csr_from_coo: touched_rows is produced for full-row COO only");
+    } else if (full) {
+        if (in->dim != rows)
+            return fail(SPOPT_ESHAPE, "csr_from_coo: full-row COO dim %lld != rows %lld",
+                        (long long)in->dim, (long long)rows);
+    } else {
+        return fail(SPOPT_ESHAPE, "csr_from_coo: width %lld is neither 1 nor cols %lld",
+                    (long long)in->width, (long long)cols);
+    }
+    if (in->nnz * in->width >= ((int64_t)1 << 31))
+        return fail(SPOPT_EOVERFLOW, "csr_from_coo: %lld entries do not fit int32 offsets",
+                    (long long)(in->nnz * in->width));
+    if (flags & SPOPT_VALIDATE) {
+        const int rc = validate_on_device(st, false, "csr_from_coo", [&](uint32_t* status) {
+            return launch_check_coo(in, 0, nullptr, 0, status, st);
+        });
+        if (rc) return rc;
+    }
+    k_row_offsets<<<(unsigned)ceil_div(rows + 1, kRoRows), kRoThreads, 0, st>>>(
+        in->indices, in->d_nnz, in->nnz, rows, cols, in->width, row_offsets);
+    SPOPT_LAUNCHED();
+    if (full) {
+        if (col_indices) {
+            k_full_cols<<<grid_for(in->nnz * cols / 4 + 1, 256), 256, 0, st>>>(
+                col_indices, in->d_nnz, in->nnz, cols);
+            SPOPT_LAUNCHED();
+        }
+        if (values && values != in->values) {
+            k_copy_f32<<<grid_for(in->nnz * cols / 4 + 1, 256), 256, 0, st>>>(
+                in->values, values, in->d_nnz, in->nnz, cols);
+            SPOPT_LAUNCHED();
+        }
+        if ((touched_rows && touched_rows != in->indices) ||
+            (d_n_touched && d_n_touched != in->d_nnz)) {
+            k_copy_rows<<<grid_for(in->nnz, 256), 256, 0, st>>>(
+                in->indices, touched_rows == in->indices ? nullptr : touched_rows, in->d_nnz,
+                in->nnz, d_n_touched == in->d_nnz ? nullptr : d_n_touched);
+            SPOPT_LAUNCHED();
+        }
+    } else {
+        k_scalar_cols<<<grid_for(in->nnz, 256), 256, 0, st>>>(
+            in->indices, in->values, in->d_nnz, in->nnz, cols, col_indices,
+            values == in->values ? nullptr : values);
+        SPOPT_LAUNCHED();
+    }
+    return SPOPT_OK;
+}
+
+extern "C" int csr_to_coo(const spopt_csr* in, int64_t* out_indices, float* out_values,
+                          void* stream, uint32_t flags) {
+    hipStream_t st = (hipStream_t)stream;
+    if (in == nullptr || out_indices == nullptr || in->row_offsets == nullptr || in->rows < 1 ||
+        in->cols < 1)
+        return fail(SPOPT_EINVAL, "csr_to_coo: NULL argument or bad size");
+    if (out_values && in->values == nullptr)
+        return fail(SPOPT_EINVAL, "csr_to_coo: values requested but CSR has none");
+    if (flags & SPOPT_VALIDATE) {
+        const int rc = validate_on_device(st, false, "csr_to_coo", [&](uint32_t* status) {
+            return launch_check_csr(in, 0, nullptr, 0, status, st);
+        });
+        if (rc) return rc;
+    }
+    k_csr_to_coo<<<grid_for(ceil_div(in->rows, kWave), 4), 256, 0, st>>>(
+        in->row_offsets, in->col_indices, in->values, in->rows, in->cols, out_indices,
+        out_values);
+    SPOPT_LAUNCHED();
+    return SPOPT_OK;
+}

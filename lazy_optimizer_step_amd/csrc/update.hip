@@ -1,0 +1,335 @@
+// update.hip - gather-update-scatter over the touched coordinates only.
+//
+// The per-coordinate arithmetic follows the optirs_gpu sparse_optimizer page:
+//   Adam, sections "LazyAdamMode::Lazy" / "LazyAdamMode::DormancyDecay":
+//     d = beta (Lazy) or beta^(t - last_step) (DormancyDecay)
+//     m = d1*m + (1-beta1)*g,  v = d2*v + (1-beta2)*g^2
+//     p -= lr * (m/(1-beta1^t)) / (sqrt(v/(1-beta2^t)) + eps),  last_step = t
+//   SGD, section "Sparse SGD": g' = g + wd*p; with momentum b = mu*b + g',
+//     p -= lr*b; without, p -= lr*g'.
+// Every scalar that depends only on the hyper-parameters and t (1 - beta,
+// 1/(1 - beta^t), log2 beta) is formed in double on the host and passed
+// rounded to float.  beta^gap is exp2(gap * log2 beta), exact beta for gap 1.
+//
+// Work mapping: LPR lanes per touched row, 64/LPR rows per wave.  A full row
+// (all cols entries present) is moved with 16-byte loads and stores of p, m,
+// v, last_step and g; a partial row uses one lane per entry.  Rows come from
+// a touched-row list (CSR) or the keys of a full-row COO; without a list the
+// CSR kernel scans row_offsets 64 rows per wave.
+#include "common.hpp"
+
+namespace spopt {
+
+
+template <int MODE>
+struct AdamOp {
+    float* __restrict__ p;
+    float* __restrict__ m;
+    float* __restrict__ v;
+    int32_t* __restrict__ ls;
+    AdamScalars a;
+
+    struct Vec {
+        float4 p, m, v;
+        int4 ls;
+    };
+
+    __device__ __forceinline__ void coord(float& pp, float& mm, float& vv, int32_t last,
+                                          float g) const {
+        float d1 = a.beta1, d2 = a.beta2;
+        if (MODE == SPOPT_MODE_DORMANCY) {
+            const int32_t gap = a.t - last;
+            if (gap != 1) {
+                const float fg = (float)gap;
+                d1 = exp2f(fg * a.l2b1);
+                d2 = exp2f(fg * a.l2b2);
+            }
+        }
+        mm = fmaf(d1, mm, a.c1 * g);
+        vv = fmaf(d2, vv, a.c2 * (g * g));
+        const float mh = mm * a.inv_bc1;
+        const float vh = vv * a.inv_bc2;
+        pp = pp - a.lr * mh / (sqrtf(vh) + a.eps);
+    }
+
+    __device__ __forceinline__ void load(int64_t i, Vec& r) const {
+        r.p = *reinterpret_cast<const float4*>(p + i);
+        r.m = *reinterpret_cast<const float4*>(m + i);
+        r.v = *reinterpret_cast<const float4*>(v + i);
+        if (MODE == SPOPT_MODE_DORMANCY)
+            r.ls = *reinterpret_cast<const int4*>(ls + i);
+        else
+            r.ls = make_int4(0, 0, 0, 0);
+    }
+    __device__ __forceinline__ void compute(Vec& r, const float4 g) const {
+        coord(r.p.x, r.m.x, r.v.x, r.ls.x, g.x);
+        coord(r.p.y, r.m.y, r.v.y, r.ls.y, g.y);
+        coord(r.p.z, r.m.z, r.v.z, r.ls.z, g.z);
+        coord(r.p.w, r.m.w, r.v.w, r.ls.w, g.w);
+    }
+    __device__ __forceinline__ void store(int64_t i, const Vec& r) const {
+        *reinterpret_cast<float4*>(p + i) = r.p;
+        *reinterpret_cast<float4*>(m + i) = r.m;
+        *reinterpret_cast<float4*>(v + i) = r.v;
+        *reinterpret_cast<int4*>(ls + i) = make_int4(a.t, a.t, a.t, a.t);
+    }
+    __device__ __forceinline__ void scalar(int64_t i, float g) const {
+        float pp = p[i], mm = m[i], vv = v[i];
+        const int32_t last = (MODE == SPOPT_MODE_DORMANCY) ? ls[i] : 0;
+        coord(pp, mm, vv, last, g);
+        p[i] = pp;
+        m[i] = mm;
+        v[i] = vv;
+        ls[i] = a.t;
+    }
+};
+
+template <bool MOM>
+struct SgdOp {
+    float* __restrict__ p;
+    float* __restrict__ b;
+    float lr, mu, wd;
+
+    struct Vec {
+        float4 p, b;
+    };
+
+    __device__ __forceinline__ void coord(float& pp, float& bb, float g) const {
+        const float gg = fmaf(wd, pp, g);
+        if (MOM) {
+            bb = fmaf(mu, bb, gg);
+            pp = fmaf(-lr, bb, pp);
+        } else {
+            pp = fmaf(-lr, gg, pp);
+        }
+    }
+    __device__ __forceinline__ void load(int64_t i, Vec& r) const {
+        r.p = *reinterpret_cast<const float4*>(p + i);
+        if (MOM)
+            r.b = *reinterpret_cast<const float4*>(b + i);
+        else
+            r.b = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    __device__ __forceinline__ void compute(Vec& r, const float4 g) const {
+        coord(r.p.x, r.b.x, g.x);
+        coord(r.p.y, r.b.y, g.y);
+        coord(r.p.z, r.b.z, g.z);
+        coord(r.p.w, r.b.w, g.w);
+    }
+    __device__ __forceinline__ void store(int64_t i, const Vec& r) const {
+        *reinterpret_cast<float4*>(p + i) = r.p;
+        if (MOM) *reinterpret_cast<float4*>(b + i) = r.b;
+    }
+    __device__ __forceinline__ void scalar(int64_t i, float g) const {
+        float pp = p[i], bb = MOM ? b[i] : 0.f;
+        coord(pp, bb, g);
+        p[i] = pp;
+        if (MOM) b[i] = bb;
+    }
+};
+
+// Touched rows given as the keys of a full-row COO: row k's values start at k*cols.
+struct SrcBlockCoo {
+    const int64_t* __restrict__ idx;
+    int64_t cols;
+    __device__ __forceinline__ void get(int64_t k, int64_t& row, int64_t& st, int64_t& len) const {
+        row = idx[k];
+        st = k * cols;
+        len = cols;
+    }
+    __device__ __forceinline__ int64_t col(int64_t, int64_t j) const { return j; }
+};
+
+// Touched rows of a CSR gradient.
+struct SrcCsrTouched {
+    const int64_t* __restrict__ touched;
+    const int32_t* __restrict__ ro;
+    const int32_t* __restrict__ ci;
+    int64_t rows;
+    __device__ __forceinline__ void get(int64_t k, int64_t& row, int64_t& st, int64_t& len) const {
+        row = touched[k];
+        if ((uint64_t)row >= (uint64_t)rows) {
+            len = 0;
+            st = 0;
+            return;
+        }
+        st = ro[row];
+        len = (int64_t)ro[row + 1] - st;
+        if (st < 0 || st + len > (int64_t)ro[rows]) len = 0;  // entries stay in [0, nnz)
+    }
+    __device__ __forceinline__ int64_t col(int64_t st, int64_t j) const {
+        return ci ? (int64_t)ci[st + j] : j;
+    }
+};
+
+template <class Op, class Src, int LPR>
+__global__ __launch_bounds__(256) void k_update_rows(Op op, Src src, const int64_t* d_count,
+                                                     int64_t count_host, int64_t rows,
+                                                     int64_t cols, const float* __restrict__ g,
+                                                     int vec_ok) {
+    const int64_t count = d_count ? (*d_count < count_host ? *d_count : count_host) : count_host;
+    constexpr int RPW = kWave / LPR;
+    const int lane = lane_id();
+    const int sub = lane / LPR, sl = lane % LPR;
+    const int64_t gw = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const int64_t nw = ((int64_t)gridDim.x * blockDim.x) >> 6;
+    const int64_t nvec = cols >> 2;
+    for (int64_t k = gw * RPW + sub; k < count; k += nw * RPW) {
+        int64_t row, st, len;
+        src.get(k, row, st, len);
+        if ((uint64_t)row >= (uint64_t)rows || len <= 0) continue;
+        const int64_t base = row * cols;
+        if (len == cols && vec_ok && (st & 3) == 0) {
+            for (int64_t c4 = sl; c4 < nvec; c4 += LPR) {
+                typename Op::Vec r;
+                op.load(base + 4 * c4, r);
+                const float4 gv = *reinterpret_cast<const float4*>(g + st + 4 * c4);
+                op.compute(r, gv);
+                op.store(base + 4 * c4, r);
+            }
+        } else {
+            const int64_t n = len < cols ? len : cols;
+            for (int64_t j = sl; j < n; j += LPR) {
+                const int64_t c = src.col(st, j);
+                if ((uint64_t)c < (uint64_t)cols) op.scalar(base + c, g[st + j]);
+            }
+        }
+    }
+}
+
+// CSR without a touched-row list: one wave per 64 rows of row_offsets.
+template <class Op>
+__global__ __launch_bounds__(256) void k_update_csr_scan(Op op, const int32_t* __restrict__ ro,
+                                                         const int32_t* __restrict__ ci,
+                                                         int64_t rows, int64_t cols,
+                                                         const float* __restrict__ g) {
+    const int lane = lane_id();
+    const int64_t nw = ((int64_t)gridDim.x * blockDim.x) >> 6;
+    const int nnz = ro[rows];  // entries stay inside [0, nnz) even for malformed offsets
+    for (int64_t tile = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+         tile * kWave < rows; tile += nw) {
+        const int64_t r = tile * kWave + lane;
+        int a = 0, b = 0;
+        if (r < rows) {
+            a = ro[r];
+            b = ro[r + 1];
+        }
+        uint64_t mask = ballot(b > a && a >= 0 && b <= nnz);
+        while (mask) {
+            const int bit = __builtin_ctzll(mask);
+            mask &= mask - 1;
+            const int st = read_lane(a, bit), en = read_lane(b, bit);
+            const int64_t row = tile * kWave + bit;
+            const int64_t base = row * cols;
+            for (int j = st + lane; j < en && j - st < cols; j += kWave) {
+                const int64_t c = ci ? (int64_t)ci[j] : (int64_t)(j - st);
+                if ((uint64_t)c < (uint64_t)cols) op.scalar(base + c, g[j]);
+            }
+        }
+    }
+}
+
+// Scalar COO entries over the flattened state: one thread per entry.
+template <class Op>
+__global__ __launch_bounds__(256) void k_update_coo_scalar(Op op, const int64_t* __restrict__ idx,
+                                                           const int64_t* d_count,
+                                                           int64_t count_host, int64_t dim,
+                                                           const float* __restrict__ g) {
+    const int64_t count = d_count ? (*d_count < count_host ? *d_count : count_host) : count_host;
+    for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < count;
+         k += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t i = idx[k];
+        if ((uint64_t)i < (uint64_t)dim) op.scalar(i, g[k]);
+    }
+}
+
+// ---------------------------------------------------------------- launch ---
+
+static int lanes_per_row(int64_t cols) {
+    const int64_t nvec = (cols + 3) / 4;
+    if (nvec <= 4) return 4;
+    if (nvec <= 16) return 16;
+    if (nvec <= 32) return 32;
+    return 64;
+}
+
+static unsigned grid_cap(int64_t blocks, int64_t cap = 4096) {
+    if (blocks < 1) blocks = 1;
+    return (unsigned)(blocks < cap ? blocks : cap);
+}
+
+template <class Op, class Src>
+static int launch_rows(const Op& op, const Src& src, const int64_t* d_count, int64_t count,
+                       int64_t rows, int64_t cols, const float* g, bool vec_ok, hipStream_t s) {
+    const int lpr = lanes_per_row(cols);
+    const int64_t rows_per_block = 4 * (kWave / lpr);
+    const unsigned grid = grid_cap(ceil_div(count, rows_per_block));
+    const int v = vec_ok ? 1 : 0;
+    switch (lpr) {
+        case 4:
+            k_update_rows<Op, Src, 4><<<grid, 256, 0, s>>>(op, src, d_count, count, rows, cols, g, v);
+            break;
+        case 16:
+            k_update_rows<Op, Src, 16><<<grid, 256, 0, s>>>(op, src, d_count, count, rows, cols, g, v);
+            break;
+        case 32:
+            k_update_rows<Op, Src, 32><<<grid, 256, 0, s>>>(op, src, d_count, count, rows, cols, g, v);
+            break;
+        default:
+            k_update_rows<Op, Src, 64><<<grid, 256, 0, s>>>(op, src, d_count, count, rows, cols, g, v);
+            break;
+    }
+    SPOPT_LAUNCHED();
+    return SPOPT_OK;
+}
+
+// Dispatch one gradient to the kernel family that fits it.
+template <class Op>
+static int launch_update(const Op& op, bool state_aligned, const spopt_grad* gr, int64_t rows,
+                         int64_t cols, hipStream_t s) {
+    if (gr->format == SPOPT_FORMAT_COO) {
+        const spopt_coo& c = gr->coo;
+        if (c.nnz == 0) return SPOPT_OK;
+        if (c.width == 1) {
+            const unsigned grid = grid_cap(ceil_div(c.nnz, 256));
+            k_update_coo_scalar<Op><<<grid, 256, 0, s>>>(op, c.indices, c.d_nnz, c.nnz,
+                                                         rows * cols, c.values);
+            SPOPT_LAUNCHED();
+            return SPOPT_OK;
+        }
+        const bool vec_ok = state_aligned && (cols & 3) == 0 && aligned16(c.values);
+        return launch_rows(op, SrcBlockCoo{c.indices, cols}, c.d_nnz, c.nnz, rows, cols, c.values,
+                           vec_ok, s);
+    }
+    const spopt_csr& c = gr->csr;
+    if (c.touched_rows) {
+        if (c.n_touched == 0) return SPOPT_OK;
+        const bool vec_ok = state_aligned && (cols & 3) == 0 && aligned16(c.values);
+        return launch_rows(op, SrcCsrTouched{c.touched_rows, c.row_offsets, c.col_indices, rows},
+                           c.d_n_touched, c.n_touched, rows, cols, c.values, vec_ok, s);
+    }
+    const unsigned grid = grid_cap(ceil_div(ceil_div(rows, kWave), 4));
+    k_update_csr_scan<Op><<<grid, 256, 0, s>>>(op, c.row_offsets, c.col_indices, rows, cols,
+                                               c.values);
+    SPOPT_LAUNCHED();
+    return SPOPT_OK;
+}
+
+int launch_adam(float* p, float* m, float* v, int32_t* ls, const AdamScalars& a, int mode,
+                const spopt_grad* gr, int64_t rows, int64_t cols, hipStream_t s) {
+    const bool al = aligned16(p) && aligned16(m) && aligned16(v) && aligned16(ls);
+    if (mode == SPOPT_MODE_DORMANCY)
+        return launch_update(AdamOp<SPOPT_MODE_DORMANCY>{p, m, v, ls, a}, al, gr, rows, cols, s);
+    return launch_update(AdamOp<SPOPT_MODE_LAZY>{p, m, v, ls, a}, al, gr, rows, cols, s);
+}
+
+int launch_sgd(float* p, float* b, float lr, float mu, float wd, const spopt_grad* gr,
+               int64_t rows, int64_t cols, hipStream_t s) {
+    if (mu != 0.f && b != nullptr) {
+        const bool al = aligned16(p) && aligned16(b);
+        return launch_update(SgdOp<true>{p, b, lr, mu, wd}, al, gr, rows, cols, s);
+    }
+    return launch_update(SgdOp<false>{p, nullptr, lr, 0.f, wd}, aligned16(p), gr, rows, cols, s);
+}
+
+}  // namespace spopt

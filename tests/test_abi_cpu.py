@@ -1,0 +1,104 @@
+"""CPU-side checks of the C ABI: the library loads, exports every entry point
+declared in include/*.h, and rejects bad host-side arguments without touching
+a device."""
+import ctypes as C
+import glob
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+import lazy_optimizer_step_amd as L
+from lazy_optimizer_step_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        for m in re.finditer(r"^SPOPT_API\s+[\w\s\*]+?\b(\w+)\s*\(", text, flags=re.M):
+            names.add(m.group(1))
+    return names
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 11
+    lib = C.CDLL(_lib.LIB_PATH)
+    for n in sorted(names):
+        assert hasattr(lib, n), n
+    assert names == set(_lib.EXPORTED)
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert exported == names
+
+
+def test_workspace_size():
+    assert L.sparse_opt_workspace_size(65536, 128, 10_000_000) > 65536 * 16
+    assert L.sparse_opt_workspace_size(0, 1, 1) >= 0
+    for bad in [(-1, 1, 1), (10, 0, 5), (10, 1, 0), (1 << 30, 1, 1 << 40)]:
+        with pytest.raises(L.SparseOptError) as e:
+            L.sparse_opt_workspace_size(*bad)
+        assert e.value.code == _lib.EINVAL
+
+
+FAKE = 256  # a non-NULL address that create() stores but never dereferences
+
+
+@pytest.mark.parametrize("cfg", [
+    _lib.AdamConfig(1e-3, 1.0, 0.999, 1e-8, 1), _lib.AdamConfig(1e-3, 0.9, -0.1, 1e-8, 1),
+    _lib.AdamConfig(1e-3, 0.9, 0.999, 0.0, 1), _lib.AdamConfig(-1.0, 0.9, 0.999, 1e-8, 1),
+    _lib.AdamConfig(1e-3, 0.9, 0.999, 1e-8, 7)])
+def test_create_rejects_bad_adam_config(cfg):
+    h = C.c_void_p()
+    rc = _lib.lib().sparse_opt_create(C.byref(h), _lib.KIND_ADAM, C.byref(cfg), 10, 4, FAKE, FAKE,
+                                      FAKE, FAKE)
+    assert rc == _lib.EINVAL and not h.value
+    assert _lib.lib().sparse_opt_last_error()
+
+
+@pytest.mark.parametrize("cfg", [_lib.SgdConfig(-0.1, 0.9, 0.0), _lib.SgdConfig(0.1, 1.0, 0.0),
+                                 _lib.SgdConfig(0.1, 0.5, -1e-4)])
+def test_create_rejects_bad_sgd_config(cfg):
+    h = C.c_void_p()
+    rc = _lib.lib().sparse_opt_create(C.byref(h), _lib.KIND_SGD, C.byref(cfg), 10, 4, FAKE, FAKE,
+                                      None, None)
+    assert rc == _lib.EINVAL
+
+
+def test_handle_step_counter_and_shape_errors():
+    L_ = _lib.lib()
+    h = C.c_void_p()
+    cfg = _lib.AdamConfig(1e-3, 0.9, 0.999, 1e-8, 1)
+    assert L_.sparse_opt_create(C.byref(h), _lib.KIND_ADAM, C.byref(cfg), 10, 4, FAKE, FAKE, FAKE,
+                                FAKE) == 0
+    try:
+        assert L_.sparse_opt_get_step(h) == 0
+        assert L_.sparse_opt_set_step(h, 41) == 0 and L_.sparse_opt_get_step(h) == 41
+        assert L_.sparse_opt_set_step(h, -1) == _lib.EINVAL
+        assert L_.sparse_opt_set_step(h, 1 << 31) == _lib.EINVAL
+        # Shape errors are found on the host, before any device work.
+        g = _lib.Grad(_lib.FORMAT_COO, _lib.Coo(11, 4, 0, None, FAKE, FAKE), _lib.Csr())
+        assert L_.sparse_adam_step(h, C.byref(g), None, 0) == _lib.ESHAPE
+        g = _lib.Grad(_lib.FORMAT_CSR, _lib.Coo(), _lib.Csr(10, 5, FAKE, None, FAKE, None, 0, None))
+        assert L_.sparse_adam_step(h, C.byref(g), None, 0) == _lib.ESHAPE
+        g = _lib.Grad(9, _lib.Coo(), _lib.Csr())
+        assert L_.sparse_adam_step(h, C.byref(g), None, 0) == _lib.EINVAL
+        assert L_.sparse_sgd_step(h, C.byref(g), None, 0) == _lib.EINVAL   # wrong kind
+        assert L_.sparse_opt_get_step(h) == 41
+        assert L_.sparse_opt_set_step(h, (1 << 31) - 2) == 0
+        g = _lib.Grad(_lib.FORMAT_COO, _lib.Coo(10, 4, 0, None, FAKE, FAKE), _lib.Csr())
+        assert L_.sparse_adam_step(h, C.byref(g), None, 0) == _lib.EINVAL   # t would hit 2^31
+    finally:
+        L_.sparse_opt_destroy(h)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True)
+    assert r.returncode == 2 and "one GPU" in r.stderr

@@ -1,0 +1,172 @@
+"""GPU parity of canonicalisation and COO <-> CSR against the oracle.
+
+Integer outputs (distinct keys, U, multiplicities, row_offsets, col_indices,
+linear indices) must match bit for bit; duplicate sums within the float32
+summation bound (the order of a float32 sum is not fixed by the pages).
+Pages: optirs_gpu sparse_optimizer, "Sparse gradient representations";
+DiskSparseAdam README, "Safe Duplicate Aggregation & Sorted I/O".
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import lazy_optimizer_step_amd as L
+import oracle
+from tests.gpu_util import assert_sums_close, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(ids, vals, key_space, validate=False):
+    n = len(ids)
+    keys, sums, counts, U = L.coo_from_lookups(dev(ids), dev(vals.reshape(n, -1) if n else vals),
+                                               key_space, validate=validate)
+    torch.cuda.synchronize()
+    u = int(host(U)[0])
+    return host(keys)[:u], host(sums)[:u], host(counts)[:u], u
+
+
+CASES = [
+    # (name, n, key_space, width, hot_fraction)
+    ("single", 1, 10, 4, 0.0),
+    ("key_space_1", 300, 1, 3, 0.0),
+    ("two_passes", 5000, 200, 1, 0.0),
+    ("ragged_width3", 3333, 70000, 3, 0.0),
+    ("width64_zipfish", 8192, 1_000_000, 64, 0.2),
+    ("width128_heavy", 20000, 10_000_000, 128, 0.6),
+    ("width256", 4100, 2_000_000, 256, 0.1),
+    ("width1_heavy", 70000, 5000, 1, 0.7),
+    ("four_passes", 2048, 1 << 30, 2, 0.0),
+    ("33bit_keys", 1500, 6_400_000_000, 1, 0.3),
+    ("all_distinct", 4096, 4096, 8, 0.0),
+]
+
+
+@pytest.mark.parametrize("name,n,key_space,width,hot", CASES, ids=[c[0] for c in CASES])
+def test_coo_from_lookups_matches_oracle(name, n, key_space, width, hot):
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    ids = rng.integers(0, key_space, size=n, dtype=np.int64)
+    if hot:
+        ids[rng.random(n) < hot] = key_space - 1      # one long segment at the last key
+    vals = rng.standard_normal((n, width)).astype(np.float32)
+    gk, gv, gc, u = _run(ids, vals, key_space)
+    ok, ov, oc = oracle.coo_from_lookups(ids, vals, key_space)
+    assert u == ok.size
+    assert np.array_equal(gk, ok) and np.array_equal(gc, oc)
+    assert_sums_close(gv, ov, ids, ok, oc, vals)
+
+
+def test_empty_lookups():
+    keys, sums, counts, U = L.coo_from_lookups(dev(np.zeros(0, np.int64)),
+                                               dev(np.zeros((0, 4), np.float32)), 10)
+    torch.cuda.synchronize()
+    assert int(host(U)[0]) == 0
+
+
+def test_deterministic_run_to_run():
+    rng = np.random.default_rng(1)
+    ids = np.minimum(rng.zipf(1.3, size=30000) - 1, 99999).astype(np.int64)
+    vals = rng.standard_normal((30000, 128)).astype(np.float32)
+    a = _run(ids, vals, 100000)
+    b = _run(ids, vals, 100000)
+    for x, y in zip(a[:3], b[:3]):
+        assert x.tobytes() == y.tobytes()
+
+
+def test_zero_sum_duplicates_stay_present():
+    ids = np.array([4, 4, 2], np.int64)
+    vals = np.array([[1.5], [-1.5], [0.0]], np.float32)
+    gk, gv, gc, u = _run(ids, vals, 8)
+    assert gk.tolist() == [2, 4] and gc.tolist() == [1, 2] and gv.reshape(-1).tolist() == [0, 0]
+
+
+def test_validate_range_and_nonfinite():
+    vals = np.ones((3, 2), np.float32)
+    with pytest.raises(L.SparseOptError) as e:
+        _run(np.array([0, 7, 2], np.int64), vals, 5, validate=True)
+    assert e.value.code == oracle.ERANGE
+    with pytest.raises(L.SparseOptError) as e:
+        _run(np.array([0, -1, 2], np.int64), vals, 5, validate=True)
+    assert e.value.code == oracle.ERANGE
+    bad = vals.copy()
+    bad[1, 1] = np.inf
+    with pytest.raises(L.SparseOptError) as e:
+        _run(np.array([0, 1, 2], np.int64), bad, 5, validate=True)
+    assert e.value.code == oracle.ENONFINITE
+
+
+def test_trusted_out_of_range_gives_empty_result():
+    gk, gv, gc, u = _run(np.array([0, 9, 2], np.int64), np.ones((3, 2), np.float32), 5)
+    assert u == 0
+
+
+def test_workspace_too_small():
+    ids = dev(np.arange(100, dtype=np.int64))
+    vals = dev(np.ones((100, 4), np.float32))
+    with pytest.raises(L.SparseOptError) as e:
+        L.coo_from_lookups(ids, vals, 100, workspace=torch.empty(16, dtype=torch.uint8,
+                                                                   device="cuda"))
+    assert e.value.code == oracle.EWORKSPACE
+
+
+# ---------------------------------------------------------------------------
+# COO <-> CSR
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("rows,cols,n", [(1000, 64, 3000), (50000, 128, 20000), (7, 4, 30),
+                                         (9000, 3, 500)])
+def test_csr_from_full_row_coo(rows, cols, n):
+    rng = np.random.default_rng(rows)
+    ids = rng.integers(0, rows, size=n, dtype=np.int64)
+    ids[:5] = rows - 1
+    vals = rng.standard_normal((n, cols)).astype(np.float32)
+    keys, sums, counts, U = L.coo_from_lookups(dev(ids), dev(vals), rows)
+    coo = L.CooGradient(keys, sums, dim=rows, width=cols, nnz=n, d_nnz=U)
+    csr = L.csr_from_coo(coo, rows, cols)
+    torch.cuda.synchronize()
+    u = int(host(U)[0])
+    ok, ov, oc = oracle.coo_from_lookups(ids, vals, rows)
+    ro, ci, cv = oracle.csr_from_coo(ok, ov, rows, cols, rows, cols)
+    assert np.array_equal(host(csr.row_offsets), ro)
+    assert np.array_equal(host(csr.col_indices)[:u * cols], ci)
+    assert np.array_equal(host(csr.touched_rows)[:u], ok)
+    assert np.array_equal(host(csr.values)[:u * cols], host(sums)[:u].reshape(-1))
+
+
+@pytest.mark.parametrize("rows,cols,nnz", [(2000, 256, 40000), (300, 7, 900), (5000, 1, 1200),
+                                           (1, 16, 16), (64, 8, 0)])
+def test_csr_from_scalar_coo_and_back(rows, cols, nnz):
+    rng = np.random.default_rng(nnz + rows)
+    lin = np.sort(rng.choice(rows * cols, size=nnz, replace=False)).astype(np.int64)
+    vals = rng.standard_normal(nnz).astype(np.float32)
+    coo = L.CooGradient(dev(lin) if nnz else torch.zeros(1, dtype=torch.int64, device="cuda"),
+                        dev(vals) if nnz else torch.zeros(1, device="cuda"), dim=rows * cols,
+                        width=1, nnz=nnz)
+    csr = L.csr_from_coo(coo, rows, cols)
+    torch.cuda.synchronize()
+    ro, ci, cv = oracle.csr_from_coo(lin, vals, rows * cols, 1, rows, cols)
+    assert np.array_equal(host(csr.row_offsets), ro)
+    assert np.array_equal(host(csr.col_indices)[:nnz], ci)
+    assert np.array_equal(host(csr.values)[:nnz], cv)
+    back = L.csr_to_coo(csr)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(back.indices)[:nnz], lin)
+    assert np.array_equal(host(back.values)[:nnz], vals)
+
+
+def test_csr_validate_errors():
+    lin = dev(np.array([5, 2], np.int64))
+    v = dev(np.ones(2, np.float32))
+    with pytest.raises(L.SparseOptError) as e:
+        L.csr_from_coo(L.CooGradient(lin, v, dim=40, width=1), 10, 4, validate=True)
+    assert e.value.code == oracle.ENOTCANON
+    with pytest.raises(L.SparseOptError) as e:
+        L.csr_from_coo(L.CooGradient(lin, v, dim=39, width=1), 10, 4)
+    assert e.value.code == oracle.ESHAPE
+    bad = L.CsrGradient(dev(np.array([0, 2, 2], np.int32)), dev(np.array([3, 1], np.int32)),
+                        v, rows=2, cols=4)
+    with pytest.raises(L.SparseOptError) as e:
+        L.csr_to_coo(bad, validate=True)
+    assert e.value.code == oracle.ENOTCANON
