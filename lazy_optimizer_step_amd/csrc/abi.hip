@@ -4,8 +4,8 @@
 // The handle holds the configuration and the global step t (optirs_gpu
 // sparse_optimizer page: bias correction uses the number of step calls so
 // far, never a per-coordinate count).  Each step computes, in double, the
-// scalars that depend only on t and the hyper-parameters and rounds each once
-// to float for the kernels.
+// scalars that depend only on t and the hyper-parameters; an Adam handle also
+// keeps a device table of beta^k (k < kPowTable) built with the host's pow().
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -91,6 +91,7 @@ struct spopt_optimizer {
     float* v;
     int32_t* ls;
     int64_t t;
+    double* d_pow;  // device [2 * kPowTable]: beta1^k then beta2^k (Adam only)
 };
 
 static int check_adam_config(const spopt_adam_config* c) {
@@ -150,13 +151,37 @@ extern "C" int sparse_opt_create(spopt_t* out, int32_t kind, const void* config,
     } else {
         return fail(SPOPT_EINVAL, "create: unknown kind %d", kind);
     }
+    h.d_pow = nullptr;
+    if (kind == SPOPT_KIND_ADAM) {
+        // beta^k for short dormancy gaps, from the host's pow() in double.
+        std::vector<double> tab(2 * (size_t)kPowTable);
+        for (int k = 0; k < kPowTable; ++k) {
+            tab[(size_t)k] = pow(h.adam.beta1, (double)k);
+            tab[(size_t)kPowTable + (size_t)k] = pow(h.adam.beta2, (double)k);
+        }
+        void* d = nullptr;
+        SPOPT_HIP(hipMalloc(&d, tab.size() * sizeof(double)));
+        if (hipMemcpy(d, tab.data(), tab.size() * sizeof(double), hipMemcpyHostToDevice) !=
+            hipSuccess) {
+            (void)hipFree(d);
+            return fail(SPOPT_EDEVICE, "create: copying the power table failed");
+        }
+        h.d_pow = (double*)d;
+    }
     spopt_optimizer* p = new (std::nothrow) spopt_optimizer(h);
-    if (p == nullptr) return fail(SPOPT_EINVAL, "create: out of host memory");
+    if (p == nullptr) {
+        if (h.d_pow) (void)hipFree(h.d_pow);
+        return fail(SPOPT_EINVAL, "create: out of host memory");
+    }
     *out = p;
     return SPOPT_OK;
 }
 
-extern "C" void sparse_opt_destroy(spopt_t h) { delete h; }
+extern "C" void sparse_opt_destroy(spopt_t h) {
+    if (h == nullptr) return;
+    if (h->d_pow) (void)hipFree(h->d_pow);
+    delete h;
+}
 
 extern "C" int64_t sparse_opt_get_step(spopt_t h) { return h ? h->t : -1; }
 
@@ -221,16 +246,18 @@ extern "C" int sparse_adam_step(spopt_t h, const spopt_grad* g, void* stream, ui
     }
     const spopt_adam_config& c = h->adam;
     AdamScalars a;
-    a.lr = (float)c.lr;
-    a.c1 = (float)(1.0 - c.beta1);
-    a.c2 = (float)(1.0 - c.beta2);
-    a.inv_bc1 = (float)(1.0 / (1.0 - pow(c.beta1, (double)t)));
-    a.inv_bc2 = (float)(1.0 / (1.0 - pow(c.beta2, (double)t)));
-    a.eps = (float)c.eps;
-    a.beta1 = (float)c.beta1;
-    a.beta2 = (float)c.beta2;
-    a.l2b1 = (float)log2(c.beta1);
-    a.l2b2 = (float)log2(c.beta2);
+    a.lr = c.lr;
+    a.c1 = 1.0 - c.beta1;
+    a.c2 = 1.0 - c.beta2;
+    a.bc1 = 1.0 - pow(c.beta1, (double)t);
+    a.bc2 = 1.0 - pow(c.beta2, (double)t);
+    a.eps = c.eps;
+    a.beta1 = c.beta1;
+    a.beta2 = c.beta2;
+    a.l2b1 = log2(c.beta1);
+    a.l2b2 = log2(c.beta2);
+    a.pow1 = h->d_pow;
+    a.pow2 = h->d_pow + kPowTable;
     a.t = (int32_t)t;
     rc = launch_adam(h->p, h->m, h->v, h->ls, a, c.mode, g, h->rows, h->cols, s);
     if (rc) return rc;
@@ -251,8 +278,7 @@ extern "C" int sparse_sgd_step(spopt_t h, const spopt_grad* g, void* stream, uin
         if (rc) return rc;
     }
     const spopt_sgd_config& c = h->sgd;
-    rc = launch_sgd(h->p, h->m, (float)c.lr, (float)c.momentum, (float)c.weight_decay, g,
-                    h->rows, h->cols, s);
+    rc = launch_sgd(h->p, h->m, c.lr, c.momentum, c.weight_decay, g, h->rows, h->cols, s);
     if (rc) return rc;
     h->t = t;
     return SPOPT_OK;

@@ -9,10 +9,10 @@
 //      ids keep lookup order);
 //   2. mark segment heads (id differs from its predecessor), scan them to give
 //      every lookup its segment number and emit the distinct ids;
-//   3. sum each segment's value rows in a fixed order: fixed chunks of 64
-//      sorted lookups per wave, partial sums for segments that cross a chunk
-//      boundary, then an ordered combine of those partials.  No float atomics,
-//      so the result is the same run to run.
+//   3. sum each segment's value rows in double, in a fixed order, and round
+//      once: fixed chunks of 64 sorted lookups per wave, partial sums for
+//      segments that cross a chunk boundary, then an ordered combine of those
+//      partials.  No atomics, so the result is the same run to run.
 #include <stdarg.h>
 #include <stdio.h>
 
@@ -63,8 +63,8 @@ static bool canon_layout(int64_t n, int64_t width, int64_t key_space, CanonLayou
     L->off_blk = take(sizeof(uint32_t) * ((size_t)L->nblk_seg + 1));
     L->off_segid = take(sizeof(int32_t) * (size_t)n);
     L->off_segstart = take(sizeof(int32_t) * ((size_t)n + 1));
-    L->off_pfirst = take(sizeof(float) * (size_t)L->nchunks * (size_t)width);
-    L->off_plast = take(sizeof(float) * (size_t)L->nchunks * (size_t)width);
+    L->off_pfirst = take(sizeof(double) * (size_t)L->nchunks * (size_t)width);
+    L->off_plast = take(sizeof(double) * (size_t)L->nchunks * (size_t)width);
     L->off_status = take(sizeof(uint32_t) * 4);
     L->total = o;
     return true;
@@ -276,18 +276,11 @@ __global__ __launch_bounds__(256) void k_seg_emit(const uint64_t* __restrict__ s
 
 // ----------------------------------------------------------- dup sums ---
 
-// V-wide row access: vector loads when the row layout allows, scalar with a
-// column bound otherwise.
+// V-wide access to a row of floats: a vector load when the layout allows, a
+// scalar loop with a column bound otherwise.
 template <int V>
-__device__ __forceinline__ bool aligned_v(const void* a, const void* b, const void* c,
-                                          const void* d) {
-    const uintptr_t m = (uintptr_t)(V * sizeof(float)) - 1u;
-    return (((uintptr_t)a | (uintptr_t)b | (uintptr_t)c | (uintptr_t)d) & m) == 0;
-}
-
-template <int V>
-__device__ __forceinline__ void load_v(float (&r)[V], const float* src, int64_t col,
-                                       int64_t width, bool vec) {
+__device__ __forceinline__ void load_row(float (&r)[V], const float* src, int64_t col,
+                                         int64_t width, bool vec) {
     if (V == 4 && vec && col < width) {
         const float4 x = *reinterpret_cast<const float4*>(src);
         r[0] = x.x; r[1 % V] = x.y; r[2 % V] = x.z; r[3 % V] = x.w;
@@ -301,17 +294,34 @@ __device__ __forceinline__ void load_v(float (&r)[V], const float* src, int64_t 
 }
 
 template <int V>
-__device__ __forceinline__ void store_v(float* dst, const float (&r)[V], int64_t col,
-                                        int64_t width, bool vec) {
+__device__ __forceinline__ void store_row(float* dst, const double (&r)[V], int64_t col,
+                                          int64_t width, bool vec) {
     if (V == 4 && vec && col < width) {
-        *reinterpret_cast<float4*>(dst) = make_float4(r[0], r[1 % V], r[2 % V], r[3 % V]);
+        *reinterpret_cast<float4*>(dst) =
+            make_float4((float)r[0], (float)r[1 % V], (float)r[2 % V], (float)r[3 % V]);
     } else if (V == 2 && vec && col < width) {
-        *reinterpret_cast<float2*>(dst) = make_float2(r[0], r[1 % V]);
+        *reinterpret_cast<float2*>(dst) = make_float2((float)r[0], (float)r[1 % V]);
     } else {
 #pragma unroll
         for (int v = 0; v < V; ++v)
-            if (col + v < width) dst[v] = r[v];
+            if (col + v < width) dst[v] = (float)r[v];
     }
+}
+
+// Partial sums of segments that cross a chunk boundary stay in double.
+template <int V>
+__device__ __forceinline__ void load_part(double (&r)[V], const double* src, int64_t col,
+                                          int64_t width) {
+#pragma unroll
+    for (int v = 0; v < V; ++v) r[v] = (col + v < width) ? src[v] : 0.0;
+}
+
+template <int V>
+__device__ __forceinline__ void store_part(double* dst, const double (&r)[V], int64_t col,
+                                           int64_t width) {
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+        if (col + v < width) dst[v] = r[v];
 }
 
 // Destination of the running sum when item j of a chunk closes it.
@@ -347,13 +357,14 @@ __device__ __forceinline__ ChunkItem chunk_item(const uint64_t* s, const int32_t
 }
 
 // One wave per chunk of 64 sorted lookups, value rows of `width` floats; each
-// lane owns V consecutive columns of every 64*V-column block.
+// lane owns V consecutive columns of every 64*V-column block and accumulates
+// them in double, in sorted (= lookup) order within the chunk.
 template <int V>
 __global__ __launch_bounds__(256) void k_dupsum_rows(
     const uint64_t* __restrict__ s, const int32_t* __restrict__ seg_id,
     const int32_t* __restrict__ seg_start, int64_t n, int pos_bits,
     const float* __restrict__ vals, int64_t width, float* __restrict__ out_vals,
-    int32_t* __restrict__ out_counts, float* __restrict__ pfirst, float* __restrict__ plast,
+    int32_t* __restrict__ out_counts, double* __restrict__ pfirst, double* __restrict__ plast,
     const uint32_t* status) {
     if (*status != 0u) return;
     const int lane = lane_id();
@@ -364,12 +375,14 @@ __global__ __launch_bounds__(256) void k_dupsum_rows(
     const ChunkItem it = chunk_item(s, seg_id, seg_start, n, pos_bits, i0, cnt, lane);
     if (it.ends) out_counts[it.seg] = (int32_t)(i0 + lane + 1 - seg_start[it.seg]);
 
-    const bool vec = (V > 1) && (width % V == 0) && aligned_v<V>(vals, out_vals, pfirst, plast);
+    const uintptr_t vmask = (uintptr_t)(V * sizeof(float)) - 1u;
+    const bool vec = (V > 1) && (width % V == 0) &&
+                     ((((uintptr_t)vals) | ((uintptr_t)out_vals)) & vmask) == 0;
     for (int64_t c0 = 0; c0 < width; c0 += (int64_t)kWave * V) {
         const int64_t col = c0 + (int64_t)lane * V;
-        float acc[V];
+        double acc[V];
 #pragma unroll
-        for (int v = 0; v < V; ++v) acc[v] = 0.f;
+        for (int v = 0; v < V; ++v) acc[v] = 0.0;
         for (int j0 = 0; j0 < cnt; j0 += 8) {
             float row[8][V];
 #pragma unroll
@@ -377,8 +390,7 @@ __global__ __launch_bounds__(256) void k_dupsum_rows(
                 const int j = j0 + u;
                 if (j < cnt) {
                     const uint32_t pos = read_lane(it.pos, j);
-                    const float* src = vals + (int64_t)pos * width + col;
-                    load_v<V>(row[u], src, col, width, vec);
+                    load_row<V>(row[u], vals + (int64_t)pos * width + col, col, width, vec);
                 }
             }
 #pragma unroll
@@ -386,19 +398,18 @@ __global__ __launch_bounds__(256) void k_dupsum_rows(
                 const int j = j0 + u;
                 if (j < cnt) {
 #pragma unroll
-                    for (int v = 0; v < V; ++v) acc[v] += row[u][v];
+                    for (int v = 0; v < V; ++v) acc[v] += (double)row[u][v];
                     const int kind = read_lane(it.kind, j);
                     if (kind != kFlushNone) {
-                        float* dst;
                         if (kind == kFlushOut)
-                            dst = out_vals + (int64_t)read_lane(it.seg, j) * width;
+                            store_row<V>(out_vals + (int64_t)read_lane(it.seg, j) * width + col,
+                                         acc, col, width, vec);
                         else if (kind == kFlushFirst)
-                            dst = pfirst + chunk * width;
+                            store_part<V>(pfirst + chunk * width + col, acc, col, width);
                         else
-                            dst = plast + chunk * width;
-                        store_v<V>(dst + col, acc, col, width, vec);
+                            store_part<V>(plast + chunk * width + col, acc, col, width);
 #pragma unroll
-                        for (int v = 0; v < V; ++v) acc[v] = 0.f;
+                        for (int v = 0; v < V; ++v) acc[v] = 0.0;
                     }
                 }
             }
@@ -406,12 +417,12 @@ __global__ __launch_bounds__(256) void k_dupsum_rows(
     }
 }
 
-// Width 1: one lookup per lane, segmented inclusive scan across the wave.
+// Width 1: one lookup per lane, segmented inclusive scan (double) across the wave.
 __global__ __launch_bounds__(256) void k_dupsum_scalar(
     const uint64_t* __restrict__ s, const int32_t* __restrict__ seg_id,
     const int32_t* __restrict__ seg_start, int64_t n, int pos_bits,
     const float* __restrict__ vals, float* __restrict__ out_vals,
-    int32_t* __restrict__ out_counts, float* __restrict__ pfirst, float* __restrict__ plast,
+    int32_t* __restrict__ out_counts, double* __restrict__ pfirst, double* __restrict__ plast,
     const uint32_t* status) {
     if (*status != 0u) return;
     const int lane = lane_id();
@@ -421,12 +432,12 @@ __global__ __launch_bounds__(256) void k_dupsum_scalar(
     const int cnt = (int)((n - i0) < kChunk ? (n - i0) : kChunk);
     const ChunkItem it = chunk_item(s, seg_id, seg_start, n, pos_bits, i0, cnt, lane);
     if (it.ends) out_counts[it.seg] = (int32_t)(i0 + lane + 1 - seg_start[it.seg]);
-    float x = lane < cnt ? vals[it.pos] : 0.f;
+    double x = lane < cnt ? (double)vals[it.pos] : 0.0;
     const int prev_seg = __shfl_up(it.seg, 1, kWave);
     bool f = lane == 0 || prev_seg != it.seg;  // first lookup of its segment in this chunk
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
-        const float y = __shfl_up(x, off, kWave);
+        const double y = __shfl_up(x, off, kWave);
         const bool g = __shfl_up((int)f, off, kWave) != 0;
         if (lane >= off && !f) {
             x = y + x;
@@ -434,7 +445,7 @@ __global__ __launch_bounds__(256) void k_dupsum_scalar(
         }
     }
     if (it.kind == kFlushOut)
-        out_vals[it.seg] = x;
+        out_vals[it.seg] = (float)x;
     else if (it.kind == kFlushFirst)
         pfirst[chunk] = x;
     else if (it.kind == kFlushLast)
@@ -442,11 +453,11 @@ __global__ __launch_bounds__(256) void k_dupsum_scalar(
 }
 
 // Segments that cross chunk boundaries: the wave of the chunk where such a
-// segment starts adds its partials in chunk order.
+// segment starts adds its partials in chunk order and rounds once.
 template <int V>
 __global__ __launch_bounds__(256) void k_dupsum_fixup(
     const int32_t* __restrict__ seg_id, const int32_t* __restrict__ seg_start, int64_t n,
-    const float* __restrict__ pfirst, const float* __restrict__ plast, int64_t width,
+    const double* __restrict__ pfirst, const double* __restrict__ plast, int64_t width,
     float* __restrict__ out_vals, const uint32_t* status) {
     if (*status != 0u) return;
     const int lane = lane_id();
@@ -458,17 +469,18 @@ __global__ __launch_bounds__(256) void k_dupsum_fixup(
     const int64_t s0 = seg_start[seg], s1 = seg_start[seg + 1];
     if (!(s0 >= i0 && s1 > i0 + kChunk)) return;
     const int64_t ce = (s1 - 1) / kChunk;
-    const bool vec = (V > 1) && (width % V == 0) && aligned_v<V>(pfirst, plast, out_vals, out_vals);
+    const uintptr_t vmask = (uintptr_t)(V * sizeof(float)) - 1u;
+    const bool vec = (V > 1) && (width % V == 0) && (((uintptr_t)out_vals) & vmask) == 0;
     for (int64_t c0 = 0; c0 < width; c0 += (int64_t)kWave * V) {
         const int64_t col = c0 + (int64_t)lane * V;
-        float acc[V], row[V];
-        load_v<V>(acc, plast + chunk * width + col, col, width, vec);
+        double acc[V], row[V];
+        load_part<V>(acc, plast + chunk * width + col, col, width);
         for (int64_t c = chunk + 1; c <= ce; ++c) {
-            load_v<V>(row, pfirst + c * width + col, col, width, vec);
+            load_part<V>(row, pfirst + c * width + col, col, width);
 #pragma unroll
             for (int v = 0; v < V; ++v) acc[v] += row[v];
         }
-        store_v<V>(out_vals + (int64_t)seg * width + col, acc, col, width, vec);
+        store_row<V>(out_vals + (int64_t)seg * width + col, acc, col, width, vec);
     }
 }
 
@@ -528,8 +540,8 @@ extern "C" int coo_from_lookups(const int64_t* ids, const float* vals, int64_t n
     uint32_t* blk = (uint32_t*)(ws + L.off_blk);
     int32_t* seg_id = (int32_t*)(ws + L.off_segid);
     int32_t* seg_start = (int32_t*)(ws + L.off_segstart);
-    float* pfirst = (float*)(ws + L.off_pfirst);
-    float* plast = (float*)(ws + L.off_plast);
+    double* pfirst = (double*)(ws + L.off_pfirst);
+    double* plast = (double*)(ws + L.off_plast);
     uint32_t* status = (uint32_t*)(ws + L.off_status);
 
     if (n == 0) {

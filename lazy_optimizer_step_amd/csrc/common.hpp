@@ -144,14 +144,19 @@ int launch_check_coo(const spopt_coo* c, int check_finite, const int32_t* ls, in
 int launch_check_csr(const spopt_csr* c, int check_finite, const int32_t* ls, int32_t t,
                      uint32_t* status, hipStream_t s);
 
-// Per-step scalars of Adam, each formed in double on the host and rounded once.
+// beta^gap for gap < kPowTable comes from a table built on the host with pow().
+constexpr int kPowTable = 1024;
+
+// Per-step scalars of Adam, formed in double on the host.
 struct AdamScalars {
-    float lr, c1, c2, inv_bc1, inv_bc2, eps, beta1, beta2, l2b1, l2b2;
+    double lr, c1, c2, bc1, bc2, eps, beta1, beta2, l2b1, l2b2;
+    const double* pow1;  // device [kPowTable]: beta1^k
+    const double* pow2;  // device [kPowTable]: beta2^k
     int32_t t;
 };
 int launch_adam(float* p, float* m, float* v, int32_t* ls, const AdamScalars& a, int mode,
                 const spopt_grad* gr, int64_t rows, int64_t cols, hipStream_t s);
-int launch_sgd(float* p, float* b, float lr, float mu, float wd, const spopt_grad* gr,
+int launch_sgd(float* p, float* b, double lr, double mu, double wd, const spopt_grad* gr,
                int64_t rows, int64_t cols, hipStream_t s);
 
 // A validated call: serialised with every other validated call of the

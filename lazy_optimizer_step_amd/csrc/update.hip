@@ -7,9 +7,14 @@
 //     p -= lr * (m/(1-beta1^t)) / (sqrt(v/(1-beta2^t)) + eps),  last_step = t
 //   SGD, section "Sparse SGD": g' = g + wd*p; with momentum b = mu*b + g',
 //     p -= lr*b; without, p -= lr*g'.
-// Every scalar that depends only on the hyper-parameters and t (1 - beta,
-// 1/(1 - beta^t), log2 beta) is formed in double on the host and passed
-// rounded to float.  beta^gap is exp2(gap * log2 beta), exact beta for gap 1.
+// Arithmetic is double with contraction off, state loaded from and rounded
+// once back to float32: the same operations in the same order as the CPU
+// oracle, so results agree bit for bit except where beta^gap comes from exp2
+// (gaps beyond the pow() table) or a duplicate sum rounds differently.  On
+// gfx950 a double FMA issues at the rate of an unpacked float FMA, and the
+// kernels are bound by HBM, not by the ALUs.  Scalars that depend only on the
+// hyper-parameters and t (1 - beta, 1 - beta^t, beta^gap for short gaps) are
+// computed on the host in double.
 //
 // Work mapping: LPR lanes per touched row, 64/LPR rows per wave.  A full row
 // (all cols entries present) is moved with 16-byte loads and stores of p, m,
@@ -34,22 +39,34 @@ struct AdamOp {
         int4 ls;
     };
 
+    // beta^gap: 1 step -> beta; shorter gaps from the host-built pow() table;
+    // longer ones exp2(gap * log2 beta).  Skipped when m = v = 0 (a coordinate
+    // never touched), where any finite factor gives the same zero.
+    __device__ __forceinline__ void decay(int32_t gap, double& d1, double& d2) const {
+        if (gap == 1) return;
+        if ((uint32_t)gap < (uint32_t)kPowTable) {
+            d1 = a.pow1[gap];
+            d2 = a.pow2[gap];
+        } else {
+            d1 = exp2((double)gap * a.l2b1);
+            d2 = exp2((double)gap * a.l2b2);
+        }
+    }
+
     __device__ __forceinline__ void coord(float& pp, float& mm, float& vv, int32_t last,
                                           float g) const {
-        float d1 = a.beta1, d2 = a.beta2;
-        if (MODE == SPOPT_MODE_DORMANCY) {
-            const int32_t gap = a.t - last;
-            if (gap != 1) {
-                const float fg = (float)gap;
-                d1 = exp2f(fg * a.l2b1);
-                d2 = exp2f(fg * a.l2b2);
-            }
-        }
-        mm = fmaf(d1, mm, a.c1 * g);
-        vv = fmaf(d2, vv, a.c2 * (g * g));
-        const float mh = mm * a.inv_bc1;
-        const float vh = vv * a.inv_bc2;
-        pp = pp - a.lr * mh / (sqrtf(vh) + a.eps);
+#pragma clang fp contract(off)
+        double d1 = a.beta1, d2 = a.beta2;
+        const double m0 = mm, v0 = vv, gd = g;
+        if (MODE == SPOPT_MODE_DORMANCY && (m0 != 0.0 || v0 != 0.0)) decay(a.t - last, d1, d2);
+        const double m1 = d1 * m0 + a.c1 * gd;
+        const double v1 = d2 * v0 + a.c2 * (gd * gd);
+        const double m_hat = m1 / a.bc1;
+        const double v_hat = v1 / a.bc2;
+        const double p1 = (double)pp - a.lr * m_hat / (sqrt(v_hat) + a.eps);
+        pp = (float)p1;
+        mm = (float)m1;
+        vv = (float)v1;
     }
 
     __device__ __forceinline__ void load(int64_t i, Vec& r) const {
@@ -88,19 +105,22 @@ template <bool MOM>
 struct SgdOp {
     float* __restrict__ p;
     float* __restrict__ b;
-    float lr, mu, wd;
+    double lr, mu, wd;
 
     struct Vec {
         float4 p, b;
     };
 
     __device__ __forceinline__ void coord(float& pp, float& bb, float g) const {
-        const float gg = fmaf(wd, pp, g);
+#pragma clang fp contract(off)
+        const double p0 = pp;
+        const double gg = (double)g + wd * p0;
         if (MOM) {
-            bb = fmaf(mu, bb, gg);
-            pp = fmaf(-lr, bb, pp);
+            const double b1 = mu * (double)bb + gg;
+            pp = (float)(p0 - lr * b1);
+            bb = (float)b1;
         } else {
-            pp = fmaf(-lr, gg, pp);
+            pp = (float)(p0 - lr * gg);
         }
     }
     __device__ __forceinline__ void load(int64_t i, Vec& r) const {
@@ -323,13 +343,13 @@ int launch_adam(float* p, float* m, float* v, int32_t* ls, const AdamScalars& a,
     return launch_update(AdamOp<SPOPT_MODE_LAZY>{p, m, v, ls, a}, al, gr, rows, cols, s);
 }
 
-int launch_sgd(float* p, float* b, float lr, float mu, float wd, const spopt_grad* gr,
+int launch_sgd(float* p, float* b, double lr, double mu, double wd, const spopt_grad* gr,
                int64_t rows, int64_t cols, hipStream_t s) {
-    if (mu != 0.f && b != nullptr) {
+    if (mu != 0.0 && b != nullptr) {
         const bool al = aligned16(p) && aligned16(b);
         return launch_update(SgdOp<true>{p, b, lr, mu, wd}, al, gr, rows, cols, s);
     }
-    return launch_update(SgdOp<false>{p, nullptr, lr, 0.f, wd}, aligned16(p), gr, rows, cols, s);
+    return launch_update(SgdOp<false>{p, nullptr, lr, 0.0, wd}, aligned16(p), gr, rows, cols, s);
 }
 
 }  // namespace spopt

@@ -72,11 +72,13 @@ def test_create_rejects_bad_sgd_config(cfg):
 
 
 def test_handle_step_counter_and_shape_errors():
+    # An SGD handle needs no device memory of its own (an Adam handle uploads a
+    # table of beta powers at creation), so this runs without a GPU.
     L_ = _lib.lib()
     h = C.c_void_p()
-    cfg = _lib.AdamConfig(1e-3, 0.9, 0.999, 1e-8, 1)
-    assert L_.sparse_opt_create(C.byref(h), _lib.KIND_ADAM, C.byref(cfg), 10, 4, FAKE, FAKE, FAKE,
-                                FAKE) == 0
+    cfg = _lib.SgdConfig(0.1, 0.9, 0.0)
+    assert L_.sparse_opt_create(C.byref(h), _lib.KIND_SGD, C.byref(cfg), 10, 4, FAKE, FAKE, None,
+                                None) == 0
     try:
         assert L_.sparse_opt_get_step(h) == 0
         assert L_.sparse_opt_set_step(h, 41) == 0 and L_.sparse_opt_get_step(h) == 41
@@ -84,16 +86,16 @@ def test_handle_step_counter_and_shape_errors():
         assert L_.sparse_opt_set_step(h, 1 << 31) == _lib.EINVAL
         # Shape errors are found on the host, before any device work.
         g = _lib.Grad(_lib.FORMAT_COO, _lib.Coo(11, 4, 0, None, FAKE, FAKE), _lib.Csr())
-        assert L_.sparse_adam_step(h, C.byref(g), None, 0) == _lib.ESHAPE
+        assert L_.sparse_sgd_step(h, C.byref(g), None, 0) == _lib.ESHAPE
         g = _lib.Grad(_lib.FORMAT_CSR, _lib.Coo(), _lib.Csr(10, 5, FAKE, None, FAKE, None, 0, None))
-        assert L_.sparse_adam_step(h, C.byref(g), None, 0) == _lib.ESHAPE
+        assert L_.sparse_sgd_step(h, C.byref(g), None, 0) == _lib.ESHAPE
         g = _lib.Grad(9, _lib.Coo(), _lib.Csr())
-        assert L_.sparse_adam_step(h, C.byref(g), None, 0) == _lib.EINVAL
-        assert L_.sparse_sgd_step(h, C.byref(g), None, 0) == _lib.EINVAL   # wrong kind
+        assert L_.sparse_sgd_step(h, C.byref(g), None, 0) == _lib.EINVAL
+        assert L_.sparse_adam_step(h, C.byref(g), None, 0) == _lib.EINVAL   # wrong kind
         assert L_.sparse_opt_get_step(h) == 41
         assert L_.sparse_opt_set_step(h, (1 << 31) - 2) == 0
         g = _lib.Grad(_lib.FORMAT_COO, _lib.Coo(10, 4, 0, None, FAKE, FAKE), _lib.Csr())
-        assert L_.sparse_adam_step(h, C.byref(g), None, 0) == _lib.EINVAL   # t would hit 2^31
+        assert L_.sparse_sgd_step(h, C.byref(g), None, 0) == _lib.EINVAL   # t would hit 2^31
     finally:
         L_.sparse_opt_destroy(h)
 
