@@ -43,6 +43,8 @@ int status_to_code(uint32_t bits, const char* what) {
     if (bits & kStatusNonFinite) return fail(SPOPT_ENONFINITE, "%s: non-finite gradient", what);
     if (bits & kStatusStep)
         return fail(SPOPT_EINVAL, "%s: a touched coordinate has last_step >= t", what);
+    if (bits & kStatusTimeout)
+        return fail(SPOPT_EDEVICE, "%s: a device-side wait timed out", what);
     return fail(SPOPT_EINVAL, "%s: status 0x%x", what, bits);
 }
 

@@ -6,9 +6,12 @@
 // indices):
 //   1. pack each lookup as (id << pos_bits) | position and radix-sort the
 //      packed words on the id bits only (LSD, 8-bit digits, stable, so equal
-//      ids keep lookup order);
-//   2. mark segment heads (id differs from its predecessor), scan them to give
-//      every lookup its segment number and emit the distinct ids;
+//      ids keep lookup order): one kernel counts the digits of every pass,
+//      then each pass is one kernel whose tiles find their offsets by
+//      decoupled look-back;
+//   2. mark segment heads (id differs from its predecessor) and number them
+//      in one look-back pass, giving every lookup its segment number and
+//      emitting the distinct ids;
 //   3. sum each segment's value rows in double, in a fixed order, and round
 //      once: fixed chunks of 64 sorted lookups per wave, partial sums for
 //      segments that cross a chunk boundary, then an ordered combine of those
@@ -20,20 +23,33 @@
 
 namespace spopt {
 
-constexpr int kSortThreads = 256;
-constexpr int kSortWaves = kSortThreads / kWave;
-constexpr int kSortIpt = 4;                                  // items per thread
-constexpr int kSortTile = kSortThreads * kSortIpt;           // 1024 lookups per block
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kIpt = 4;                         // items per thread
+constexpr int kTile = kThreads * kIpt;          // 1024 lookups per sort / segment tile
 constexpr int kRadixBits = 8;
 constexpr int kRadix = 1 << kRadixBits;
-constexpr int kSegTile = 1024;                                // lookups per block, segmenting
-constexpr int kChunk = 64;                                    // lookups per wave, summing
+constexpr int kMaxPasses = 8;
+constexpr int kChunk = 64;                      // sorted lookups per wave, summing
+constexpr int kFixThreads = 1024;               // block of the ordered combine
+constexpr int kFixWaves = kFixThreads / kWave;
+
+// Decoupled look-back words: bits 31..30 state (aggregate / inclusive prefix),
+// bits 29..0 a count, so n stays below 2^30.
+constexpr uint32_t kLbAgg = 1u << 30;
+constexpr uint32_t kLbInc = 2u << 30;
+constexpr uint32_t kLbState = 3u << 30;
+constexpr uint32_t kLbCount = (1u << 30) - 1u;
+// A tile waits only for tiles that took their ticket earlier, which publish
+// their own count before they wait on anybody; the bound only turns a bug
+// into a reported error instead of a hang.
+constexpr uint32_t kSpinLimit = 1u << 16;
 
 struct CanonLayout {
     int key_bits, pos_bits, passes;
-    int64_t nblk_sort, nblk_seg, nchunks;
-    size_t off_a, off_b, off_hist, off_blk, off_segid, off_segstart, off_pfirst, off_plast,
-        off_status, total;
+    int64_t ntiles, nchunks;
+    size_t off_a, off_b, off_clear, clear_bytes, off_status, off_tickets, off_hist, off_lb,
+        off_seglb, off_segid, off_segstart, off_pfirst, off_plast, total;
 };
 
 static int bits_for(uint64_t x) {  // bits needed to represent values in [0, x)
@@ -48,8 +64,7 @@ static bool canon_layout(int64_t n, int64_t width, int64_t key_space, CanonLayou
     L->pos_bits = bits_for((uint64_t)(n > 0 ? n : 1));
     if (L->key_bits + L->pos_bits > 64) return false;
     L->passes = (L->key_bits + kRadixBits - 1) / kRadixBits;
-    L->nblk_sort = ceil_div(n, kSortTile);
-    L->nblk_seg = ceil_div(n, kSegTile);
+    L->ntiles = ceil_div(n, kTile);
     L->nchunks = ceil_div(n, kChunk);
     size_t o = 0;
     auto take = [&](size_t bytes) {
@@ -59,36 +74,103 @@ static bool canon_layout(int64_t n, int64_t width, int64_t key_space, CanonLayou
     };
     L->off_a = take(sizeof(uint64_t) * (size_t)n);
     L->off_b = take(sizeof(uint64_t) * (size_t)n);
-    L->off_hist = take(sizeof(uint32_t) * (size_t)kRadix * (size_t)L->nblk_sort);
-    L->off_blk = take(sizeof(uint32_t) * ((size_t)L->nblk_seg + 1));
+    // Everything a call must find zeroed sits in one contiguous region.
+    L->off_clear = o;
+    L->off_status = take(sizeof(uint32_t) * 4);
+    L->off_tickets = take(sizeof(uint32_t) * (kMaxPasses + 1));
+    L->off_hist = take(sizeof(uint32_t) * (size_t)kRadix * (size_t)(L->passes ? L->passes : 1));
+    L->off_lb = take(sizeof(uint32_t) * (size_t)kRadix * (size_t)L->ntiles *
+                     (size_t)(L->passes ? L->passes : 1));
+    L->off_seglb = take(sizeof(uint32_t) * ((size_t)L->ntiles + 1));
+    L->clear_bytes = o - L->off_clear;
     L->off_segid = take(sizeof(int32_t) * (size_t)n);
     L->off_segstart = take(sizeof(int32_t) * ((size_t)n + 1));
     L->off_pfirst = take(sizeof(double) * (size_t)L->nchunks * (size_t)width);
     L->off_plast = take(sizeof(double) * (size_t)L->nchunks * (size_t)width);
-    L->off_status = take(sizeof(uint32_t) * 4);
     L->total = o;
     return true;
 }
 
-// ------------------------------------------------------------------ sort ---
+__device__ __forceinline__ uint32_t ld_agent(const uint32_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(uint32_t* p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Waits for a look-back word to leave state 0.  Returns false on timeout.
+__device__ __forceinline__ bool lb_wait(const uint32_t* p, uint32_t* out) {
+    for (uint32_t spins = 0; spins < kSpinLimit; ++spins) {
+        const uint32_t v = ld_agent(p);
+        if (v & kLbState) {
+            *out = v;
+            return true;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    return false;
+}
+
+// Sum of the counts published by tiles tile-1, tile-2, ... (words at
+// lb[j * stride]) back to the nearest inclusive prefix.  Reads 8 words at a
+// time so that one memory round trip covers 8 predecessors.
+__device__ __forceinline__ bool look_back(const uint32_t* lb, int64_t tile, int64_t stride,
+                                          uint32_t* excl_out) {
+    uint32_t excl = 0;
+    int64_t j = tile - 1;
+    while (j >= 0) {
+        uint32_t v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = (j - u >= 0) ? ld_agent(lb + (j - u) * stride) : kLbInc;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (j - u < 0) {
+                *excl_out = excl;
+                return true;
+            }
+            uint32_t x = v[u];
+            if (!(x & kLbState) && !lb_wait(lb + (j - u) * stride, &x)) return false;
+            excl += x & kLbCount;
+            if ((x & kLbState) == kLbInc) {
+                *excl_out = excl;
+                return true;
+            }
+        }
+        j -= 8;
+    }
+    *excl_out = excl;
+    return true;
+}
+
+// ----------------------------------------------------------------- clear ---
+
+__global__ void k_clear(uint4* p, int64_t n16) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
+         i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
 
 __global__ void k_status_clear(uint32_t* st, int nwords) {
     if ((int)threadIdx.x < nwords) st[threadIdx.x] = 0u;
 }
 
-// Pass 0: range-check ids, pack (id, position), digit histogram of this block.
-__global__ __launch_bounds__(kSortThreads) void k_pack_hist(
-    const int64_t* __restrict__ ids, int64_t n, int64_t key_space, int pos_bits, int shift,
-    uint32_t mask, uint64_t* __restrict__ out, uint32_t* __restrict__ hist, int64_t nblk,
-    int do_hist, uint32_t* status) {
-    __shared__ uint32_t h[kRadix];
-    for (int i = threadIdx.x; i < kRadix; i += blockDim.x) h[i] = 0;
+// ------------------------------------------------------------------ sort ---
+
+// Range-check ids, pack (id << pos_bits | position), and count the digits of
+// every radix pass into the global per-pass histograms.
+__global__ __launch_bounds__(kThreads) void k_pack(const int64_t* __restrict__ ids, int64_t n,
+                                                   int64_t key_space, int pos_bits, int passes,
+                                                   uint64_t* __restrict__ out,
+                                                   uint32_t* __restrict__ hist,
+                                                   uint32_t* status) {
+    __shared__ uint32_t h[kMaxPasses][kRadix];
+    for (int i = threadIdx.x; i < passes * kRadix; i += kThreads) (&h[0][0])[i] = 0;
     __syncthreads();
-    const int64_t base = (int64_t)blockIdx.x * kSortTile;
+    const int64_t base = (int64_t)blockIdx.x * kTile;
     bool bad = false;
 #pragma unroll
-    for (int j = 0; j < kSortIpt; ++j) {
-        const int64_t i = base + (int64_t)j * kSortThreads + threadIdx.x;
+    for (int j = 0; j < kIpt; ++j) {
+        const int64_t i = base + (int64_t)j * kThreads + threadIdx.x;
         if (i < n) {
             int64_t id = ids[i];
             if (id < 0 || id >= key_space) {
@@ -97,79 +179,59 @@ __global__ __launch_bounds__(kSortThreads) void k_pack_hist(
             }
             const uint64_t packed = ((uint64_t)id << pos_bits) | (uint64_t)i;
             out[i] = packed;
-            if (do_hist) atomicAdd(&h[(uint32_t)(packed >> shift) & mask], 1u);
+            for (int p = 0; p < passes; ++p)
+                atomicAdd(&h[p][(uint32_t)(packed >> (pos_bits + p * kRadixBits)) & (kRadix - 1)],
+                          1u);
         }
     }
     if (ballot(bad) != 0ull && lane_id() == 0) atomicOr(status, kStatusRange);
-    if (!do_hist) return;
     __syncthreads();
-    for (int d = threadIdx.x; d < kRadix; d += blockDim.x) hist[(int64_t)d * nblk + blockIdx.x] = h[d];
-}
-
-// Digit histogram of one block for passes after the first.
-__global__ __launch_bounds__(kSortThreads) void k_hist(const uint64_t* __restrict__ in, int64_t n,
-                                                       int shift, uint32_t mask,
-                                                       uint32_t* __restrict__ hist, int64_t nblk) {
-    __shared__ uint32_t h[kRadix];
-    for (int i = threadIdx.x; i < kRadix; i += blockDim.x) h[i] = 0;
-    __syncthreads();
-    const int64_t base = (int64_t)blockIdx.x * kSortTile;
-#pragma unroll
-    for (int j = 0; j < kSortIpt; ++j) {
-        const int64_t i = base + (int64_t)j * kSortThreads + threadIdx.x;
-        if (i < n) atomicAdd(&h[(uint32_t)(in[i] >> shift) & mask], 1u);
-    }
-    __syncthreads();
-    for (int d = threadIdx.x; d < kRadix; d += blockDim.x) hist[(int64_t)d * nblk + blockIdx.x] = h[d];
-}
-
-// In-place exclusive scan of a uint32 array by one block of 1024 threads; each
-// thread owns one contiguous segment.
-__global__ __launch_bounds__(1024) void k_scan_u32(uint32_t* data, int64_t len) {
-    __shared__ uint32_t wt[16];
-    const int64_t per = (len + blockDim.x - 1) / blockDim.x;
-    const int64_t beg = (int64_t)threadIdx.x * per;
-    const int64_t end = beg + per < len ? beg + per : len;
-    uint32_t sum = 0;
-    for (int64_t i = beg; i < end; ++i) sum += data[i];
-    uint32_t total;
-    uint32_t off = block_excl_scan(sum, wt, &total);
-    for (int64_t i = beg; i < end; ++i) {
-        uint32_t x = data[i];
-        data[i] = off;
-        off += x;
+    for (int i = threadIdx.x; i < passes * kRadix; i += kThreads) {
+        const uint32_t c = (&h[0][0])[i];
+        if (c) atomicAdd(&hist[i], c);
     }
 }
 
-// Stable scatter of one radix pass.  Wave w of a block ranks the block's items
-// [w*256, (w+1)*256) in four rounds of 64 consecutive items: lanes holding the
-// same digit are found with 8 ballots, each lane's rank is the number of
-// lower lanes with its digit plus the wave's running count of that digit.
-__global__ __launch_bounds__(kSortThreads) void k_scatter(const uint64_t* __restrict__ in,
-                                                          uint64_t* __restrict__ out, int64_t n,
-                                                          int shift, uint32_t mask, int nbits,
-                                                          const uint32_t* __restrict__ hist,
-                                                          int64_t nblk) {
-    __shared__ uint32_t cnt[kSortWaves][kRadix];
-    const int w = (int)(threadIdx.x >> 6);
+// One stable radix pass in a single kernel.  A block takes the next tile
+// ticket, ranks its 1024 items (wave w owns items [w*256, (w+1)*256) in four
+// rounds of 64: lanes holding the same digit are matched with one ballot per
+// digit bit, a lane's rank is the number of lower lanes with its digit plus
+// the wave's running count of that digit), publishes its per-digit counts,
+// and sums the counts of the tiles before it by decoupled look-back.  Its
+// items then go to  digit base (scan of the pass histogram) + prefix of the
+// tiles before + prefix of the waves before + rank.
+__global__ __launch_bounds__(kThreads) void k_onesweep(
+    const uint64_t* __restrict__ in, uint64_t* __restrict__ out, int64_t n, int shift, int nbits,
+    const uint32_t* __restrict__ hist, uint32_t* lb, uint32_t* ticket, uint32_t* status) {
+    __shared__ uint32_t cnt[kWaves][kRadix];
+    __shared__ uint32_t base[kRadix];
+    __shared__ uint32_t wt[kWaves];
+    __shared__ uint32_t s_tile, s_bad;
+    const int tid = threadIdx.x;
+    const int w = tid >> 6;
     const int lane = lane_id();
-    for (int i = threadIdx.x; i < kSortWaves * kRadix; i += blockDim.x) (&cnt[0][0])[i] = 0;
+    if (tid == 0) {
+        s_tile = atomicAdd(ticket, 1u);
+        s_bad = 0u;
+    }
+    for (int i = tid; i < kWaves * kRadix; i += kThreads) (&cnt[0][0])[i] = 0;
     __syncthreads();
+    const int64_t tile = s_tile;
 
-    const int64_t base = (int64_t)blockIdx.x * kSortTile + (int64_t)w * (kSortIpt * kWave);
+    const int64_t first = tile * kTile + (int64_t)w * (kIpt * kWave);
     const uint64_t lt = lanemask_lt();
-    uint64_t key[kSortIpt];
-    uint32_t dig[kSortIpt], rank[kSortIpt];
-    bool valid[kSortIpt];
+    uint64_t key[kIpt];
+    uint32_t dig[kIpt], rank[kIpt];
+    bool valid[kIpt];
 #pragma unroll
-    for (int r = 0; r < kSortIpt; ++r) {
-        const int64_t i = base + (int64_t)r * kWave + lane;
+    for (int r = 0; r < kIpt; ++r) {
+        const int64_t i = first + (int64_t)r * kWave + lane;
         valid[r] = i < n;
         key[r] = valid[r] ? in[i] : 0ull;
-        dig[r] = (uint32_t)(key[r] >> shift) & mask;
+        dig[r] = (uint32_t)(key[r] >> shift) & (kRadix - 1);
     }
 #pragma unroll
-    for (int r = 0; r < kSortIpt; ++r) {
+    for (int r = 0; r < kIpt; ++r) {
         uint64_t peers = ballot(valid[r]);
         for (int b = 0; b < nbits; ++b) {
             const bool bit = (dig[r] >> b) & 1u;
@@ -187,18 +249,40 @@ __global__ __launch_bounds__(kSortThreads) void k_scatter(const uint64_t* __rest
         rank[r] = old + below;
     }
     __syncthreads();
-    for (int d = threadIdx.x; d < kRadix; d += blockDim.x) {
-        uint32_t run = hist[(int64_t)d * nblk + blockIdx.x];
-        for (int ww = 0; ww < kSortWaves; ++ww) {
-            const uint32_t c = cnt[ww][d];
-            cnt[ww][d] = run;
-            run += c;
-        }
+
+    // Thread d owns digit d: prefix over the waves, then over earlier tiles.
+    const int d = tid;
+    uint32_t run = 0;
+    for (int ww = 0; ww < kWaves; ++ww) {
+        const uint32_t c = cnt[ww][d];
+        cnt[ww][d] = run;
+        run += c;
     }
+    uint32_t* mine = lb + tile * kRadix + d;
+    uint32_t excl = 0;
+    bool ok = true;
+    if (tile == 0) {
+        st_agent(mine, kLbInc | run);
+    } else {
+        st_agent(mine, kLbAgg | run);
+        ok = look_back(lb + d, tile, kRadix, &excl);
+        if (ok) st_agent(mine, kLbInc | (excl + run));
+    }
+    if (!ok) atomicOr(&s_bad, 1u);
+    uint32_t total;
+    const uint32_t gbase = block_excl_scan(hist[d], wt, &total);
+    base[d] = gbase + excl;
     __syncthreads();
+    if (s_bad) {
+        if (tid == 0) atomicOr(status, kStatusTimeout);
+        return;
+    }
 #pragma unroll
-    for (int r = 0; r < kSortIpt; ++r)
-        if (valid[r]) out[cnt[w][dig[r]] + rank[r]] = key[r];
+    for (int r = 0; r < kIpt; ++r) {
+        if (!valid[r]) continue;
+        const uint64_t dst = (uint64_t)base[dig[r]] + cnt[w][dig[r]] + rank[r];
+        if (dst < (uint64_t)n) out[dst] = key[r];
+    }
 }
 
 // ------------------------------------------------------------- segments ---
@@ -207,104 +291,115 @@ __device__ __forceinline__ bool seg_head(const uint64_t* s, int64_t i, int pos_b
     return i == 0 || (s[i] >> pos_bits) != (s[i - 1] >> pos_bits);
 }
 
-__global__ __launch_bounds__(256) void k_seg_count(const uint64_t* __restrict__ s, int64_t n,
-                                                   int pos_bits, uint32_t* __restrict__ blk) {
-    __shared__ uint32_t wt[4];
-    const int64_t base = (int64_t)blockIdx.x * kSegTile;
-    uint32_t c = 0;
-    for (int j = 0; j < kSegTile / 256; ++j) {
-        const int64_t i = base + (int64_t)j * 256 + threadIdx.x;
-        if (i < n && seg_head(s, i, pos_bits)) ++c;
-    }
-    uint32_t total;
-    block_excl_scan(c, wt, &total);
-    if (threadIdx.x == 0) blk[blockIdx.x] = total;
-}
-
-// Scan the per-block head counts; publish U (0 when an id was out of range)
+// Segment heads (id differs from its predecessor) of each tile, counted and
+// prefixed across tiles by decoupled look-back in one pass: every sorted
+// lookup gets its segment number, every head writes its id and position.  The
+// last tile publishes U (0 when an id was out of range or a wait timed out)
 // and the sentinel seg_start[U] = n.
-__global__ __launch_bounds__(1024) void k_seg_scan(uint32_t* blk, int64_t nblk, int64_t n,
-                                                   int32_t* seg_start, int64_t* d_nunique,
-                                                   const uint32_t* status) {
-    __shared__ uint32_t wt[16];
-    const int64_t per = (nblk + blockDim.x - 1) / blockDim.x;
-    const int64_t beg = (int64_t)threadIdx.x * per;
-    const int64_t end = beg + per < nblk ? beg + per : nblk;
-    uint32_t sum = 0;
-    for (int64_t i = beg; i < end; ++i) sum += blk[i];
-    uint32_t total;
-    uint32_t off = block_excl_scan(sum, wt, &total);
-    for (int64_t i = beg; i < end; ++i) {
-        uint32_t x = blk[i];
-        blk[i] = off;
-        off += x;
+__global__ __launch_bounds__(kThreads) void k_segment(
+    const uint64_t* __restrict__ s, int64_t n, int pos_bits, int64_t ntiles, uint32_t* lb,
+    uint32_t* ticket, int32_t* __restrict__ seg_id, int32_t* __restrict__ seg_start,
+    int64_t* __restrict__ out_keys, int64_t* __restrict__ d_nunique, uint32_t* status) {
+    if (*status != 0u) {
+        if (blockIdx.x == 0 && threadIdx.x == 0) *d_nunique = 0;
+        return;
     }
-    if (threadIdx.x == 0) {
-        const bool ok = *status == 0u;
-        *d_nunique = ok ? (int64_t)total : 0;
-        seg_start[total] = (int32_t)n;
+    __shared__ uint32_t wt[kWaves];
+    __shared__ uint32_t s_tile, s_excl, s_ok;
+    const int tid = threadIdx.x;
+    if (tid == 0) s_tile = atomicAdd(ticket, 1u);
+    __syncthreads();
+    const int64_t tile = s_tile;
+    const int64_t base = tile * kTile;
+    bool head[kIpt];
+    uint32_t mine = 0;
+#pragma unroll
+    for (int j = 0; j < kIpt; ++j) {
+        const int64_t i = base + (int64_t)j * kThreads + tid;
+        head[j] = i < n && seg_head(s, i, pos_bits);
+        mine += head[j] ? 1u : 0u;
     }
-}
-
-// Segment number of every sorted lookup; distinct ids and segment starts.
-__global__ __launch_bounds__(256) void k_seg_emit(const uint64_t* __restrict__ s, int64_t n,
-                                                  int pos_bits, const uint32_t* __restrict__ blk,
-                                                  int32_t* __restrict__ seg_id,
-                                                  int32_t* __restrict__ seg_start,
-                                                  int64_t* __restrict__ out_keys,
-                                                  const uint32_t* status) {
-    if (*status != 0u) return;
-    __shared__ uint32_t wt[4];
-    const int64_t base = (int64_t)blockIdx.x * kSegTile;
-    uint32_t run = blk[blockIdx.x];
-    for (int j = 0; j < kSegTile / 256; ++j) {
-        const int64_t i = base + (int64_t)j * 256 + threadIdx.x;
-        const bool h = i < n && seg_head(s, i, pos_bits);
-        uint32_t total;
-        const uint32_t before = block_excl_scan(h ? 1u : 0u, wt, &total);
+    uint32_t tile_heads;
+    block_excl_scan(mine, wt, &tile_heads);
+    if (tid == 0) {
+        uint32_t excl = 0;
+        bool ok = true;
+        if (tile == 0) {
+            st_agent(lb, kLbInc | tile_heads);
+        } else {
+            st_agent(lb + tile, kLbAgg | tile_heads);
+            ok = look_back(lb, tile, 1, &excl);
+            if (ok) st_agent(lb + tile, kLbInc | (excl + tile_heads));
+        }
+        s_excl = excl;
+        s_ok = ok ? 1u : 0u;
+    }
+    __syncthreads();
+    if (!s_ok) {
+        if (tid == 0) {
+            atomicOr(status, kStatusTimeout);
+            *d_nunique = 0;
+        }
+        return;
+    }
+    uint32_t run = s_excl;
+#pragma unroll
+    for (int j = 0; j < kIpt; ++j) {
+        const int64_t i = base + (int64_t)j * kThreads + tid;
+        uint32_t round_total;
+        const uint32_t before = block_excl_scan(head[j] ? 1u : 0u, wt, &round_total);
         if (i < n) {
-            const uint32_t seg = run + before + (h ? 1u : 0u) - 1u;
+            const uint32_t seg = run + before + (head[j] ? 1u : 0u) - 1u;
             seg_id[i] = (int32_t)seg;
-            if (h) {
+            if (head[j]) {
                 out_keys[seg] = (int64_t)(s[i] >> pos_bits);
                 seg_start[seg] = (int32_t)i;
             }
         }
-        run += total;
+        run += round_total;
+    }
+    if (tile == ntiles - 1 && tid == 0) {
+        *d_nunique = (int64_t)run;
+        seg_start[run] = (int32_t)n;
     }
 }
 
 // ----------------------------------------------------------- dup sums ---
 
-// V-wide access to a row of floats: a vector load when the layout allows, a
-// scalar loop with a column bound otherwise.
+// V-wide access to a row of floats.  V > 1 is chosen on the host only when the
+// width is a multiple of V and the arrays are V*4-byte aligned, so a lane
+// whose first column is inside the row owns all V of its columns.
+// Straight-line: a lane past the end of the row loads the row's first V
+// columns instead and zeroes them, so loads are never behind a branch.
 template <int V>
-__device__ __forceinline__ void load_row(float (&r)[V], const float* src, int64_t col,
-                                         int64_t width, bool vec) {
-    if (V == 4 && vec && col < width) {
+__device__ __forceinline__ void load_row(float (&r)[V], const float* row, int64_t col,
+                                         int64_t width) {
+    const bool in = col < width;
+    const float* src = row + (in ? col : 0);
+    if constexpr (V == 4) {
         const float4 x = *reinterpret_cast<const float4*>(src);
-        r[0] = x.x; r[1 % V] = x.y; r[2 % V] = x.z; r[3 % V] = x.w;
-    } else if (V == 2 && vec && col < width) {
+        r[0] = in ? x.x : 0.f; r[1] = in ? x.y : 0.f; r[2] = in ? x.z : 0.f; r[3] = in ? x.w : 0.f;
+    } else if constexpr (V == 2) {
         const float2 x = *reinterpret_cast<const float2*>(src);
-        r[0] = x.x; r[1 % V] = x.y;
+        r[0] = in ? x.x : 0.f; r[1] = in ? x.y : 0.f;
     } else {
-#pragma unroll
-        for (int v = 0; v < V; ++v) r[v] = (col + v < width) ? src[v] : 0.f;
+        const float x = src[0];
+        r[0] = in ? x : 0.f;
     }
 }
 
 template <int V>
 __device__ __forceinline__ void store_row(float* dst, const double (&r)[V], int64_t col,
-                                          int64_t width, bool vec) {
-    if (V == 4 && vec && col < width) {
-        *reinterpret_cast<float4*>(dst) =
-            make_float4((float)r[0], (float)r[1 % V], (float)r[2 % V], (float)r[3 % V]);
-    } else if (V == 2 && vec && col < width) {
-        *reinterpret_cast<float2*>(dst) = make_float2((float)r[0], (float)r[1 % V]);
-    } else {
-#pragma unroll
-        for (int v = 0; v < V; ++v)
-            if (col + v < width) dst[v] = (float)r[v];
+                                          int64_t width) {
+    if (col < width) {
+        if constexpr (V == 4) {
+            *reinterpret_cast<float4*>(dst) =
+                make_float4((float)r[0], (float)r[1], (float)r[2], (float)r[3]);
+        } else if constexpr (V == 2) {
+            *reinterpret_cast<float2*>(dst) = make_float2((float)r[0], (float)r[1]);
+        } else {
+            dst[0] = (float)r[0];
+        }
     }
 }
 
@@ -357,8 +452,9 @@ __device__ __forceinline__ ChunkItem chunk_item(const uint64_t* s, const int32_t
 }
 
 // One wave per chunk of 64 sorted lookups, value rows of `width` floats; each
-// lane owns V consecutive columns of every 64*V-column block and accumulates
-// them in double, in sorted (= lookup) order within the chunk.
+// lane owns V consecutive columns of every 64*V-column block.  All rows of the
+// chunk are loaded before the first add (D rows in flight per lane), then
+// accumulated in double in sorted (= lookup) order.
 template <int V>
 __global__ __launch_bounds__(256) void k_dupsum_rows(
     const uint64_t* __restrict__ s, const int32_t* __restrict__ seg_id,
@@ -366,6 +462,7 @@ __global__ __launch_bounds__(256) void k_dupsum_rows(
     const float* __restrict__ vals, int64_t width, float* __restrict__ out_vals,
     int32_t* __restrict__ out_counts, double* __restrict__ pfirst, double* __restrict__ plast,
     const uint32_t* status) {
+    constexpr int D = (kChunk * V <= 128) ? kChunk : 128 / V;
     if (*status != 0u) return;
     const int lane = lane_id();
     const int64_t chunk = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
@@ -375,26 +472,22 @@ __global__ __launch_bounds__(256) void k_dupsum_rows(
     const ChunkItem it = chunk_item(s, seg_id, seg_start, n, pos_bits, i0, cnt, lane);
     if (it.ends) out_counts[it.seg] = (int32_t)(i0 + lane + 1 - seg_start[it.seg]);
 
-    const uintptr_t vmask = (uintptr_t)(V * sizeof(float)) - 1u;
-    const bool vec = (V > 1) && (width % V == 0) &&
-                     ((((uintptr_t)vals) | ((uintptr_t)out_vals)) & vmask) == 0;
     for (int64_t c0 = 0; c0 < width; c0 += (int64_t)kWave * V) {
         const int64_t col = c0 + (int64_t)lane * V;
         double acc[V];
 #pragma unroll
         for (int v = 0; v < V; ++v) acc[v] = 0.0;
-        for (int j0 = 0; j0 < cnt; j0 += 8) {
-            float row[8][V];
+        for (int j0 = 0; j0 < cnt; j0 += D) {
+            float row[D][V];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int j = j0 + u;
-                if (j < cnt) {
-                    const uint32_t pos = read_lane(it.pos, j);
-                    load_row<V>(row[u], vals + (int64_t)pos * width + col, col, width, vec);
-                }
+            for (int u = 0; u < D; ++u) {
+                // Past the chunk's last lookup, reload that lookup's row (unused).
+                const int j = (j0 + u < cnt) ? j0 + u : cnt - 1;
+                const uint32_t pos = read_lane(it.pos, j);
+                load_row<V>(row[u], vals + (int64_t)pos * width, col, width);
             }
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
+            for (int u = 0; u < D; ++u) {
                 const int j = j0 + u;
                 if (j < cnt) {
 #pragma unroll
@@ -403,7 +496,7 @@ __global__ __launch_bounds__(256) void k_dupsum_rows(
                     if (kind != kFlushNone) {
                         if (kind == kFlushOut)
                             store_row<V>(out_vals + (int64_t)read_lane(it.seg, j) * width + col,
-                                         acc, col, width, vec);
+                                         acc, col, width);
                         else if (kind == kFlushFirst)
                             store_part<V>(pfirst + chunk * width + col, acc, col, width);
                         else
@@ -452,35 +545,66 @@ __global__ __launch_bounds__(256) void k_dupsum_scalar(
         plast[chunk] = x;
 }
 
-// Segments that cross chunk boundaries: the wave of the chunk where such a
-// segment starts adds its partials in chunk order and rounds once.
+// Segments that cross chunk boundaries.  The block of the chunk where such a
+// segment starts combines its partials (plast of that chunk, then pfirst of
+// each following chunk up to the one where it ends): its 16 waves each add a
+// contiguous run of partials, 8 loads in flight, then wave 0 adds the 16 wave
+// sums in wave order and rounds once.  A fixed order, so deterministic.
+// Blocks stride over the chunks.
 template <int V>
-__global__ __launch_bounds__(256) void k_dupsum_fixup(
+__global__ __launch_bounds__(kFixThreads) void k_dupsum_fixup(
     const int32_t* __restrict__ seg_id, const int32_t* __restrict__ seg_start, int64_t n,
-    const double* __restrict__ pfirst, const double* __restrict__ plast, int64_t width,
-    float* __restrict__ out_vals, const uint32_t* status) {
+    int64_t nchunks, const double* __restrict__ pfirst, const double* __restrict__ plast,
+    int64_t width, float* __restrict__ out_vals, const uint32_t* status) {
+    __shared__ double part[kFixWaves][kWave * V];
     if (*status != 0u) return;
+    const int w = (int)(threadIdx.x >> 6);
     const int lane = lane_id();
-    const int64_t chunk = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
-    const int64_t i0 = chunk * kChunk;
-    if (i0 >= n) return;
-    const int64_t last = (i0 + kChunk < n ? i0 + kChunk : n) - 1;
-    const int32_t seg = seg_id[last];
-    const int64_t s0 = seg_start[seg], s1 = seg_start[seg + 1];
-    if (!(s0 >= i0 && s1 > i0 + kChunk)) return;
-    const int64_t ce = (s1 - 1) / kChunk;
-    const uintptr_t vmask = (uintptr_t)(V * sizeof(float)) - 1u;
-    const bool vec = (V > 1) && (width % V == 0) && (((uintptr_t)out_vals) & vmask) == 0;
-    for (int64_t c0 = 0; c0 < width; c0 += (int64_t)kWave * V) {
-        const int64_t col = c0 + (int64_t)lane * V;
-        double acc[V], row[V];
-        load_part<V>(acc, plast + chunk * width + col, col, width);
-        for (int64_t c = chunk + 1; c <= ce; ++c) {
-            load_part<V>(row, pfirst + c * width + col, col, width);
+    for (int64_t chunk = blockIdx.x; chunk < nchunks; chunk += gridDim.x) {
+        const int64_t i0 = chunk * kChunk;
+        const int64_t last = (i0 + kChunk < n ? i0 + kChunk : n) - 1;
+        const int32_t seg = seg_id[last];
+        const int64_t s0 = seg_start[seg], s1 = seg_start[seg + 1];
+        if (!(s0 >= i0 && s1 > i0 + kChunk)) continue;  // uniform over the block
+        const int64_t m = (s1 - 1) / kChunk - chunk + 1;  // partials: plast[chunk], pfirst[...]
+        const int64_t lo = m * w / kFixWaves, hi = m * (w + 1) / kFixWaves;
+        for (int64_t c0 = 0; c0 < width; c0 += (int64_t)kWave * V) {
+            const int64_t col = c0 + (int64_t)lane * V;
+            double acc[V];
 #pragma unroll
-            for (int v = 0; v < V; ++v) acc[v] += row[v];
+            for (int v = 0; v < V; ++v) acc[v] = 0.0;
+            for (int64_t q0 = lo; q0 < hi; q0 += 8) {
+                double row[8][V];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int64_t q = q0 + u;
+                    if (q < hi) {
+                        const double* src = (q == 0) ? plast + chunk * width
+                                                     : pfirst + (chunk + q) * width;
+                        load_part<V>(row[u], src + col, col, width);
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    if (q0 + u < hi) {
+#pragma unroll
+                        for (int v = 0; v < V; ++v) acc[v] += row[u][v];
+                    }
+            }
+#pragma unroll
+            for (int v = 0; v < V; ++v) part[w][lane * V + v] = acc[v];
+            __syncthreads();
+            if (w == 0) {
+                double tot[V];
+#pragma unroll
+                for (int v = 0; v < V; ++v) tot[v] = part[0][lane * V + v];
+                for (int ww = 1; ww < kFixWaves; ++ww)
+#pragma unroll
+                    for (int v = 0; v < V; ++v) tot[v] += part[ww][lane * V + v];
+                store_row<V>(out_vals + (int64_t)seg * width + col, tot, col, width);
+            }
+            __syncthreads();
         }
-        store_row<V>(out_vals + (int64_t)seg * width + col, acc, col, width, vec);
     }
 }
 
@@ -522,7 +646,7 @@ extern "C" int coo_from_lookups(const int64_t* ids, const float* vals, int64_t n
                                 size_t workspace_bytes, void* stream, uint32_t flags) {
     hipStream_t st = (hipStream_t)stream;
     CanonLayout L;
-    if (n >= ((int64_t)1 << 31)) return fail(SPOPT_EOVERFLOW, "coo_from_lookups: n >= 2^31");
+    if (n >= ((int64_t)1 << 30)) return fail(SPOPT_EOVERFLOW, "coo_from_lookups: n >= 2^30");
     if (!canon_layout(n, width, key_space, &L))
         return fail(SPOPT_EINVAL, "coo_from_lookups: bad n=%lld width=%lld key_space=%lld",
                     (long long)n, (long long)width, (long long)key_space);
@@ -530,27 +654,34 @@ extern "C" int coo_from_lookups(const int64_t* ids, const float* vals, int64_t n
     if (n > 0 && (ids == nullptr || vals == nullptr || out_keys == nullptr ||
                   out_vals == nullptr || out_counts == nullptr))
         return fail(SPOPT_EINVAL, "coo_from_lookups: NULL array");
-    if (workspace == nullptr || workspace_bytes < L.total)
+    if (n > 0 && (workspace == nullptr || workspace_bytes < L.total))
         return fail(SPOPT_EWORKSPACE, "coo_from_lookups: workspace %zu bytes, need %zu",
                     workspace_bytes, L.total);
-    char* ws = (char*)workspace;
-    uint64_t* a = (uint64_t*)(ws + L.off_a);
-    uint64_t* b = (uint64_t*)(ws + L.off_b);
-    uint32_t* hist = (uint32_t*)(ws + L.off_hist);
-    uint32_t* blk = (uint32_t*)(ws + L.off_blk);
-    int32_t* seg_id = (int32_t*)(ws + L.off_segid);
-    int32_t* seg_start = (int32_t*)(ws + L.off_segstart);
-    double* pfirst = (double*)(ws + L.off_pfirst);
-    double* plast = (double*)(ws + L.off_plast);
-    uint32_t* status = (uint32_t*)(ws + L.off_status);
-
     if (n == 0) {
         k_write_i64<<<1, 1, 0, st>>>(d_nunique, 0);
         SPOPT_LAUNCHED();
         return SPOPT_OK;
     }
-    int rc = launch_status_clear(status, 4, st);
-    if (rc) return rc;
+    if (((uintptr_t)workspace & 255u) != 0)
+        return fail(SPOPT_EWORKSPACE, "coo_from_lookups: workspace must be 256-byte aligned");
+    char* ws = (char*)workspace;
+    uint64_t* a = (uint64_t*)(ws + L.off_a);
+    uint64_t* b = (uint64_t*)(ws + L.off_b);
+    uint32_t* status = (uint32_t*)(ws + L.off_status);
+    uint32_t* tickets = (uint32_t*)(ws + L.off_tickets);
+    uint32_t* hist = (uint32_t*)(ws + L.off_hist);
+    uint32_t* lb = (uint32_t*)(ws + L.off_lb);
+    uint32_t* seglb = (uint32_t*)(ws + L.off_seglb);
+    int32_t* seg_id = (int32_t*)(ws + L.off_segid);
+    int32_t* seg_start = (int32_t*)(ws + L.off_segstart);
+    double* pfirst = (double*)(ws + L.off_pfirst);
+    double* plast = (double*)(ws + L.off_plast);
+
+    // Zero the status word, tickets, histograms and look-back words.
+    const int64_t n16 = (int64_t)(L.clear_bytes / 16);
+    k_clear<<<(unsigned)(ceil_div(n16, 256) < 256 ? ceil_div(n16, 256) : 256), 256, 0, st>>>(
+        (uint4*)(ws + L.off_clear), n16);
+    SPOPT_LAUNCHED();
     const bool validate = (flags & SPOPT_VALIDATE) != 0;
     if (validate) {
         const int64_t len = n * width;
@@ -558,17 +689,8 @@ extern "C" int coo_from_lookups(const int64_t* ids, const float* vals, int64_t n
         k_check_finite<<<grid, 256, 0, st>>>(vals, len, status);
         SPOPT_LAUNCHED();
     }
-
-    // Radix sort on the id bits of the packed words.
-    const uint32_t full_mask = kRadix - 1;
-    auto pass_bits = [&](int p) {
-        const int rem = L.key_bits - p * kRadixBits;
-        return rem < kRadixBits ? rem : kRadixBits;
-    };
-    const int64_t nblk = L.nblk_sort;
-    k_pack_hist<<<(unsigned)nblk, kSortThreads, 0, st>>>(
-        ids, n, key_space, L.pos_bits, L.pos_bits, L.passes ? ((1u << pass_bits(0)) - 1u) : 0u,
-        a, hist, nblk, L.passes > 0, status);
+    k_pack<<<(unsigned)L.ntiles, kThreads, 0, st>>>(ids, n, key_space, L.pos_bits, L.passes, a,
+                                                    hist, status);
     SPOPT_LAUNCHED();
     if (validate) {
         uint32_t h_status = 0;
@@ -579,62 +701,59 @@ extern "C" int coo_from_lookups(const int64_t* ids, const float* vals, int64_t n
     uint64_t* src = a;
     uint64_t* dst = b;
     for (int p = 0; p < L.passes; ++p) {
-        const int shift = L.pos_bits + p * kRadixBits;
-        const int nb = pass_bits(p);
-        const uint32_t mask = (nb == kRadixBits) ? full_mask : ((1u << nb) - 1u);
-        if (p > 0) {
-            k_hist<<<(unsigned)nblk, kSortThreads, 0, st>>>(src, n, shift, mask, hist, nblk);
-            SPOPT_LAUNCHED();
-        }
-        k_scan_u32<<<1, 1024, 0, st>>>(hist, (int64_t)kRadix * nblk);
-        SPOPT_LAUNCHED();
-        k_scatter<<<(unsigned)nblk, kSortThreads, 0, st>>>(src, dst, n, shift, mask, nb, hist,
-                                                           nblk);
+        const int rem = L.key_bits - p * kRadixBits;
+        k_onesweep<<<(unsigned)L.ntiles, kThreads, 0, st>>>(
+            src, dst, n, L.pos_bits + p * kRadixBits, rem < kRadixBits ? rem : kRadixBits,
+            hist + p * kRadix, lb + (int64_t)p * L.ntiles * kRadix, tickets + p, status);
         SPOPT_LAUNCHED();
         uint64_t* t = src;
         src = dst;
         dst = t;
     }
     const uint64_t* sorted = src;
-
-    // Segments.
-    k_seg_count<<<(unsigned)L.nblk_seg, 256, 0, st>>>(sorted, n, L.pos_bits, blk);
-    SPOPT_LAUNCHED();
-    k_seg_scan<<<1, 1024, 0, st>>>(blk, L.nblk_seg, n, seg_start, d_nunique, status);
-    SPOPT_LAUNCHED();
-    k_seg_emit<<<(unsigned)L.nblk_seg, 256, 0, st>>>(sorted, n, L.pos_bits, blk, seg_id,
-                                                     seg_start, out_keys, status);
+    k_segment<<<(unsigned)L.ntiles, kThreads, 0, st>>>(sorted, n, L.pos_bits, L.ntiles, seglb,
+                                                       tickets + kMaxPasses, seg_id, seg_start,
+                                                       out_keys, d_nunique, status);
     SPOPT_LAUNCHED();
 
-    // Duplicate sums: 4 chunks (waves) per block.
+    // Duplicate sums: 4 chunks (waves) per block, then the ordered combine of
+    // segments that cross chunks.  V floats per lane: 16- or 8-byte accesses
+    // when the width and the value arrays allow them.
     const unsigned grid = (unsigned)ceil_div(L.nchunks, 4);
+    const unsigned fgrid = (unsigned)(L.nchunks < 1024 ? L.nchunks : 1024);
+    const uintptr_t al = (uintptr_t)vals | (uintptr_t)out_vals;
+    int V = 1;
+    if (width % 4 == 0 && width >= 256 && (al & 15u) == 0)
+        V = 4;
+    else if (width % 2 == 0 && width >= 128 && (al & 7u) == 0)
+        V = 2;
     if (width == 1) {
         k_dupsum_scalar<<<grid, 256, 0, st>>>(sorted, seg_id, seg_start, n, L.pos_bits, vals,
                                               out_vals, out_counts, pfirst, plast, status);
         SPOPT_LAUNCHED();
-        k_dupsum_fixup<1><<<grid, 256, 0, st>>>(seg_id, seg_start, n, pfirst, plast, 1, out_vals,
-                                                status);
+        k_dupsum_fixup<1><<<fgrid, kFixThreads, 0, st>>>(seg_id, seg_start, n, L.nchunks, pfirst,
+                                                         plast, 1, out_vals, status);
         SPOPT_LAUNCHED();
-    } else if (width % 4 == 0 && width >= 256) {
+    } else if (V == 4) {
         k_dupsum_rows<4><<<grid, 256, 0, st>>>(sorted, seg_id, seg_start, n, L.pos_bits, vals,
                                                width, out_vals, out_counts, pfirst, plast, status);
         SPOPT_LAUNCHED();
-        k_dupsum_fixup<4><<<grid, 256, 0, st>>>(seg_id, seg_start, n, pfirst, plast, width,
-                                                out_vals, status);
+        k_dupsum_fixup<4><<<fgrid, kFixThreads, 0, st>>>(seg_id, seg_start, n, L.nchunks, pfirst,
+                                                         plast, width, out_vals, status);
         SPOPT_LAUNCHED();
-    } else if (width % 2 == 0 && width >= 128) {
+    } else if (V == 2) {
         k_dupsum_rows<2><<<grid, 256, 0, st>>>(sorted, seg_id, seg_start, n, L.pos_bits, vals,
                                                width, out_vals, out_counts, pfirst, plast, status);
         SPOPT_LAUNCHED();
-        k_dupsum_fixup<2><<<grid, 256, 0, st>>>(seg_id, seg_start, n, pfirst, plast, width,
-                                                out_vals, status);
+        k_dupsum_fixup<2><<<fgrid, kFixThreads, 0, st>>>(seg_id, seg_start, n, L.nchunks, pfirst,
+                                                         plast, width, out_vals, status);
         SPOPT_LAUNCHED();
     } else {
         k_dupsum_rows<1><<<grid, 256, 0, st>>>(sorted, seg_id, seg_start, n, L.pos_bits, vals,
                                                width, out_vals, out_counts, pfirst, plast, status);
         SPOPT_LAUNCHED();
-        k_dupsum_fixup<1><<<grid, 256, 0, st>>>(seg_id, seg_start, n, pfirst, plast, width,
-                                                out_vals, status);
+        k_dupsum_fixup<1><<<fgrid, kFixThreads, 0, st>>>(seg_id, seg_start, n, L.nchunks, pfirst,
+                                                         plast, width, out_vals, status);
         SPOPT_LAUNCHED();
     }
     return SPOPT_OK;

@@ -19,7 +19,8 @@ enum : uint32_t {
     kStatusNotCanon = 2u,  // not strictly ascending / CSR not canonical
     kStatusNonFinite = 4u, // NaN or inf gradient value
     kStatusStep = 8u,      // last_step >= t on a touched coordinate
-    kStatusTouched = 16u   // touched-row list inconsistent with row_offsets
+    kStatusTouched = 16u,  // touched-row list inconsistent with row_offsets
+    kStatusTimeout = 32u   // a bounded device-side wait gave up (a library bug)
 };
 
 // ---------------------------------------------------------------- device ---

@@ -70,6 +70,70 @@ __global__ __launch_bounds__(kRoThreads) void k_row_offsets(
         row_offsets[r] = (int32_t)((ka + (int64_t)cnt[r - r0]) * per_entry);
 }
 
+// Full-row COO (keys are row ids, each row complete): row_offsets[r] =
+// cols * #{keys < r}.  A block owns kRoBits consecutive entries: it finds the
+// keys in its rows with two wave-parallel lower bounds, marks them in an LDS
+// bitmap and turns the bitmap into prefix counts with popcounts.  Blocks past
+// the row_offsets range write col_indices (0..cols-1 per touched row).
+constexpr int kRoBits = 16384;
+
+__global__ __launch_bounds__(kRoThreads) void k_csr_full(
+    const int64_t* __restrict__ keys, const int64_t* d_nnz, int64_t nnz_host, int64_t rows,
+    int64_t cols, int32_t* __restrict__ row_offsets, int64_t nblk_ro,
+    int32_t* __restrict__ col_indices) {
+    const int64_t nnz = d_nnz ? (*d_nnz < nnz_host ? *d_nnz : nnz_host) : nnz_host;
+    if ((int64_t)blockIdx.x >= nblk_ro) {
+        if (col_indices == nullptr) return;
+        const int64_t total4 = nnz * cols / 4;  // cols % 4 == 0 on this path
+        const int64_t stride = ((int64_t)gridDim.x - nblk_ro) * kRoThreads;
+        for (int64_t q = ((int64_t)blockIdx.x - nblk_ro) * kRoThreads + threadIdx.x; q < total4;
+             q += stride) {
+            const int32_t c = (int32_t)((q * 4) % cols);
+            reinterpret_cast<int4*>(col_indices)[q] = make_int4(c, c + 1, c + 2, c + 3);
+        }
+        return;
+    }
+    __shared__ uint32_t bits[kRoBits / 32];
+    __shared__ uint32_t wpre[kRoBits / 32];
+    __shared__ int64_t bounds[2];
+    __shared__ uint32_t wt[kRoThreads / kWave];
+    const int64_t r0 = (int64_t)blockIdx.x * kRoBits;
+    const int64_t r1 = (r0 + kRoBits < rows + 1) ? r0 + kRoBits : rows + 1;
+    const int w = (int)(threadIdx.x >> 6);
+    if (w < 2) {
+        const int64_t lb = wave_lower_bound(keys, nnz, w == 0 ? r0 : r1);
+        if (lane_id() == 0) bounds[w] = lb;
+    }
+    for (int i = threadIdx.x; i < kRoBits / 32; i += kRoThreads) bits[i] = 0u;
+    __syncthreads();
+    const int64_t ka = bounds[0], kb = bounds[1];
+    for (int64_t k = ka + threadIdx.x; k < kb; k += kRoThreads) {
+        const int64_t o = keys[k] - r0;  // inside [0, kRoBits) for canonical keys
+        if ((uint64_t)o < (uint64_t)kRoBits) atomicOr(&bits[o >> 5], 1u << (o & 31));
+    }
+    __syncthreads();
+    constexpr int kWordsPer = kRoBits / 32 / kRoThreads;
+    uint32_t c[kWordsPer], sum = 0;
+#pragma unroll
+    for (int j = 0; j < kWordsPer; ++j) {
+        c[j] = (uint32_t)__popc(bits[threadIdx.x * kWordsPer + j]);
+        sum += c[j];
+    }
+    uint32_t total;
+    uint32_t run = block_excl_scan(sum, wt, &total);
+#pragma unroll
+    for (int j = 0; j < kWordsPer; ++j) {
+        wpre[threadIdx.x * kWordsPer + j] = run;
+        run += c[j];
+    }
+    __syncthreads();
+    for (int64_t r = r0 + threadIdx.x; r < r1; r += kRoThreads) {
+        const int o = (int)(r - r0);
+        const uint32_t below = wpre[o >> 5] + (uint32_t)__popc(bits[o >> 5] & ((1u << (o & 31)) - 1u));
+        row_offsets[r] = (int32_t)((ka + (int64_t)below) * cols);
+    }
+}
+
 // col_indices of full rows: 0..cols-1 repeated for every touched row.
 __global__ void k_full_cols(int32_t* __restrict__ ci, const int64_t* d_nnz, int64_t nnz_host,
                             int64_t cols) {
@@ -318,15 +382,24 @@ extern "C" int csr_from_coo(const spopt_coo* in, int64_t rows, int64_t cols,
         });
         if (rc) return rc;
     }
-    k_row_offsets<<<(unsigned)ceil_div(rows + 1, kRoRows), kRoThreads, 0, st>>>(
-        in->indices, in->d_nnz, in->nnz, rows, cols, in->width, row_offsets);
-    SPOPT_LAUNCHED();
-    if (full) {
-        if (col_indices) {
+    if (full && (cols & 3) == 0 && (col_indices == nullptr || aligned16(col_indices))) {
+        // row_offsets and col_indices in one launch.
+        const int64_t nblk_ro = ceil_div(rows + 1, kRoBits);
+        const int64_t nblk_ci = col_indices ? grid_for(in->nnz * cols / 4, kRoThreads, 1024) : 0;
+        k_csr_full<<<(unsigned)(nblk_ro + nblk_ci), kRoThreads, 0, st>>>(
+            in->indices, in->d_nnz, in->nnz, rows, cols, row_offsets, nblk_ro, col_indices);
+        SPOPT_LAUNCHED();
+    } else {
+        k_row_offsets<<<(unsigned)ceil_div(rows + 1, kRoRows), kRoThreads, 0, st>>>(
+            in->indices, in->d_nnz, in->nnz, rows, cols, in->width, row_offsets);
+        SPOPT_LAUNCHED();
+        if (full && col_indices) {
             k_full_cols<<<grid_for(in->nnz * cols / 4 + 1, 256), 256, 0, st>>>(
                 col_indices, in->d_nnz, in->nnz, cols);
             SPOPT_LAUNCHED();
         }
+    }
+    if (full) {
         if (values && values != in->values) {
             k_copy_f32<<<grid_for(in->nnz * cols / 4 + 1, 256), 256, 0, st>>>(
                 in->values, values, in->d_nnz, in->nnz, cols);

@@ -16,16 +16,22 @@
 // hyper-parameters and t (1 - beta, 1 - beta^t, beta^gap for short gaps) are
 // computed on the host in double.
 //
-// Work mapping: LPR lanes per touched row, 64/LPR rows per wave.  A full row
-// (all cols entries present) is moved with 16-byte loads and stores of p, m,
-// v, last_step and g; a partial row uses one lane per entry.  Rows come from
-// a touched-row list (CSR) or the keys of a full-row COO; without a list the
-// CSR kernel scans row_offsets 64 rows per wave.
+// Work mapping: LPR lanes per touched row, 64/LPR rows per wave at a time and
+// a batch of ITERS such groups per wave.  A full row (all cols entries
+// present) is moved with 16-byte loads and stores of p, m, v, last_step and g;
+// a partial row uses one lane per entry.  Rows come from a touched-row list
+// (CSR) or the keys of a full-row COO; without a list the CSR kernel scans
+// row_offsets 64 rows per wave.
 #include "common.hpp"
 
 namespace spopt {
 
 
+// Per-coordinate ops.  A vector step is split into phases so that a kernel can
+// issue every load of a batch as straight-line code before it computes:
+//   load(i, r)      p, m, v (and last_step) of 4 coordinates,
+//   prep(r, x)      loads that depend on them (beta^gap from the table),
+//   compute(r, x, g), store(i, r).
 template <int MODE>
 struct AdamOp {
     float* __restrict__ p;
@@ -38,27 +44,30 @@ struct AdamOp {
         float4 p, m, v;
         int4 ls;
     };
+    struct Aux {
+        double d1[4], d2[4];
+    };
 
-    // beta^gap: 1 step -> beta; shorter gaps from the host-built pow() table;
-    // longer ones exp2(gap * log2 beta).  Skipped when m = v = 0 (a coordinate
-    // never touched), where any finite factor gives the same zero.
-    __device__ __forceinline__ void decay(int32_t gap, double& d1, double& d2) const {
-        if (gap == 1) return;
-        if ((uint32_t)gap < (uint32_t)kPowTable) {
-            d1 = a.pow1[gap];
-            d2 = a.pow2[gap];
-        } else {
-            d1 = exp2((double)gap * a.l2b1);
-            d2 = exp2((double)gap * a.l2b2);
-        }
-    }
-
-    __device__ __forceinline__ void coord(float& pp, float& mm, float& vv, int32_t last,
-                                          float g) const {
+    // beta^gap: gap 1 -> beta; gaps below kPowTable -> the host's pow() values
+    // (t1, t2, fetched in prep); longer gaps -> exp2(gap * log2 beta), skipped
+    // when m = v = 0 (never touched), where any finite factor gives zero.
+    __device__ __forceinline__ void coord(float& pp, float& mm, float& vv, int32_t last, double t1,
+                                          double t2, float g) const {
 #pragma clang fp contract(off)
         double d1 = a.beta1, d2 = a.beta2;
         const double m0 = mm, v0 = vv, gd = g;
-        if (MODE == SPOPT_MODE_DORMANCY && (m0 != 0.0 || v0 != 0.0)) decay(a.t - last, d1, d2);
+        if (MODE == SPOPT_MODE_DORMANCY) {
+            const int32_t gap = a.t - last;
+            if (gap != 1) {
+                if ((uint32_t)gap < (uint32_t)kPowTable) {
+                    d1 = t1;
+                    d2 = t2;
+                } else if (m0 != 0.0 || v0 != 0.0) {
+                    d1 = exp2((double)gap * a.l2b1);
+                    d2 = exp2((double)gap * a.l2b2);
+                }
+            }
+        }
         const double m1 = d1 * m0 + a.c1 * gd;
         const double v1 = d2 * v0 + a.c2 * (gd * gd);
         const double m_hat = m1 / a.bc1;
@@ -67,6 +76,11 @@ struct AdamOp {
         pp = (float)p1;
         mm = (float)m1;
         vv = (float)v1;
+    }
+
+    __device__ __forceinline__ int table_index(int32_t last) const {
+        const int32_t gap = a.t - last;
+        return gap < 0 ? 0 : (gap >= kPowTable ? kPowTable - 1 : gap);
     }
 
     __device__ __forceinline__ void load(int64_t i, Vec& r) const {
@@ -78,11 +92,21 @@ struct AdamOp {
         else
             r.ls = make_int4(0, 0, 0, 0);
     }
-    __device__ __forceinline__ void compute(Vec& r, const float4 g) const {
-        coord(r.p.x, r.m.x, r.v.x, r.ls.x, g.x);
-        coord(r.p.y, r.m.y, r.v.y, r.ls.y, g.y);
-        coord(r.p.z, r.m.z, r.v.z, r.ls.z, g.z);
-        coord(r.p.w, r.m.w, r.v.w, r.ls.w, g.w);
+    __device__ __forceinline__ void prep(const Vec& r, Aux& x) const {
+        if (MODE == SPOPT_MODE_DORMANCY) {
+            const int i0 = table_index(r.ls.x), i1 = table_index(r.ls.y);
+            const int i2 = table_index(r.ls.z), i3 = table_index(r.ls.w);
+            x.d1[0] = a.pow1[i0]; x.d2[0] = a.pow2[i0];
+            x.d1[1] = a.pow1[i1]; x.d2[1] = a.pow2[i1];
+            x.d1[2] = a.pow1[i2]; x.d2[2] = a.pow2[i2];
+            x.d1[3] = a.pow1[i3]; x.d2[3] = a.pow2[i3];
+        }
+    }
+    __device__ __forceinline__ void compute(Vec& r, const Aux& x, const float4 g) const {
+        coord(r.p.x, r.m.x, r.v.x, r.ls.x, x.d1[0], x.d2[0], g.x);
+        coord(r.p.y, r.m.y, r.v.y, r.ls.y, x.d1[1], x.d2[1], g.y);
+        coord(r.p.z, r.m.z, r.v.z, r.ls.z, x.d1[2], x.d2[2], g.z);
+        coord(r.p.w, r.m.w, r.v.w, r.ls.w, x.d1[3], x.d2[3], g.w);
     }
     __device__ __forceinline__ void store(int64_t i, const Vec& r) const {
         *reinterpret_cast<float4*>(p + i) = r.p;
@@ -93,7 +117,13 @@ struct AdamOp {
     __device__ __forceinline__ void scalar(int64_t i, float g) const {
         float pp = p[i], mm = m[i], vv = v[i];
         const int32_t last = (MODE == SPOPT_MODE_DORMANCY) ? ls[i] : 0;
-        coord(pp, mm, vv, last, g);
+        double t1 = 1.0, t2 = 1.0;
+        if (MODE == SPOPT_MODE_DORMANCY) {
+            const int k = table_index(last);
+            t1 = a.pow1[k];
+            t2 = a.pow2[k];
+        }
+        coord(pp, mm, vv, last, t1, t2, g);
         p[i] = pp;
         m[i] = mm;
         v[i] = vv;
@@ -110,6 +140,7 @@ struct SgdOp {
     struct Vec {
         float4 p, b;
     };
+    struct Aux {};
 
     __device__ __forceinline__ void coord(float& pp, float& bb, float g) const {
 #pragma clang fp contract(off)
@@ -130,7 +161,8 @@ struct SgdOp {
         else
             r.b = make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    __device__ __forceinline__ void compute(Vec& r, const float4 g) const {
+    __device__ __forceinline__ void prep(const Vec&, Aux&) const {}
+    __device__ __forceinline__ void compute(Vec& r, const Aux&, const float4 g) const {
         coord(r.p.x, r.b.x, g.x);
         coord(r.p.y, r.b.y, g.y);
         coord(r.p.z, r.b.z, g.z);
@@ -182,36 +214,98 @@ struct SrcCsrTouched {
     }
 };
 
-template <class Op, class Src, int LPR>
+// Each wave takes a batch of RPW*ITERS consecutive touched rows.  Lanes
+// 0..RPW*ITERS-1 first fetch one row each (id, start of its values, length),
+// so the dependent index loads of the whole batch cost one round trip; then
+// every sub-group issues the 16-byte loads of all ITERS of its full rows
+// before it computes and stores any of them.  Partial rows (and rows whose
+// values are not 16-byte aligned) take a scalar loop, one lane per entry.
+template <class Op, class Src, int LPR, int ITERS>
 __global__ __launch_bounds__(256) void k_update_rows(Op op, Src src, const int64_t* d_count,
                                                      int64_t count_host, int64_t rows,
                                                      int64_t cols, const float* __restrict__ g,
                                                      int vec_ok) {
     const int64_t count = d_count ? (*d_count < count_host ? *d_count : count_host) : count_host;
     constexpr int RPW = kWave / LPR;
+    constexpr int BATCH = RPW * ITERS;
+    static_assert(BATCH <= kWave, "one lane per row of the batch");
     const int lane = lane_id();
     const int sub = lane / LPR, sl = lane % LPR;
     const int64_t gw = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
     const int64_t nw = ((int64_t)gridDim.x * blockDim.x) >> 6;
     const int64_t nvec = cols >> 2;
-    for (int64_t k = gw * RPW + sub; k < count; k += nw * RPW) {
-        int64_t row, st, len;
-        src.get(k, row, st, len);
-        if ((uint64_t)row >= (uint64_t)rows || len <= 0) continue;
-        const int64_t base = row * cols;
-        if (len == cols && vec_ok && (st & 3) == 0) {
-            for (int64_t c4 = sl; c4 < nvec; c4 += LPR) {
-                typename Op::Vec r;
-                op.load(base + 4 * c4, r);
-                const float4 gv = *reinterpret_cast<const float4*>(g + st + 4 * c4);
-                op.compute(r, gv);
-                op.store(base + 4 * c4, r);
+    for (int64_t k0 = gw * BATCH; k0 < count; k0 += nw * BATCH) {
+        int64_t prow = -1, pst = 0, plen = 0;
+        if (lane < BATCH && k0 + lane < count) src.get(k0 + lane, prow, pst, plen);
+        int64_t row[ITERS], st[ITERS], len[ITERS];
+#pragma unroll
+        for (int it = 0; it < ITERS; ++it) {
+            const int from = it * RPW + sub;
+            row[it] = __shfl(prow, from, kWave);
+            st[it] = __shfl(pst, from, kWave);
+            len[it] = __shfl(plen, from, kWave);
+            if ((uint64_t)row[it] >= (uint64_t)rows) len[it] = 0;
+        }
+        if (vec_ok && nvec <= LPR) {
+            // One 16-byte vector per lane covers a full row.  The loads of the
+            // batch are straight-line code: a lane without a full row loads
+            // element 0 instead and drops the result, so no branch separates
+            // the loads and all of them are in flight together.
+            typename Op::Vec r[ITERS];
+            typename Op::Aux x[ITERS];
+            float4 gv[ITERS];
+            bool act[ITERS];
+#pragma unroll
+            for (int it = 0; it < ITERS; ++it) {
+                act[it] = len[it] == cols && (st[it] & 3) == 0 && sl < nvec;
+                const int64_t off = act[it] ? row[it] * cols + 4 * sl : 0;
+                const int64_t goff = act[it] ? st[it] + 4 * sl : 0;
+                op.load(off, r[it]);
+                gv[it] = *reinterpret_cast<const float4*>(g + goff);
+            }
+#pragma unroll
+            for (int it = 0; it < ITERS; ++it) op.prep(r[it], x[it]);
+#pragma unroll
+            for (int it = 0; it < ITERS; ++it) {
+                if (act[it]) {
+                    op.compute(r[it], x[it], gv[it]);
+                    op.store(row[it] * cols + 4 * sl, r[it]);
+                }
+            }
+            bool full[ITERS];
+#pragma unroll
+            for (int it = 0; it < ITERS; ++it) full[it] = len[it] == cols && (st[it] & 3) == 0;
+#pragma unroll
+            for (int it = 0; it < ITERS; ++it) {
+                if (full[it] || len[it] <= 0) continue;
+                const int64_t n = len[it] < cols ? len[it] : cols;
+                for (int64_t j = sl; j < n; j += LPR) {
+                    const int64_t c = src.col(st[it], j);
+                    if ((uint64_t)c < (uint64_t)cols) op.scalar(row[it] * cols + c, g[st[it] + j]);
+                }
             }
         } else {
-            const int64_t n = len < cols ? len : cols;
-            for (int64_t j = sl; j < n; j += LPR) {
-                const int64_t c = src.col(st, j);
-                if ((uint64_t)c < (uint64_t)cols) op.scalar(base + c, g[st + j]);
+#pragma unroll
+            for (int it = 0; it < ITERS; ++it) {
+                if (len[it] <= 0) continue;
+                const int64_t base = row[it] * cols;
+                if (vec_ok && len[it] == cols && (st[it] & 3) == 0) {
+                    for (int64_t c4 = sl; c4 < nvec; c4 += LPR) {
+                        typename Op::Vec r;
+                        typename Op::Aux x;
+                        op.load(base + 4 * c4, r);
+                        const float4 gv = *reinterpret_cast<const float4*>(g + st[it] + 4 * c4);
+                        op.prep(r, x);
+                        op.compute(r, x, gv);
+                        op.store(base + 4 * c4, r);
+                    }
+                } else {
+                    const int64_t n = len[it] < cols ? len[it] : cols;
+                    for (int64_t j = sl; j < n; j += LPR) {
+                        const int64_t c = src.col(st[it], j);
+                        if ((uint64_t)c < (uint64_t)cols) op.scalar(base + c, g[st[it] + j]);
+                    }
+                }
             }
         }
     }
@@ -278,25 +372,39 @@ static unsigned grid_cap(int64_t blocks, int64_t cap = 4096) {
     return (unsigned)(blocks < cap ? blocks : cap);
 }
 
+template <class Op>
+struct RowBatch {
+    static constexpr int kIters = 4;  // full rows per sub-group in flight
+};
+template <int MODE>
+struct RowBatch<AdamOp<MODE>> {
+    static constexpr int kIters = 2;  // Adam holds more state per row in registers
+};
+
 template <class Op, class Src>
 static int launch_rows(const Op& op, const Src& src, const int64_t* d_count, int64_t count,
                        int64_t rows, int64_t cols, const float* g, bool vec_ok, hipStream_t s) {
+    constexpr int kIters = RowBatch<Op>::kIters;
     const int lpr = lanes_per_row(cols);
-    const int64_t rows_per_block = 4 * (kWave / lpr);
+    const int64_t rows_per_block = 4 * (kWave / lpr) * kIters;
     const unsigned grid = grid_cap(ceil_div(count, rows_per_block));
     const int v = vec_ok ? 1 : 0;
     switch (lpr) {
         case 4:
-            k_update_rows<Op, Src, 4><<<grid, 256, 0, s>>>(op, src, d_count, count, rows, cols, g, v);
+            k_update_rows<Op, Src, 4, 1><<<grid_cap(ceil_div(count, 64)), 256, 0, s>>>(
+                op, src, d_count, count, rows, cols, g, v);
             break;
         case 16:
-            k_update_rows<Op, Src, 16><<<grid, 256, 0, s>>>(op, src, d_count, count, rows, cols, g, v);
+            k_update_rows<Op, Src, 16, kIters><<<grid, 256, 0, s>>>(op, src, d_count, count, rows,
+                                                                    cols, g, v);
             break;
         case 32:
-            k_update_rows<Op, Src, 32><<<grid, 256, 0, s>>>(op, src, d_count, count, rows, cols, g, v);
+            k_update_rows<Op, Src, 32, kIters><<<grid, 256, 0, s>>>(op, src, d_count, count, rows,
+                                                                    cols, g, v);
             break;
         default:
-            k_update_rows<Op, Src, 64><<<grid, 256, 0, s>>>(op, src, d_count, count, rows, cols, g, v);
+            k_update_rows<Op, Src, 64, kIters><<<grid, 256, 0, s>>>(op, src, d_count, count, rows,
+                                                                    cols, g, v);
             break;
     }
     SPOPT_LAUNCHED();
