@@ -230,3 +230,9 @@ def partial_rows(w: Workload, step: int):
     if w.grad_std != 1.0:
         vals *= np.float32(w.grad_std)
     return ent_rows, ent_cols, vals
+
+
+def partial_rows_many(w: Workload, steps):
+    """partial_rows() for several steps, generated on a thread pool."""
+    with ThreadPoolExecutor(_threads()) as ex:
+        return list(ex.map(lambda s: partial_rows(w, s), steps))
