@@ -33,6 +33,26 @@ HBM_PEAK_GBS = 8000.0
 BYTES_PER_COORD = 36
 BYTES_PER_ROW = 16
 
+# HBM bytes per launch of the update kernel on this workload, from two
+# rocprofv3 --pmc passes of this command (FETCH_SIZE scaled by 2.0 and
+# WRITE_SIZE by 1.0: a plain 1 GiB device copy reads 512 MiB by FETCH_SIZE and
+# writes 1 GiB by WRITE_SIZE).  Valid only for the kernel sources they were
+# taken with; reported as null once those sources change.
+UPDATE_SOURCES = ("lazy_optimizer_step_amd/csrc/update.hip",
+                  "lazy_optimizer_step_amd/csrc/common.hpp")
+UPDATE_TRAFFIC = {"sources_sha256": "685678540a177313871765b5edd68b564eee48e774c2e7a2903e0c36d10bc48a",
+                  "fetch_bytes": 2.0 * 33838.2 * 1024, "write_bytes": 1.0 * 59032.1 * 1024}
+
+
+def sources_sha256() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in UPDATE_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
 
 def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
@@ -48,6 +68,19 @@ def parse():
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling HBM counters)")
     return ap.parse_args()
+
+
+def calibrate_sleep(torch, stream, hold_ms: float) -> int:
+    """Spin-kernel cycles that hold the stream for about hold_ms milliseconds."""
+    probe = 1 << 20
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(probe)
+    e0.record(stream)
+    torch.cuda._sleep(probe)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = max(e0.elapsed_time(e1), 1e-3)
+    return int(min(probe * hold_ms / ms, 1 << 40))
 
 
 def copy_probe(steps: int) -> None:
@@ -157,9 +190,14 @@ def main() -> int:
     for s in range(W):
         step(s)
     torch.cuda.synchronize()
-    log(f"timed {K} steps")
+    # Hold the stream with a bounded spin kernel while the host queues every
+    # timed step behind it, so the steps then run back to back and the events
+    # time device work rather than the host's launch rate.
+    cycles = calibrate_sleep(torch, stream, hold_ms=2.0 + 0.5 * K)
+    log(f"timed {K} steps (queued behind a {cycles}-cycle spin)")
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(cycles)
     t_start.record(stream)
     for s in range(W, W + K):
         step(s)
@@ -174,6 +212,9 @@ def main() -> int:
     upd = np.array([ev[s][2].elapsed_time(ev[s][3]) for s in range(W, W + K)])
     upd_bytes = BYTES_PER_COORD * U * Cc + BYTES_PER_ROW * U
     achieved = float((upd_bytes / (upd * 1e-3)).mean() / 1e9)
+    traffic = None
+    if sources_sha256() == UPDATE_TRAFFIC["sources_sha256"]:
+        traffic = UPDATE_TRAFFIC["fetch_bytes"] + UPDATE_TRAFFIC["write_bytes"]
 
     result = {
         "metric": METRIC,
@@ -192,7 +233,9 @@ def main() -> int:
                    "zipf_s": w.zipf_s, "mode": w.mode, "state": "p,m,v float32 + last_step int32",
                    "mean_unique_rows": float(U.mean())},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled)",
+                     "algorithmic_bytes_per_launch": float(upd_bytes.mean()),
                      "kernel": "k_update_rows<AdamOp<DormancyDecay>, SrcCsrTouched, 32>",
                      "mean_us": float(upd.mean() * 1e3),
                      "coords_per_s_G": float((U * Cc / (upd * 1e-3)).mean() / 1e9)},
