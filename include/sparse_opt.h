@@ -195,7 +195,7 @@ SPOPT_API int sparse_opt_workspace_size(int64_t n, int64_t width, int64_t key_sp
  * width == 1 gives a 1-D CooGradient; width == cols with key_space == rows
  * gives full table rows.
  * Workspace: device, at least sparse_opt_workspace_size(n, width, key_space).
- * Errors: SPOPT_EINVAL, SPOPT_EWORKSPACE, SPOPT_EOVERFLOW (n >= 2^31);
+ * Errors: SPOPT_EINVAL, SPOPT_EWORKSPACE, SPOPT_EOVERFLOW (n >= 2^30);
  * with SPOPT_VALIDATE also SPOPT_ERANGE (an id outside [0, key_space)) and
  * SPOPT_ENONFINITE.  In trusted mode an out-of-range id is still detected on
  * the device; the call then sets *d_nunique = 0 (an empty gradient) and

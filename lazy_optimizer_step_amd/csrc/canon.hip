@@ -5,10 +5,10 @@
 // sparse_optimizer page requires of a CooGradient (strictly ascending
 // indices):
 //   1. pack each lookup as (id << pos_bits) | position and radix-sort the
-//      packed words on the id bits only (LSD, 8-bit digits, stable, so equal
-//      ids keep lookup order): one kernel counts the digits of every pass,
-//      then each pass is one kernel whose tiles find their offsets by
-//      decoupled look-back;
+//      packed words on the id bits only (LSD, stable, so equal ids keep
+//      lookup order, digits of at most 8 bits): one kernel counts the digits
+//      of every pass, then each pass is one kernel whose tiles find their
+//      offsets by decoupled look-back;
 //   2. mark segment heads (id differs from its predecessor) and number them
 //      in one look-back pass, giving every lookup its segment number and
 //      emitting the distinct ids;
@@ -27,29 +27,32 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kIpt = 4;                         // items per thread
 constexpr int kTile = kThreads * kIpt;          // 1024 lookups per sort / segment tile
-constexpr int kRadixBits = 8;
+constexpr int kRadixBits = 8;                   // at most 256 buckets per radix pass
 constexpr int kRadix = 1 << kRadixBits;
 constexpr int kMaxPasses = 8;
 constexpr int kChunk = 64;                      // sorted lookups per wave, summing
 constexpr int kFixThreads = 1024;               // block of the ordered combine
 constexpr int kFixWaves = kFixThreads / kWave;
 
-// Decoupled look-back words: bits 31..30 state (aggregate / inclusive prefix),
-// bits 29..0 a count, so n stays below 2^30.
+// Decoupled look-back.  A tile publishes one 32-bit word per count:
+// bits 31..30 its state (aggregate of this tile / inclusive prefix through
+// this tile), bits 29..0 the count, so n stays below 2^30.  Each word carries
+// its own state and is written and read with device-coherent atomics, so no
+// fence is needed.
 constexpr uint32_t kLbAgg = 1u << 30;
 constexpr uint32_t kLbInc = 2u << 30;
 constexpr uint32_t kLbState = 3u << 30;
 constexpr uint32_t kLbCount = (1u << 30) - 1u;
 // A tile waits only for tiles that took their ticket earlier, which publish
-// their own count before they wait on anybody; the bound only turns a bug
+// their own counts before they wait on anybody; the bound only turns a bug
 // into a reported error instead of a hang.
 constexpr uint32_t kSpinLimit = 1u << 16;
 
 struct CanonLayout {
-    int key_bits, pos_bits, passes;
+    int key_bits, pos_bits, passes, digit_bits;
     int64_t ntiles, nchunks;
-    size_t off_a, off_b, off_clear, clear_bytes, off_status, off_tickets, off_hist, off_lb,
-        off_seglb, off_segid, off_segstart, off_pfirst, off_plast, total;
+    size_t off_a, off_b, off_clear, clear_bytes, off_status, off_tickets, off_hist,
+        off_segwords, off_words, off_segid, off_segstart, off_pfirst, off_plast, total;
 };
 
 static int bits_for(uint64_t x) {  // bits needed to represent values in [0, x)
@@ -63,9 +66,15 @@ static bool canon_layout(int64_t n, int64_t width, int64_t key_space, CanonLayou
     L->key_bits = bits_for((uint64_t)key_space);
     L->pos_bits = bits_for((uint64_t)(n > 0 ? n : 1));
     if (L->key_bits + L->pos_bits > 64) return false;
+    // As few passes as digits of at most 8 bits allow, digits as even as
+    // possible.  (Wider digits would need fewer passes, but the look-back
+    // words are device-coherent atomics, which do not coalesce: 1024 or 4096
+    // buckets per tile cost far more per pass than the passes they save.)
     L->passes = (L->key_bits + kRadixBits - 1) / kRadixBits;
+    L->digit_bits = L->passes ? (L->key_bits + L->passes - 1) / L->passes : 0;
     L->ntiles = ceil_div(n, kTile);
     L->nchunks = ceil_div(n, kChunk);
+    const size_t P = (size_t)(L->passes ? L->passes : 1);
     size_t o = 0;
     auto take = [&](size_t bytes) {
         size_t at = o;
@@ -78,10 +87,9 @@ static bool canon_layout(int64_t n, int64_t width, int64_t key_space, CanonLayou
     L->off_clear = o;
     L->off_status = take(sizeof(uint32_t) * 4);
     L->off_tickets = take(sizeof(uint32_t) * (kMaxPasses + 1));
-    L->off_hist = take(sizeof(uint32_t) * (size_t)kRadix * (size_t)(L->passes ? L->passes : 1));
-    L->off_lb = take(sizeof(uint32_t) * (size_t)kRadix * (size_t)L->ntiles *
-                     (size_t)(L->passes ? L->passes : 1));
-    L->off_seglb = take(sizeof(uint32_t) * ((size_t)L->ntiles + 1));
+    L->off_hist = take(sizeof(uint32_t) * (size_t)kRadix * P);
+    L->off_words = take(sizeof(uint32_t) * (size_t)kRadix * (size_t)L->ntiles * P);
+    L->off_segwords = take(sizeof(uint32_t) * (size_t)L->ntiles);
     L->clear_bytes = o - L->off_clear;
     L->off_segid = take(sizeof(int32_t) * (size_t)n);
     L->off_segstart = take(sizeof(int32_t) * ((size_t)n + 1));
@@ -91,17 +99,17 @@ static bool canon_layout(int64_t n, int64_t width, int64_t key_space, CanonLayou
     return true;
 }
 
-__device__ __forceinline__ uint32_t ld_agent(const uint32_t* p) {
+__device__ __forceinline__ uint32_t ld_dev(const uint32_t* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void st_agent(uint32_t* p, uint32_t v) {
+__device__ __forceinline__ void st_dev(uint32_t* p, uint32_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Waits for a look-back word to leave state 0.  Returns false on timeout.
 __device__ __forceinline__ bool lb_wait(const uint32_t* p, uint32_t* out) {
     for (uint32_t spins = 0; spins < kSpinLimit; ++spins) {
-        const uint32_t v = ld_agent(p);
+        const uint32_t v = ld_dev(p);
         if (v & kLbState) {
             *out = v;
             return true;
@@ -121,7 +129,7 @@ __device__ __forceinline__ bool look_back(const uint32_t* lb, int64_t tile, int6
     while (j >= 0) {
         uint32_t v[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = (j - u >= 0) ? ld_agent(lb + (j - u) * stride) : kLbInc;
+        for (int u = 0; u < 8; ++u) v[u] = (j - u >= 0) ? ld_dev(lb + (j - u) * stride) : kLbInc;
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             if (j - u < 0) {
@@ -157,16 +165,18 @@ __global__ void k_status_clear(uint32_t* st, int nwords) {
 // ------------------------------------------------------------------ sort ---
 
 // Range-check ids, pack (id << pos_bits | position), and count the digits of
-// every radix pass into the global per-pass histograms.
+// every radix pass into the global per-pass histograms (LDS first).
 __global__ __launch_bounds__(kThreads) void k_pack(const int64_t* __restrict__ ids, int64_t n,
                                                    int64_t key_space, int pos_bits, int passes,
-                                                   uint64_t* __restrict__ out,
+                                                   int digit_bits, uint64_t* __restrict__ out,
                                                    uint32_t* __restrict__ hist,
                                                    uint32_t* status) {
-    __shared__ uint32_t h[kMaxPasses][kRadix];
-    for (int i = threadIdx.x; i < passes * kRadix; i += kThreads) (&h[0][0])[i] = 0;
+    __shared__ uint32_t h[kMaxPasses * kRadix];
+    const int words = passes * kRadix;
+    for (int i = threadIdx.x; i < words; i += kThreads) h[i] = 0;
     __syncthreads();
     const int64_t base = (int64_t)blockIdx.x * kTile;
+    const uint32_t dmask = (1u << digit_bits) - 1u;
     bool bad = false;
 #pragma unroll
     for (int j = 0; j < kIpt; ++j) {
@@ -180,20 +190,20 @@ __global__ __launch_bounds__(kThreads) void k_pack(const int64_t* __restrict__ i
             const uint64_t packed = ((uint64_t)id << pos_bits) | (uint64_t)i;
             out[i] = packed;
             for (int p = 0; p < passes; ++p)
-                atomicAdd(&h[p][(uint32_t)(packed >> (pos_bits + p * kRadixBits)) & (kRadix - 1)],
+                atomicAdd(&h[p * kRadix + ((uint32_t)(packed >> (pos_bits + p * digit_bits)) & dmask)],
                           1u);
         }
     }
     if (ballot(bad) != 0ull && lane_id() == 0) atomicOr(status, kStatusRange);
     __syncthreads();
-    for (int i = threadIdx.x; i < passes * kRadix; i += kThreads) {
-        const uint32_t c = (&h[0][0])[i];
+    for (int i = threadIdx.x; i < words; i += kThreads) {
+        const uint32_t c = h[i];
         if (c) atomicAdd(&hist[i], c);
     }
 }
 
-// One stable radix pass in a single kernel.  A block takes the next tile
-// ticket, ranks its 1024 items (wave w owns items [w*256, (w+1)*256) in four
+// One stable radix pass (digits of nbits <= 8 bits) in a single kernel.  A
+// block takes the next tile ticket, ranks its 1024 items (wave w owns items [w*256, (w+1)*256) in four
 // rounds of 64: lanes holding the same digit are matched with one ballot per
 // digit bit, a lane's rank is the number of lower lanes with its digit plus
 // the wave's running count of that digit), publishes its per-digit counts,
@@ -228,7 +238,7 @@ __global__ __launch_bounds__(kThreads) void k_onesweep(
         const int64_t i = first + (int64_t)r * kWave + lane;
         valid[r] = i < n;
         key[r] = valid[r] ? in[i] : 0ull;
-        dig[r] = (uint32_t)(key[r] >> shift) & (kRadix - 1);
+        dig[r] = (uint32_t)(key[r] >> shift) & ((1u << nbits) - 1u);
     }
 #pragma unroll
     for (int r = 0; r < kIpt; ++r) {
@@ -262,11 +272,11 @@ __global__ __launch_bounds__(kThreads) void k_onesweep(
     uint32_t excl = 0;
     bool ok = true;
     if (tile == 0) {
-        st_agent(mine, kLbInc | run);
+        st_dev(mine, kLbInc | run);
     } else {
-        st_agent(mine, kLbAgg | run);
+        st_dev(mine, kLbAgg | run);
         ok = look_back(lb + d, tile, kRadix, &excl);
-        if (ok) st_agent(mine, kLbInc | (excl + run));
+        if (ok) st_dev(mine, kLbInc | (excl + run));
     }
     if (!ok) atomicOr(&s_bad, 1u);
     uint32_t total;
@@ -291,48 +301,89 @@ __device__ __forceinline__ bool seg_head(const uint64_t* s, int64_t i, int pos_b
     return i == 0 || (s[i] >> pos_bits) != (s[i - 1] >> pos_bits);
 }
 
-// Segment heads (id differs from its predecessor) of each tile, counted and
-// prefixed across tiles by decoupled look-back in one pass: every sorted
-// lookup gets its segment number, every head writes its id and position.  The
-// last tile publishes U (0 when an id was out of range or a wait timed out)
-// and the sentinel seg_start[U] = n.
+// Segment heads (id differs from its predecessor) of each tile, counted with
+// ballots and prefixed across tiles by the same look-back in one pass: every
+// sorted lookup gets its segment number, every head writes its id and
+// position.  The last tile publishes U (0 when an id was out of range or a
+// wait timed out) and the sentinel seg_start[U] = n.
 __global__ __launch_bounds__(kThreads) void k_segment(
-    const uint64_t* __restrict__ s, int64_t n, int pos_bits, int64_t ntiles, uint32_t* lb,
-    uint32_t* ticket, int32_t* __restrict__ seg_id, int32_t* __restrict__ seg_start,
-    int64_t* __restrict__ out_keys, int64_t* __restrict__ d_nunique, uint32_t* status) {
+    const uint64_t* __restrict__ s, int64_t n, int pos_bits, int64_t ntiles, uint32_t* words,
+    uint32_t* ticket, int32_t* __restrict__ seg_id,
+    int32_t* __restrict__ seg_start, int64_t* __restrict__ out_keys,
+    int64_t* __restrict__ d_nunique, uint32_t* status) {
     if (*status != 0u) {
         if (blockIdx.x == 0 && threadIdx.x == 0) *d_nunique = 0;
         return;
     }
-    __shared__ uint32_t wt[kWaves];
+    __shared__ uint32_t wcount[kWaves];
     __shared__ uint32_t s_tile, s_excl, s_ok;
     const int tid = threadIdx.x;
+    const int w = tid >> 6;
+    const int lane = lane_id();
     if (tid == 0) s_tile = atomicAdd(ticket, 1u);
     __syncthreads();
     const int64_t tile = s_tile;
-    const int64_t base = tile * kTile;
-    bool head[kIpt];
-    uint32_t mine = 0;
+    // Wave w owns the 256 consecutive lookups [w*256, (w+1)*256) of the tile,
+    // in four rounds of 64.
+    const int64_t first = tile * kTile + (int64_t)w * (kIpt * kWave);
+    const uint64_t lt = lanemask_lt();
+    uint64_t hm[kIpt];
+    uint32_t wave_heads = 0;
 #pragma unroll
-    for (int j = 0; j < kIpt; ++j) {
-        const int64_t i = base + (int64_t)j * kThreads + tid;
-        head[j] = i < n && seg_head(s, i, pos_bits);
-        mine += head[j] ? 1u : 0u;
+    for (int r = 0; r < kIpt; ++r) {
+        const int64_t i = first + (int64_t)r * kWave + lane;
+        hm[r] = ballot(i < n && seg_head(s, i, pos_bits));
+        wave_heads += (uint32_t)popc64(hm[r]);
     }
-    uint32_t tile_heads;
-    block_excl_scan(mine, wt, &tile_heads);
-    if (tid == 0) {
+    if (lane == 0) wcount[w] = wave_heads;
+    __syncthreads();
+    uint32_t tile_heads = 0, before_wave = 0;
+    for (int ww = 0; ww < kWaves; ++ww) {
+        if (ww < w) before_wave += wcount[ww];
+        tile_heads += wcount[ww];
+    }
+    if (w == 0) {
+        // Lane l reads the word of tile lo-1-l: one round trip covers 64 earlier
+        // tiles; counts are summed back to the nearest inclusive prefix.
         uint32_t excl = 0;
         bool ok = true;
         if (tile == 0) {
-            st_agent(lb, kLbInc | tile_heads);
+            if (lane == 0) st_dev(words, kLbInc | tile_heads);
         } else {
-            st_agent(lb + tile, kLbAgg | tile_heads);
-            ok = look_back(lb, tile, 1, &excl);
-            if (ok) st_agent(lb + tile, kLbInc | (excl + tile_heads));
+            if (lane == 0) st_dev(words + tile, kLbAgg | tile_heads);
+            int64_t lo = tile;
+            uint32_t spins = 0;
+            while (lo > 0) {
+                const int64_t tj = lo - 1 - lane;
+                const bool valid = tj >= 0;
+                const uint32_t v = valid ? ld_dev(words + tj) : 0u;
+                const uint64_t not_ready = ballot(valid && (v & kLbState) == 0u);
+                const uint64_t inclusive = ballot(valid && (v & kLbState) == kLbInc);
+                const int first_nr = not_ready ? __builtin_ctzll(not_ready) : kWave;
+                const int first_inc = inclusive ? __builtin_ctzll(inclusive) : kWave;
+                const int nvalid = lo < kWave ? (int)lo : kWave;
+                const int take = first_inc < first_nr ? first_inc + 1
+                                                      : (first_nr < nvalid ? first_nr : nvalid);
+                uint32_t part = lane < take ? (v & kLbCount) : 0u;
+#pragma unroll
+                for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off, kWave);
+                excl += part;
+                if (first_inc < first_nr) break;
+                lo -= take;
+                if (take == 0) {
+                    if (++spins > kSpinLimit) {
+                        ok = false;
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
+                }
+            }
+            if (lane == 0 && ok) st_dev(words + tile, kLbInc | (excl + tile_heads));
         }
-        s_excl = excl;
-        s_ok = ok ? 1u : 0u;
+        if (lane == 0) {
+            s_excl = excl;
+            s_ok = ok ? 1u : 0u;
+        }
     }
     __syncthreads();
     if (!s_ok) {
@@ -342,25 +393,25 @@ __global__ __launch_bounds__(kThreads) void k_segment(
         }
         return;
     }
-    uint32_t run = s_excl;
+    uint32_t run = s_excl + before_wave;
 #pragma unroll
-    for (int j = 0; j < kIpt; ++j) {
-        const int64_t i = base + (int64_t)j * kThreads + tid;
-        uint32_t round_total;
-        const uint32_t before = block_excl_scan(head[j] ? 1u : 0u, wt, &round_total);
+    for (int r = 0; r < kIpt; ++r) {
+        const int64_t i = first + (int64_t)r * kWave + lane;
+        const bool h = (hm[r] >> lane) & 1ull;
         if (i < n) {
-            const uint32_t seg = run + before + (head[j] ? 1u : 0u) - 1u;
+            const uint32_t seg = run + (uint32_t)popc64(hm[r] & lt) + (h ? 1u : 0u) - 1u;
             seg_id[i] = (int32_t)seg;
-            if (head[j]) {
+            if (h) {
                 out_keys[seg] = (int64_t)(s[i] >> pos_bits);
                 seg_start[seg] = (int32_t)i;
             }
         }
-        run += round_total;
+        run += (uint32_t)popc64(hm[r]);
     }
     if (tile == ntiles - 1 && tid == 0) {
-        *d_nunique = (int64_t)run;
-        seg_start[run] = (int32_t)n;
+        const uint32_t u = s_excl + tile_heads;
+        *d_nunique = (int64_t)u;
+        seg_start[u] = (int32_t)n;
     }
 }
 
@@ -643,7 +694,7 @@ extern "C" int sparse_opt_workspace_size(int64_t n, int64_t width, int64_t key_s
 extern "C" int coo_from_lookups(const int64_t* ids, const float* vals, int64_t n, int64_t width,
                                 int64_t key_space, int64_t* out_keys, float* out_vals,
                                 int32_t* out_counts, int64_t* d_nunique, void* workspace,
-                                size_t workspace_bytes, void* stream, uint32_t flags) {
+                                size_t workspace_bytes, void* stream, uint32_t flags_arg) {
     hipStream_t st = (hipStream_t)stream;
     CanonLayout L;
     if (n >= ((int64_t)1 << 30)) return fail(SPOPT_EOVERFLOW, "coo_from_lookups: n >= 2^30");
@@ -670,8 +721,8 @@ extern "C" int coo_from_lookups(const int64_t* ids, const float* vals, int64_t n
     uint32_t* status = (uint32_t*)(ws + L.off_status);
     uint32_t* tickets = (uint32_t*)(ws + L.off_tickets);
     uint32_t* hist = (uint32_t*)(ws + L.off_hist);
-    uint32_t* lb = (uint32_t*)(ws + L.off_lb);
-    uint32_t* seglb = (uint32_t*)(ws + L.off_seglb);
+    uint32_t* words = (uint32_t*)(ws + L.off_words);
+    uint32_t* segwords = (uint32_t*)(ws + L.off_segwords);
     int32_t* seg_id = (int32_t*)(ws + L.off_segid);
     int32_t* seg_start = (int32_t*)(ws + L.off_segstart);
     double* pfirst = (double*)(ws + L.off_pfirst);
@@ -682,15 +733,15 @@ extern "C" int coo_from_lookups(const int64_t* ids, const float* vals, int64_t n
     k_clear<<<(unsigned)(ceil_div(n16, 256) < 256 ? ceil_div(n16, 256) : 256), 256, 0, st>>>(
         (uint4*)(ws + L.off_clear), n16);
     SPOPT_LAUNCHED();
-    const bool validate = (flags & SPOPT_VALIDATE) != 0;
+    const bool validate = (flags_arg & SPOPT_VALIDATE) != 0;
     if (validate) {
         const int64_t len = n * width;
         const int grid = (int)(ceil_div(len, 256) < 4096 ? ceil_div(len, 256) : 4096);
         k_check_finite<<<grid, 256, 0, st>>>(vals, len, status);
         SPOPT_LAUNCHED();
     }
-    k_pack<<<(unsigned)L.ntiles, kThreads, 0, st>>>(ids, n, key_space, L.pos_bits, L.passes, a,
-                                                    hist, status);
+    k_pack<<<(unsigned)L.ntiles, kThreads, 0, st>>>(ids, n, key_space, L.pos_bits, L.passes,
+                                                    L.digit_bits, a, hist, status);
     SPOPT_LAUNCHED();
     if (validate) {
         uint32_t h_status = 0;
@@ -701,17 +752,20 @@ extern "C" int coo_from_lookups(const int64_t* ids, const float* vals, int64_t n
     uint64_t* src = a;
     uint64_t* dst = b;
     for (int p = 0; p < L.passes; ++p) {
-        const int rem = L.key_bits - p * kRadixBits;
-        k_onesweep<<<(unsigned)L.ntiles, kThreads, 0, st>>>(
-            src, dst, n, L.pos_bits + p * kRadixBits, rem < kRadixBits ? rem : kRadixBits,
-            hist + p * kRadix, lb + (int64_t)p * L.ntiles * kRadix, tickets + p, status);
+        const int rem = L.key_bits - p * L.digit_bits;
+        const int nbits = rem < L.digit_bits ? rem : L.digit_bits;
+        const int shift = L.pos_bits + p * L.digit_bits;
+        uint32_t* pwords = words + (int64_t)p * L.ntiles * kRadix;
+        const uint32_t* phist = hist + (int64_t)p * kRadix;
+        k_onesweep<<<(unsigned)L.ntiles, kThreads, 0, st>>>(src, dst, n, shift, nbits, phist,
+                                                            pwords, tickets + p, status);
         SPOPT_LAUNCHED();
         uint64_t* t = src;
         src = dst;
         dst = t;
     }
     const uint64_t* sorted = src;
-    k_segment<<<(unsigned)L.ntiles, kThreads, 0, st>>>(sorted, n, L.pos_bits, L.ntiles, seglb,
+    k_segment<<<(unsigned)L.ntiles, kThreads, 0, st>>>(sorted, n, L.pos_bits, L.ntiles, segwords,
                                                        tickets + kMaxPasses, seg_id, seg_start,
                                                        out_keys, d_nunique, status);
     SPOPT_LAUNCHED();
