@@ -10,8 +10,15 @@ resident in HBM before the timed region starts.
 
 Prints one JSON line:  value = touched coordinates updated per second over the
 whole timed region (G/s); roofline = the update kernel's algorithmic bytes per
-launch / its mean duration (HIP events on the launch stream) against 8 TB/s;
+launch / its mean duration (HIP events around every update launch of the timed
+region, on the launch stream) against 8 TB/s; breakdown_us = median time of
+each call from a second, separately timed pass over the same inputs;
 cpu_baseline = the CPU oracle on a bounded sample of the same workload.
+
+Events are created through the HIP runtime with hipEventDisableSystemFence:
+they only take timestamps, and skipping the system-scope release (an L2
+writeback and invalidate per record) keeps them from slowing the work they
+bracket.
 """
 from __future__ import annotations
 
@@ -68,6 +75,57 @@ def parse():
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling HBM counters)")
     return ap.parse_args()
+
+
+class HipEvents:
+    """Timing-only HIP events (hipEventDisableSystemFence) recorded on a given
+    stream, from the HIP runtime this process has already loaded."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, count: int):
+        import ctypes as C
+
+        path = None
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64.so" in line:
+                    path = line.split()[-1]
+                    break
+        if path is None:
+            raise RuntimeError("the HIP runtime is not loaded in this process")
+        self.C = C
+        self.hip = C.CDLL(path)
+        self.hip.hipEventCreateWithFlags.argtypes = [C.POINTER(C.c_void_p), C.c_uint]
+        self.hip.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [C.c_void_p]
+        self.ev = []
+        for _ in range(count):
+            e = C.c_void_p()
+            self._check(self.hip.hipEventCreateWithFlags(C.byref(e), self.DISABLE_SYSTEM_FENCE),
+                        "hipEventCreateWithFlags")
+            self.ev.append(e)
+
+    @staticmethod
+    def _check(rc: int, what: str) -> None:
+        if rc != 0:
+            raise RuntimeError(f"{what} failed with HIP error {rc}")
+
+    def record(self, i: int, stream) -> None:
+        self._check(self.hip.hipEventRecord(self.ev[i], self.C.c_void_p(stream.cuda_stream)),
+                    "hipEventRecord")
+
+    def ms(self, i: int, j: int) -> float:
+        out = self.C.c_float()
+        self._check(self.hip.hipEventElapsedTime(self.C.byref(out), self.ev[i], self.ev[j]),
+                    "hipEventElapsedTime")
+        return float(out.value)
+
+    def close(self) -> None:
+        for e in self.ev:
+            self.hip.hipEventDestroy(e)
+        self.ev = []
 
 
 def calibrate_sleep(torch, stream, hold_ms: float) -> int:
@@ -170,46 +228,63 @@ def main() -> int:
     col_indices = torch.empty(n * Cc, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(W + K)]
-
-    def step(s: int) -> None:
-        e = ev[s]
-        e[0].record(stream)
+    def canon(s: int) -> None:
         L.coo_from_lookups(ids_d[s], grads_d[s], R, out_keys=keys, out_vals=sums,
                            out_counts=counts, d_nunique=nuniq[s:s + 1], workspace=ws,
                            stream=stream)
-        e[1].record(stream)
+
+    def csr(s: int):
         coo = L.CooGradient(keys, sums, dim=R, width=Cc, nnz=n, d_nnz=nuniq[s:s + 1])
-        csr = L.csr_from_coo(coo, R, Cc, row_offsets=row_offsets, col_indices=col_indices,
-                             copy_values=False, stream=stream)
-        e[2].record(stream)
-        opt.step(csr, stream=stream)
-        e[3].record(stream)
+        return L.csr_from_coo(coo, R, Cc, row_offsets=row_offsets, col_indices=col_indices,
+                              copy_values=False, stream=stream)
 
     log(f"warmup {W} steps")
     for s in range(W):
-        step(s)
+        canon(s)
+        opt.step(csr(s), stream=stream)
     torch.cuda.synchronize()
-    # Hold the stream with a bounded spin kernel while the host queues every
-    # timed step behind it, so the steps then run back to back and the events
-    # time device work rather than the host's launch rate.
+
+    # Timed region: K whole steps.  Events bracket the region and every update
+    # launch in it.  A bounded spin kernel holds the stream while the host
+    # queues every step behind it, so the steps run back to back and the
+    # events time device work rather than the host's launch rate.
+    ev = HipEvents(2 + 2 * K)
     cycles = calibrate_sleep(torch, stream, hold_ms=2.0 + 0.5 * K)
     log(f"timed {K} steps (queued behind a {cycles}-cycle spin)")
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda._sleep(cycles)
-    t_start.record(stream)
-    for s in range(W, W + K):
-        step(s)
-    t_end.record(stream)
+    ev.record(0, stream)
+    for k, s in enumerate(range(W, W + K)):
+        canon(s)
+        g = csr(s)
+        ev.record(2 + 2 * k, stream)
+        opt.step(g, stream=stream)
+        ev.record(3 + 2 * k, stream)
+    ev.record(1, stream)
     torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
+    total_ms = ev.ms(0, 1)
+    upd = np.array([ev.ms(2 + 2 * k, 3 + 2 * k) for k in range(K)])
+    ev.close()
+
+    # Breakdown (not part of the value): the same K inputs again, every call
+    # bracketed by events.
+    bev = HipEvents(4 * K)
+    torch.cuda._sleep(cycles)
+    for k, s in enumerate(range(W, W + K)):
+        bev.record(4 * k, stream)
+        canon(s)
+        bev.record(4 * k + 1, stream)
+        g = csr(s)
+        bev.record(4 * k + 2, stream)
+        opt.step(g, stream=stream)
+        bev.record(4 * k + 3, stream)
+    torch.cuda.synchronize()
+    canon_t = np.array([bev.ms(4 * k, 4 * k + 1) for k in range(K)])
+    csr_t = np.array([bev.ms(4 * k + 1, 4 * k + 2) for k in range(K)])
+    upd_b = np.array([bev.ms(4 * k + 2, 4 * k + 3) for k in range(K)])
+    bev.close()
 
     U = nuniq.cpu().numpy()[W:]
     coords = int(U.sum()) * Cc
-    canon = np.array([ev[s][0].elapsed_time(ev[s][1]) for s in range(W, W + K)])
-    csr_t = np.array([ev[s][1].elapsed_time(ev[s][2]) for s in range(W, W + K)])
-    upd = np.array([ev[s][2].elapsed_time(ev[s][3]) for s in range(W, W + K)])
     upd_bytes = BYTES_PER_COORD * U * Cc + BYTES_PER_ROW * U
     achieved = float((upd_bytes / (upd * 1e-3)).mean() / 1e9)
     traffic = None
@@ -239,9 +314,9 @@ def main() -> int:
                      "kernel": "k_update_rows<AdamOp<DormancyDecay>, SrcCsrTouched, 32>",
                      "mean_us": float(upd.mean() * 1e3),
                      "coords_per_s_G": float((U * Cc / (upd * 1e-3)).mean() / 1e9)},
-        "breakdown_us": {"coo_from_lookups": float(np.median(canon) * 1e3),
+        "breakdown_us": {"coo_from_lookups": float(np.median(canon_t) * 1e3),
                          "csr_from_coo": float(np.median(csr_t) * 1e3),
-                         "sparse_adam_step": float(np.median(upd) * 1e3)},
+                         "sparse_adam_step": float(np.median(upd_b) * 1e3)},
     }
     if args.cpu_seconds > 0:
         log("cpu baseline (oracle)")

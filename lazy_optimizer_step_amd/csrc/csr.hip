@@ -73,10 +73,17 @@ __global__ __launch_bounds__(kRoThreads) void k_row_offsets(
 // Full-row COO (keys are row ids, each row complete): row_offsets[r] =
 // cols * #{keys < r}.  A block owns kRoBits consecutive entries: it finds the
 // keys in its rows with two wave-parallel lower bounds, marks them in an LDS
-// bitmap and turns the bitmap into prefix counts with popcounts.  Blocks past
-// the row_offsets range write col_indices (0..cols-1 per touched row).
-constexpr int kRoBits = 16384;
+// bitmap and turns the bitmap into prefix counts with popcounts; each thread
+// then writes four consecutive offsets per 16-byte store (VEC, chosen on the
+// host when row_offsets is 16-byte aligned).  Blocks past the row_offsets
+// range write col_indices (0..cols-1 per touched row, cols % 4 == 0).  Both
+// are streamed out with nontemporal stores: tens of MB that the update does
+// not read back (it reads two offsets per touched row and no column index of
+// a full row) would otherwise displace cached lines.
+constexpr int kRoBits = 8192;
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
+template <bool VEC>
 __global__ __launch_bounds__(kRoThreads) void k_csr_full(
     const int64_t* __restrict__ keys, const int64_t* d_nnz, int64_t nnz_host, int64_t rows,
     int64_t cols, int32_t* __restrict__ row_offsets, int64_t nblk_ro,
@@ -84,12 +91,15 @@ __global__ __launch_bounds__(kRoThreads) void k_csr_full(
     const int64_t nnz = d_nnz ? (*d_nnz < nnz_host ? *d_nnz : nnz_host) : nnz_host;
     if ((int64_t)blockIdx.x >= nblk_ro) {
         if (col_indices == nullptr) return;
-        const int64_t total4 = nnz * cols / 4;  // cols % 4 == 0 on this path
-        const int64_t stride = ((int64_t)gridDim.x - nblk_ro) * kRoThreads;
-        for (int64_t q = ((int64_t)blockIdx.x - nblk_ro) * kRoThreads + threadIdx.x; q < total4;
-             q += stride) {
-            const int32_t c = (int32_t)((q * 4) % cols);
-            reinterpret_cast<int4*>(col_indices)[q] = make_int4(c, c + 1, c + 2, c + 3);
+        // nnz * cols < 2^31 (checked on the host), so 32-bit column arithmetic.
+        const uint32_t total4 = (uint32_t)(nnz * cols / 4);
+        const uint32_t ucols = (uint32_t)cols;
+        const uint32_t stride = (uint32_t)((int64_t)gridDim.x - nblk_ro) * kRoThreads;
+        for (uint32_t q = (uint32_t)((int64_t)blockIdx.x - nblk_ro) * kRoThreads + threadIdx.x;
+             q < total4; q += stride) {
+            const int32_t c = (int32_t)((q * 4u) % ucols);
+            const i32x4 cv = {c, c + 1, c + 2, c + 3};
+            __builtin_nontemporal_store(cv, reinterpret_cast<i32x4*>(col_indices) + q);
         }
         return;
     }
@@ -113,6 +123,7 @@ __global__ __launch_bounds__(kRoThreads) void k_csr_full(
     }
     __syncthreads();
     constexpr int kWordsPer = kRoBits / 32 / kRoThreads;
+    static_assert(kWordsPer >= 1, "one bitmap word per thread at least");
     uint32_t c[kWordsPer], sum = 0;
 #pragma unroll
     for (int j = 0; j < kWordsPer; ++j) {
@@ -127,10 +138,28 @@ __global__ __launch_bounds__(kRoThreads) void k_csr_full(
         run += c[j];
     }
     __syncthreads();
-    for (int64_t r = r0 + threadIdx.x; r < r1; r += kRoThreads) {
-        const int o = (int)(r - r0);
-        const uint32_t below = wpre[o >> 5] + (uint32_t)__popc(bits[o >> 5] & ((1u << (o & 31)) - 1u));
-        row_offsets[r] = (int32_t)((ka + (int64_t)below) * cols);
+    const int len = (int)(r1 - r0);
+    if (VEC) {
+        // Quads of rows: all four rows of a quad share one bitmap word.
+        for (int o = 4 * (int)threadIdx.x; o < len; o += 4 * kRoThreads) {
+            const uint32_t word = bits[o >> 5], pre = wpre[o >> 5];
+            const int sh = o & 31;
+            int32_t out[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                out[e] = (int32_t)((ka + (int64_t)(pre + (uint32_t)__popc(word & ((1u << (sh + e)) - 1u)))) * cols);
+            if (o + 4 <= len) {
+                const i32x4 q = {out[0], out[1], out[2], out[3]};
+                __builtin_nontemporal_store(q, reinterpret_cast<i32x4*>(row_offsets + r0 + o));
+            } else {
+                for (int e = 0; e < len - o; ++e) row_offsets[r0 + o + e] = out[e];
+            }
+        }
+    } else {
+        for (int o = (int)threadIdx.x; o < len; o += kRoThreads) {
+            const uint32_t below = wpre[o >> 5] + (uint32_t)__popc(bits[o >> 5] & ((1u << (o & 31)) - 1u));
+            row_offsets[r0 + o] = (int32_t)((ka + (int64_t)below) * cols);
+        }
     }
 }
 
@@ -386,8 +415,12 @@ extern "C" int csr_from_coo(const spopt_coo* in, int64_t rows, int64_t cols,
         // row_offsets and col_indices in one launch.
         const int64_t nblk_ro = ceil_div(rows + 1, kRoBits);
         const int64_t nblk_ci = col_indices ? grid_for(in->nnz * cols / 4, kRoThreads, 1024) : 0;
-        k_csr_full<<<(unsigned)(nblk_ro + nblk_ci), kRoThreads, 0, st>>>(
-            in->indices, in->d_nnz, in->nnz, rows, cols, row_offsets, nblk_ro, col_indices);
+        if (aligned16(row_offsets))
+            k_csr_full<true><<<(unsigned)(nblk_ro + nblk_ci), kRoThreads, 0, st>>>(
+                in->indices, in->d_nnz, in->nnz, rows, cols, row_offsets, nblk_ro, col_indices);
+        else
+            k_csr_full<false><<<(unsigned)(nblk_ro + nblk_ci), kRoThreads, 0, st>>>(
+                in->indices, in->d_nnz, in->nnz, rows, cols, row_offsets, nblk_ro, col_indices);
         SPOPT_LAUNCHED();
     } else {
         k_row_offsets<<<(unsigned)ceil_div(rows + 1, kRoRows), kRoThreads, 0, st>>>(

@@ -115,21 +115,26 @@ def test_workspace_too_small():
 # COO <-> CSR
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("rows,cols,n", [(1000, 64, 3000), (50000, 128, 20000), (7, 4, 30),
-                                         (9000, 3, 500)])
-def test_csr_from_full_row_coo(rows, cols, n):
+@pytest.mark.parametrize("rows,cols,n,ro_shift", [
+    (1000, 64, 3000, 0), (50000, 128, 20000, 0), (7, 4, 30, 0), (9000, 3, 500, 0),
+    # row_offsets blocks of 8192 entries: a full last block, a one-entry last
+    # block, and a row_offsets array that is not 16-byte aligned (scalar stores)
+    (8191, 8, 4000, 0), (8192, 8, 4000, 0), (50000, 128, 20000, 1), (24577, 4, 9000, 3)])
+def test_csr_from_full_row_coo(rows, cols, n, ro_shift):
     rng = np.random.default_rng(rows)
     ids = rng.integers(0, rows, size=n, dtype=np.int64)
     ids[:5] = rows - 1
     vals = rng.standard_normal((n, cols)).astype(np.float32)
     keys, sums, counts, U = L.coo_from_lookups(dev(ids), dev(vals), rows)
     coo = L.CooGradient(keys, sums, dim=rows, width=cols, nnz=n, d_nnz=U)
-    csr = L.csr_from_coo(coo, rows, cols)
+    ro_buf = torch.full((rows + 1 + ro_shift,), -7, dtype=torch.int32, device="cuda")
+    csr = L.csr_from_coo(coo, rows, cols, row_offsets=ro_buf[ro_shift:])
     torch.cuda.synchronize()
     u = int(host(U)[0])
     ok, ov, oc = oracle.coo_from_lookups(ids, vals, rows)
     ro, ci, cv = oracle.csr_from_coo(ok, ov, rows, cols, rows, cols)
     assert np.array_equal(host(csr.row_offsets), ro)
+    assert (host(ro_buf)[:ro_shift] == -7).all()
     assert np.array_equal(host(csr.col_indices)[:u * cols], ci)
     assert np.array_equal(host(csr.touched_rows)[:u], ok)
     assert np.array_equal(host(csr.values)[:u * cols], host(sums)[:u].reshape(-1))
