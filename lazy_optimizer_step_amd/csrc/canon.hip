@@ -13,9 +13,9 @@
 //      in one look-back pass, giving every lookup its segment number and
 //      emitting the distinct ids;
 //   3. sum each segment's value rows in double, in a fixed order, and round
-//      once: fixed chunks of 64 sorted lookups per wave, partial sums for
-//      segments that cross a chunk boundary, then an ordered combine of those
-//      partials.  No atomics, so the result is the same run to run.
+//      once: chunks of 16 sorted lookups per wave, partial sums for segments
+//      that cross a chunk boundary, then an ordered combine of those partials.
+//      No atomics in any sum, so the result is the same run to run.
 #include <stdarg.h>
 #include <stdio.h>
 
@@ -30,7 +30,7 @@ constexpr int kTile = kThreads * kIpt;          // 1024 lookups per sort / segme
 constexpr int kRadixBits = 8;                   // at most 256 buckets per radix pass
 constexpr int kRadix = 1 << kRadixBits;
 constexpr int kMaxPasses = 8;
-constexpr int kChunk = 64;                      // sorted lookups per wave, summing
+constexpr int kRowChunk = 16;                   // sorted lookups per wave, summing
 constexpr int kFixThreads = 1024;               // block of the ordered combine
 constexpr int kFixWaves = kFixThreads / kWave;
 
@@ -52,7 +52,8 @@ struct CanonLayout {
     int key_bits, pos_bits, passes, digit_bits;
     int64_t ntiles, nchunks;
     size_t off_a, off_b, off_clear, clear_bytes, off_status, off_tickets, off_hist,
-        off_segwords, off_words, off_segid, off_segstart, off_pfirst, off_plast, total;
+        off_segwords, off_words, off_segid, off_segstart, off_cross, off_big, off_pfirst,
+        off_plast, total;
 };
 
 static int bits_for(uint64_t x) {  // bits needed to represent values in [0, x)
@@ -73,7 +74,7 @@ static bool canon_layout(int64_t n, int64_t width, int64_t key_space, CanonLayou
     L->passes = (L->key_bits + kRadixBits - 1) / kRadixBits;
     L->digit_bits = L->passes ? (L->key_bits + L->passes - 1) / L->passes : 0;
     L->ntiles = ceil_div(n, kTile);
-    L->nchunks = ceil_div(n, kChunk);
+    L->nchunks = ceil_div(n, kRowChunk);
     const size_t P = (size_t)(L->passes ? L->passes : 1);
     size_t o = 0;
     auto take = [&](size_t bytes) {
@@ -86,13 +87,17 @@ static bool canon_layout(int64_t n, int64_t width, int64_t key_space, CanonLayou
     // Everything a call must find zeroed sits in one contiguous region.
     L->off_clear = o;
     L->off_status = take(sizeof(uint32_t) * 4);
-    L->off_tickets = take(sizeof(uint32_t) * (kMaxPasses + 1));
+    // tickets: one per radix pass, the segment kernel's, and the count of
+    // segments listed for a whole combining block.
+    L->off_tickets = take(sizeof(uint32_t) * (kMaxPasses + 2));
     L->off_hist = take(sizeof(uint32_t) * (size_t)kRadix * P);
     L->off_words = take(sizeof(uint32_t) * (size_t)kRadix * (size_t)L->ntiles * P);
     L->off_segwords = take(sizeof(uint32_t) * (size_t)L->ntiles);
     L->clear_bytes = o - L->off_clear;
     L->off_segid = take(sizeof(int32_t) * (size_t)n);
     L->off_segstart = take(sizeof(int32_t) * ((size_t)n + 1));
+    L->off_cross = take(sizeof(int32_t) * 2 * (size_t)L->nchunks);
+    L->off_big = take(sizeof(int32_t) * (size_t)L->nchunks);
     L->off_pfirst = take(sizeof(double) * (size_t)L->nchunks * (size_t)width);
     L->off_plast = take(sizeof(double) * (size_t)L->nchunks * (size_t)width);
     L->total = o;
@@ -297,20 +302,84 @@ __global__ __launch_bounds__(kThreads) void k_onesweep(
 
 // ------------------------------------------------------------- segments ---
 
-__device__ __forceinline__ bool seg_head(const uint64_t* s, int64_t i, int pos_bits) {
-    return i == 0 || (s[i] >> pos_bits) != (s[i - 1] >> pos_bits);
+// Run by one whole wave of tile `tile`: publishes `count` for the tile and
+// returns in *excl the sum of the counts of all earlier tiles.  Each round
+// trip reads the words of the 512 tiles below lo (lane l, load k: tile
+// lo-1-l-64k) and sums them back to the nearest inclusive prefix or the
+// nearest tile that has not published yet, then waits for that one.  Deep
+// rounds matter because every tile starts at once: inclusive prefixes spread
+// back-to-front only as fast as tiles finish their own look-back.  False on
+// timeout.
+__device__ __forceinline__ bool tile_exclusive_prefix(uint32_t* words, int64_t tile,
+                                                      uint32_t count, uint32_t* excl_out) {
+    constexpr int kDeep = 8;
+    const int lane = lane_id();
+    uint32_t excl = 0;
+    bool ok = true;
+    if (tile == 0) {
+        if (lane == 0) st_dev(words, kLbInc | count);
+    } else {
+        if (lane == 0) st_dev(words + tile, kLbAgg | count);
+        int64_t lo = tile;  // tiles [lo, tile) summed
+        uint32_t spins = 0;
+        while (lo > 0) {
+            uint32_t v[kDeep];
+#pragma unroll
+            for (int k = 0; k < kDeep; ++k) {
+                const int64_t tj = lo - 1 - lane - (int64_t)k * kWave;
+                v[k] = tj >= 0 ? ld_dev(words + tj) : kLbInc;  // below tile 0: a zero prefix
+            }
+            bool done = false;
+            int64_t advanced = 0;
+#pragma unroll
+            for (int k = 0; k < kDeep; ++k) {
+                if (!done) {
+                    const int64_t base = lo - 1 - (int64_t)k * kWave;  // tile read by lane 0
+                    const bool valid = base - lane >= 0;
+                    const uint32_t x = valid ? v[k] : kLbInc;
+                    const uint64_t not_ready = ballot(valid && (x & kLbState) == 0u);
+                    const uint64_t inclusive = ballot(!valid || (x & kLbState) == kLbInc);
+                    const int first_nr = not_ready ? __builtin_ctzll(not_ready) : kWave;
+                    const int first_inc = inclusive ? __builtin_ctzll(inclusive) : kWave;
+                    const int take = first_inc < first_nr ? first_inc + 1 : first_nr;
+                    uint32_t part = (lane < take && valid) ? (x & kLbCount) : 0u;
+#pragma unroll
+                    for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off, kWave);
+                    excl += part;
+                    advanced += take;
+                    if (first_inc < first_nr) {
+                        lo = 0;  // reached an inclusive prefix (or tile 0's base)
+                        done = true;
+                    } else if (take < kWave) {
+                        done = true;  // stopped at a tile that has not published
+                    }
+                }
+            }
+            if (lo == 0) break;
+            lo -= advanced;
+            if (advanced == 0) {
+                if (++spins > kSpinLimit) {
+                    ok = false;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+        }
+        if (lane == 0 && ok) st_dev(words + tile, kLbInc | (excl + count));
+    }
+    *excl_out = excl;
+    return ok;
 }
 
-// Segment heads (id differs from its predecessor) of each tile, counted with
-// ballots and prefixed across tiles by the same look-back in one pass: every
-// sorted lookup gets its segment number, every head writes its id and
-// position.  The last tile publishes U (0 when an id was out of range or a
-// wait timed out) and the sentinel seg_start[U] = n.
+// Segment heads (id differs from its predecessor) of each tile of 1024
+// sorted lookups, counted with ballots and prefixed across tiles by the
+// look-back in one pass: every sorted lookup gets its segment number, every
+// head writes its id and position.  The last tile publishes U (0 when an id
+// was out of range or a wait timed out) and the sentinel seg_start[U] = n.
 __global__ __launch_bounds__(kThreads) void k_segment(
     const uint64_t* __restrict__ s, int64_t n, int pos_bits, int64_t ntiles, uint32_t* words,
-    uint32_t* ticket, int32_t* __restrict__ seg_id,
-    int32_t* __restrict__ seg_start, int64_t* __restrict__ out_keys,
-    int64_t* __restrict__ d_nunique, uint32_t* status) {
+    uint32_t* ticket, int32_t* __restrict__ seg_id, int32_t* __restrict__ seg_start,
+    int64_t* __restrict__ out_keys, int64_t* __restrict__ d_nunique, uint32_t* status) {
     if (*status != 0u) {
         if (blockIdx.x == 0 && threadIdx.x == 0) *d_nunique = 0;
         return;
@@ -332,7 +401,10 @@ __global__ __launch_bounds__(kThreads) void k_segment(
 #pragma unroll
     for (int r = 0; r < kIpt; ++r) {
         const int64_t i = first + (int64_t)r * kWave + lane;
-        hm[r] = ballot(i < n && seg_head(s, i, pos_bits));
+        const bool in = i < n;
+        const int64_t ic = in ? i : 0;
+        const uint64_t cur = s[ic], prev = s[ic > 0 ? ic - 1 : 0];
+        hm[r] = ballot(in && (i == 0 || (cur >> pos_bits) != (prev >> pos_bits)));
         wave_heads += (uint32_t)popc64(hm[r]);
     }
     if (lane == 0) wcount[w] = wave_heads;
@@ -343,43 +415,8 @@ __global__ __launch_bounds__(kThreads) void k_segment(
         tile_heads += wcount[ww];
     }
     if (w == 0) {
-        // Lane l reads the word of tile lo-1-l: one round trip covers 64 earlier
-        // tiles; counts are summed back to the nearest inclusive prefix.
         uint32_t excl = 0;
-        bool ok = true;
-        if (tile == 0) {
-            if (lane == 0) st_dev(words, kLbInc | tile_heads);
-        } else {
-            if (lane == 0) st_dev(words + tile, kLbAgg | tile_heads);
-            int64_t lo = tile;
-            uint32_t spins = 0;
-            while (lo > 0) {
-                const int64_t tj = lo - 1 - lane;
-                const bool valid = tj >= 0;
-                const uint32_t v = valid ? ld_dev(words + tj) : 0u;
-                const uint64_t not_ready = ballot(valid && (v & kLbState) == 0u);
-                const uint64_t inclusive = ballot(valid && (v & kLbState) == kLbInc);
-                const int first_nr = not_ready ? __builtin_ctzll(not_ready) : kWave;
-                const int first_inc = inclusive ? __builtin_ctzll(inclusive) : kWave;
-                const int nvalid = lo < kWave ? (int)lo : kWave;
-                const int take = first_inc < first_nr ? first_inc + 1
-                                                      : (first_nr < nvalid ? first_nr : nvalid);
-                uint32_t part = lane < take ? (v & kLbCount) : 0u;
-#pragma unroll
-                for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off, kWave);
-                excl += part;
-                if (first_inc < first_nr) break;
-                lo -= take;
-                if (take == 0) {
-                    if (++spins > kSpinLimit) {
-                        ok = false;
-                        break;
-                    }
-                    __builtin_amdgcn_s_sleep(1);
-                }
-            }
-            if (lane == 0 && ok) st_dev(words + tile, kLbInc | (excl + tile_heads));
-        }
+        const bool ok = tile_exclusive_prefix(words, tile, tile_heads, &excl);
         if (lane == 0) {
             s_excl = excl;
             s_ok = ok ? 1u : 0u;
@@ -399,11 +436,11 @@ __global__ __launch_bounds__(kThreads) void k_segment(
         const int64_t i = first + (int64_t)r * kWave + lane;
         const bool h = (hm[r] >> lane) & 1ull;
         if (i < n) {
-            const uint32_t seg = run + (uint32_t)popc64(hm[r] & lt) + (h ? 1u : 0u) - 1u;
-            seg_id[i] = (int32_t)seg;
+            const uint32_t sg = run + (uint32_t)popc64(hm[r] & lt) + (h ? 1u : 0u) - 1u;
+            seg_id[i] = (int32_t)sg;
             if (h) {
-                out_keys[seg] = (int64_t)(s[i] >> pos_bits);
-                seg_start[seg] = (int32_t)i;
+                out_keys[sg] = (int64_t)(s[i] >> pos_bits);
+                seg_start[sg] = (int32_t)i;
             }
         }
         run += (uint32_t)popc64(hm[r]);
@@ -459,7 +496,11 @@ template <int V>
 __device__ __forceinline__ void load_part(double (&r)[V], const double* src, int64_t col,
                                           int64_t width) {
 #pragma unroll
-    for (int v = 0; v < V; ++v) r[v] = (col + v < width) ? src[v] : 0.0;
+    for (int v = 0; v < V; ++v) {
+        const bool in = col + v < width;
+        const double x = src[in ? v : -col];  // past the row: its first column
+        r[v] = in ? x : 0.0;
+    }
 }
 
 template <int V>
@@ -470,178 +511,206 @@ __device__ __forceinline__ void store_part(double* dst, const double (&r)[V], in
         if (col + v < width) dst[v] = r[v];
 }
 
-// Destination of the running sum when item j of a chunk closes it.
+// Destination of the running sum when lookup j of a chunk closes it.
 enum : int { kFlushNone = 0, kFlushOut = 1, kFlushFirst = 2, kFlushLast = 3 };
 
-struct ChunkItem {
-    uint32_t pos;   // lookup position
-    int32_t seg;    // segment number
-    int kind;       // kFlush*
-    bool ends;      // this lookup is the last of its segment
-};
+// Waits until every vector memory operation this wave issued has completed
+// (vmcnt 0; the export and LDS/scalar counters are left at their maximum).
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-__device__ __forceinline__ ChunkItem chunk_item(const uint64_t* s, const int32_t* seg_id,
-                                                const int32_t* seg_start, int64_t n,
-                                                int pos_bits, int64_t i0, int cnt, int lane) {
-    ChunkItem it{0u, -1, kFlushNone, false};
-    if (lane < cnt) {
-        const int64_t i = i0 + lane;
-        it.pos = (uint32_t)(s[i] & ((pos_bits == 64) ? ~0ull : ((1ull << pos_bits) - 1ull)));
-        it.seg = seg_id[i];
-        it.ends = (i + 1 >= n) || seg_id[i + 1] != it.seg;
-        if (it.ends || lane == cnt - 1) {
-            const bool starts_here = seg_start[it.seg] >= i0;
-            if (it.ends && starts_here)
-                it.kind = kFlushOut;
-            else if (!starts_here)
-                it.kind = kFlushFirst;
-            else
-                it.kind = kFlushLast;
-        }
-    }
-    return it;
-}
+constexpr int kWavePartials = 32;  // partials one wave adds alone; more go to a whole block
 
-// One wave per chunk of 64 sorted lookups, value rows of `width` floats; each
-// lane owns V consecutive columns of every 64*V-column block.  All rows of the
-// chunk are loaded before the first add (D rows in flight per lane), then
-// accumulated in double in sorted (= lookup) order.
-template <int V>
+// One wave per chunk of 16 sorted lookups (lane j: lookup i0 + j), value rows
+// of `width` floats.  LPR lanes cover LPR*V consecutive columns of one row, so
+// one load instruction fetches RPI = 64/LPR rows (16-byte loads when V = 4).
+// For each block of columns every row of the chunk is loaded first and the
+// wave then waits once for all of them: stores share the vector memory
+// counter with loads, so a store between them would make later rows wait for
+// it too.  The rows are then added in sorted (= lookup) order: row j goes to
+// the accumulator of lane group j % RPI, and a segment that ends at row j is
+// closed by adding the group accumulators pairwise across lanes (one fixed
+// order, identical on every lane) unless row j is its only row in the chunk.
+// A segment that starts and ends in the chunk is written with its count; one
+// that started earlier leaves its partial in pfirst[chunk], one that goes on
+// in plast[chunk].  Every chunk records in cross[2*chunk..] the segment that
+// starts in it and goes on (-1 if none) and that segment's number of
+// partials m; it also writes that segment's count.  Segments with more than
+// kWavePartials partials are listed for a whole combining block.
+template <int V, int LPR>
 __global__ __launch_bounds__(256) void k_dupsum_rows(
     const uint64_t* __restrict__ s, const int32_t* __restrict__ seg_id,
     const int32_t* __restrict__ seg_start, int64_t n, int pos_bits,
     const float* __restrict__ vals, int64_t width, float* __restrict__ out_vals,
     int32_t* __restrict__ out_counts, double* __restrict__ pfirst, double* __restrict__ plast,
+    int32_t* __restrict__ cross, int32_t* __restrict__ big, uint32_t* big_count,
     const uint32_t* status) {
-    constexpr int D = (kChunk * V <= 128) ? kChunk : 128 / V;
+    constexpr int RPI = kWave / LPR;
+    constexpr int U = kRowChunk / RPI;  // load instructions per block of columns
+    static_assert(RPI >= 1 && kRowChunk % RPI == 0, "lane groups must tile the chunk");
     if (*status != 0u) return;
     const int lane = lane_id();
+    const int sub = lane / LPR, sl = lane % LPR;
     const int64_t chunk = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
-    const int64_t i0 = chunk * kChunk;
+    const int64_t i0 = chunk * kRowChunk;
     if (i0 >= n) return;
-    const int cnt = (int)((n - i0) < kChunk ? (n - i0) : kChunk);
-    const ChunkItem it = chunk_item(s, seg_id, seg_start, n, pos_bits, i0, cnt, lane);
-    if (it.ends) out_counts[it.seg] = (int32_t)(i0 + lane + 1 - seg_start[it.seg]);
+    const int cnt = (int)((n - i0) < kRowChunk ? (n - i0) : kRowChunk);
 
-    for (int64_t c0 = 0; c0 < width; c0 += (int64_t)kWave * V) {
-        const int64_t col = c0 + (int64_t)lane * V;
+    // Lane j < cnt describes lookup i0 + j; the others read valid indices.
+    // Independent loads only: the segment of lookup i0 - 1 tells whether a
+    // segment started before the chunk.
+    const bool in = lane < cnt;
+    const int64_t i = i0 + (in ? lane : 0);
+    const uint32_t pos = (uint32_t)(s[i] & ((1ull << pos_bits) - 1ull));
+    const int32_t seg = seg_id[i];
+    const int32_t seg_next = seg_id[i + 1 < n ? i + 1 : i];
+    const int32_t seg_before = seg_id[i0 > 0 ? i0 - 1 : 0];
+    const bool ends = in && (i + 1 >= n || seg_next != seg);
+    const bool starts_here = i0 == 0 || seg != seg_before;
+    const int32_t seg_up = __shfl_up(seg, 1, kWave);
+    const uint64_t hm = ballot(in && (lane == 0 ? starts_here : seg_up != seg));
+    int kind = kFlushNone;
+    if (in && (ends || lane == cnt - 1))
+        kind = (ends && starts_here) ? kFlushOut : (!starts_here ? kFlushFirst : kFlushLast);
+
+    float row[U][V];
+    auto load_rows = [&](int64_t col) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            // Past the chunk's last lookup, reload that lookup's row (unused).
+            const int j = u * RPI + sub;
+            const uint32_t p = (uint32_t)__shfl((int)pos, j < cnt ? j : cnt - 1, kWave);
+            load_row<V>(row[u], vals + (int64_t)p * width, col, width);
+        }
+    };
+    load_rows((int64_t)sl * V);
+    // End of the segment that goes on past the chunk (read by every lane, used
+    // by the last one; seg + 1 <= U, inside seg_start).
+    const int32_t seg_end = seg_start[seg + 1];
+
+    for (int64_t c0 = 0; c0 < width; c0 += (int64_t)LPR * V) {
+        const int64_t col = c0 + (int64_t)sl * V;
+        if (c0 > 0) load_rows(col);
+        wait_vmem_all();
         double acc[V];
 #pragma unroll
         for (int v = 0; v < V; ++v) acc[v] = 0.0;
-        for (int j0 = 0; j0 < cnt; j0 += D) {
-            float row[D][V];
 #pragma unroll
-            for (int u = 0; u < D; ++u) {
-                // Past the chunk's last lookup, reload that lookup's row (unused).
-                const int j = (j0 + u < cnt) ? j0 + u : cnt - 1;
-                const uint32_t pos = read_lane(it.pos, j);
-                load_row<V>(row[u], vals + (int64_t)pos * width, col, width);
+        for (int j = 0; j < kRowChunk; ++j) {
+            const int k = j < cnt ? read_lane(kind, j) : kFlushNone;
+            if (j < cnt && sub == j % RPI) {
+#pragma unroll
+                for (int v = 0; v < V; ++v) acc[v] += (double)row[j / RPI][v];
             }
+            if (k != kFlushNone) {
+                const bool single = (hm >> j) & 1ull;  // row j is the segment's only row here
+                int owner = j % RPI;
+                if (!single) {
+                    owner = 0;
 #pragma unroll
-            for (int u = 0; u < D; ++u) {
-                const int j = j0 + u;
-                if (j < cnt) {
+                    for (int o = LPR; o < kWave; o <<= 1)
 #pragma unroll
-                    for (int v = 0; v < V; ++v) acc[v] += (double)row[u][v];
-                    const int kind = read_lane(it.kind, j);
-                    if (kind != kFlushNone) {
-                        if (kind == kFlushOut)
-                            store_row<V>(out_vals + (int64_t)read_lane(it.seg, j) * width + col,
-                                         acc, col, width);
-                        else if (kind == kFlushFirst)
-                            store_part<V>(pfirst + chunk * width + col, acc, col, width);
-                        else
-                            store_part<V>(plast + chunk * width + col, acc, col, width);
-#pragma unroll
-                        for (int v = 0; v < V; ++v) acc[v] = 0.0;
-                    }
+                        for (int v = 0; v < V; ++v) acc[v] += __shfl_xor(acc[v], o, kWave);
                 }
+                if (sub == owner) {
+                    if (k == kFlushOut)
+                        store_row<V>(out_vals + (int64_t)read_lane(seg, j) * width + col, acc,
+                                     col, width);
+                    else if (k == kFlushFirst)
+                        store_part<V>(pfirst + chunk * width + col, acc, col, width);
+                    else
+                        store_part<V>(plast + chunk * width + col, acc, col, width);
+                }
+#pragma unroll
+                for (int v = 0; v < V; ++v) acc[v] = 0.0;
             }
         }
     }
-}
 
-// Width 1: one lookup per lane, segmented inclusive scan (double) across the wave.
-__global__ __launch_bounds__(256) void k_dupsum_scalar(
-    const uint64_t* __restrict__ s, const int32_t* __restrict__ seg_id,
-    const int32_t* __restrict__ seg_start, int64_t n, int pos_bits,
-    const float* __restrict__ vals, float* __restrict__ out_vals,
-    int32_t* __restrict__ out_counts, double* __restrict__ pfirst, double* __restrict__ plast,
-    const uint32_t* status) {
-    if (*status != 0u) return;
-    const int lane = lane_id();
-    const int64_t chunk = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
-    const int64_t i0 = chunk * kChunk;
-    if (i0 >= n) return;
-    const int cnt = (int)((n - i0) < kChunk ? (n - i0) : kChunk);
-    const ChunkItem it = chunk_item(s, seg_id, seg_start, n, pos_bits, i0, cnt, lane);
-    if (it.ends) out_counts[it.seg] = (int32_t)(i0 + lane + 1 - seg_start[it.seg]);
-    double x = lane < cnt ? (double)vals[it.pos] : 0.0;
-    const int prev_seg = __shfl_up(it.seg, 1, kWave);
-    bool f = lane == 0 || prev_seg != it.seg;  // first lookup of its segment in this chunk
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const double y = __shfl_up(x, off, kWave);
-        const bool g = __shfl_up((int)f, off, kWave) != 0;
-        if (lane >= off && !f) {
-            x = y + x;
-            f = g;
+    const uint64_t upto = lane == 63 ? ~0ull : ((2ull << lane) - 1ull);
+    const int64_t head = i0 + (63 - __builtin_clzll((hm & upto) | 1ull));  // if starts_here
+    if (kind == kFlushOut) out_counts[seg] = (int32_t)(i - head + 1);
+    if (lane == cnt - 1) {
+        int32_t m = 0;
+        if (kind == kFlushLast) {
+            out_counts[seg] = (int32_t)(seg_end - head);
+            m = (int32_t)((seg_end - 1) / kRowChunk - chunk + 1);
+            if (m > kWavePartials) big[atomicAdd(big_count, 1u)] = (int32_t)chunk;
         }
+        cross[2 * chunk] = kind == kFlushLast ? seg : -1;
+        cross[2 * chunk + 1] = m;
     }
-    if (it.kind == kFlushOut)
-        out_vals[it.seg] = (float)x;
-    else if (it.kind == kFlushFirst)
-        pfirst[chunk] = x;
-    else if (it.kind == kFlushLast)
-        plast[chunk] = x;
 }
 
-// Segments that cross chunk boundaries.  The block of the chunk where such a
-// segment starts combines its partials (plast of that chunk, then pfirst of
-// each following chunk up to the one where it ends): its 16 waves each add a
-// contiguous run of partials, 8 loads in flight, then wave 0 adds the 16 wave
-// sums in wave order and rounds once.  A fixed order, so deterministic.
-// Blocks stride over the chunks.
+
+// Adds partials q in [lo, hi) of a segment whose start chunk is `chunk`
+// (q = 0: plast[chunk], q > 0: pfirst[chunk + q]) in increasing q, 8 loads in
+// flight (past hi, partial lo is reloaded and unused).
+template <int V>
+__device__ __forceinline__ void add_partials(double (&acc)[V], const double* pfirst,
+                                             const double* plast, int64_t chunk, int64_t lo,
+                                             int64_t hi, int64_t width, int64_t col) {
+    for (int64_t q0 = lo; q0 < hi; q0 += 8) {
+        double row[8][V];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int64_t q = q0 + u < hi ? q0 + u : lo;
+            const double* src = (q == 0) ? plast + chunk * width : pfirst + (chunk + q) * width;
+            load_part<V>(row[u], src + col, col, width);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (q0 + u < hi) {
+#pragma unroll
+                for (int v = 0; v < V; ++v) acc[v] += row[u][v];
+            }
+    }
+}
+
+// Segments that cross chunk boundaries.  The chunk where such a segment
+// starts holds its partial in plast, each following chunk up to the one where
+// it ends in pfirst: m partials, recorded with the segment in cross[] by the
+// chunk where it starts.  The order of the additions depends on m only, so
+// the result is the same run to run: up to kWavePartials partials are added
+// in chunk order by one wave (one chunk's record per wave); beyond, by a
+// whole block from the list of such chunks (blocks stride over the list):
+// [0, m) is cut into 16 equal runs, wave r adds run r in chunk order with 8
+// loads in flight, and wave 0 adds the 16 run sums in run order.
 template <int V>
 __global__ __launch_bounds__(kFixThreads) void k_dupsum_fixup(
-    const int32_t* __restrict__ seg_id, const int32_t* __restrict__ seg_start, int64_t n,
-    int64_t nchunks, const double* __restrict__ pfirst, const double* __restrict__ plast,
-    int64_t width, float* __restrict__ out_vals, const uint32_t* status) {
+    const int32_t* __restrict__ cross, const int32_t* __restrict__ big,
+    const uint32_t* big_count, int64_t nchunks, const double* __restrict__ pfirst,
+    const double* __restrict__ plast, int64_t width, float* __restrict__ out_vals,
+    const uint32_t* status) {
     __shared__ double part[kFixWaves][kWave * V];
     if (*status != 0u) return;
     const int w = (int)(threadIdx.x >> 6);
     const int lane = lane_id();
-    for (int64_t chunk = blockIdx.x; chunk < nchunks; chunk += gridDim.x) {
-        const int64_t i0 = chunk * kChunk;
-        const int64_t last = (i0 + kChunk < n ? i0 + kChunk : n) - 1;
-        const int32_t seg = seg_id[last];
-        const int64_t s0 = seg_start[seg], s1 = seg_start[seg + 1];
-        if (!(s0 >= i0 && s1 > i0 + kChunk)) continue;  // uniform over the block
-        const int64_t m = (s1 - 1) / kChunk - chunk + 1;  // partials: plast[chunk], pfirst[...]
+    for (int64_t chunk = (int64_t)blockIdx.x * kFixWaves + w; chunk < nchunks;
+         chunk += (int64_t)gridDim.x * kFixWaves) {
+        const int32_t seg = cross[2 * chunk];
+        const int64_t m = cross[2 * chunk + 1];
+        if (seg < 0 || m > kWavePartials) continue;
+        for (int64_t c0 = 0; c0 < width; c0 += (int64_t)kWave * V) {
+            const int64_t col = c0 + (int64_t)lane * V;
+            double tot[V];
+#pragma unroll
+            for (int v = 0; v < V; ++v) tot[v] = 0.0;
+            add_partials<V>(tot, pfirst, plast, chunk, 0, m, width, col);
+            store_row<V>(out_vals + (int64_t)seg * width + col, tot, col, width);
+        }
+    }
+    const uint32_t nbig = *big_count;
+    for (uint32_t b = blockIdx.x; b < nbig; b += gridDim.x) {
+        const int64_t chunk = big[b];
+        const int32_t seg = cross[2 * chunk];
+        const int64_t m = cross[2 * chunk + 1];
         const int64_t lo = m * w / kFixWaves, hi = m * (w + 1) / kFixWaves;
         for (int64_t c0 = 0; c0 < width; c0 += (int64_t)kWave * V) {
             const int64_t col = c0 + (int64_t)lane * V;
             double acc[V];
 #pragma unroll
             for (int v = 0; v < V; ++v) acc[v] = 0.0;
-            for (int64_t q0 = lo; q0 < hi; q0 += 8) {
-                double row[8][V];
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int64_t q = q0 + u;
-                    if (q < hi) {
-                        const double* src = (q == 0) ? plast + chunk * width
-                                                     : pfirst + (chunk + q) * width;
-                        load_part<V>(row[u], src + col, col, width);
-                    }
-                }
-#pragma unroll
-                for (int u = 0; u < 8; ++u)
-                    if (q0 + u < hi) {
-#pragma unroll
-                        for (int v = 0; v < V; ++v) acc[v] += row[u][v];
-                    }
-            }
+            add_partials<V>(acc, pfirst, plast, chunk, lo, hi, width, col);
 #pragma unroll
             for (int v = 0; v < V; ++v) part[w][lane * V + v] = acc[v];
             __syncthreads();
@@ -725,6 +794,8 @@ extern "C" int coo_from_lookups(const int64_t* ids, const float* vals, int64_t n
     uint32_t* segwords = (uint32_t*)(ws + L.off_segwords);
     int32_t* seg_id = (int32_t*)(ws + L.off_segid);
     int32_t* seg_start = (int32_t*)(ws + L.off_segstart);
+    int32_t* cross = (int32_t*)(ws + L.off_cross);
+    int32_t* big = (int32_t*)(ws + L.off_big);
     double* pfirst = (double*)(ws + L.off_pfirst);
     double* plast = (double*)(ws + L.off_plast);
 
@@ -770,45 +841,45 @@ extern "C" int coo_from_lookups(const int64_t* ids, const float* vals, int64_t n
                                                        out_keys, d_nunique, status);
     SPOPT_LAUNCHED();
 
-    // Duplicate sums: 4 chunks (waves) per block, then the ordered combine of
-    // segments that cross chunks.  V floats per lane: 16- or 8-byte accesses
-    // when the width and the value arrays allow them.
-    const unsigned grid = (unsigned)ceil_div(L.nchunks, 4);
-    const unsigned fgrid = (unsigned)(L.nchunks < 1024 ? L.nchunks : 1024);
+    // Duplicate sums: chunks of 16 sorted lookups, 4 per block, then the
+    // ordered combine of segments that cross chunks.  V floats per lane (16-
+    // or 8-byte accesses when the width and the value arrays allow them), over
+    // the smallest lane group that covers the row, up to the whole wave.
     const uintptr_t al = (uintptr_t)vals | (uintptr_t)out_vals;
-    int V = 1;
-    if (width % 4 == 0 && width >= 256 && (al & 15u) == 0)
-        V = 4;
-    else if (width % 2 == 0 && width >= 128 && (al & 7u) == 0)
-        V = 2;
-    if (width == 1) {
-        k_dupsum_scalar<<<grid, 256, 0, st>>>(sorted, seg_id, seg_start, n, L.pos_bits, vals,
-                                              out_vals, out_counts, pfirst, plast, status);
-        SPOPT_LAUNCHED();
-        k_dupsum_fixup<1><<<fgrid, kFixThreads, 0, st>>>(seg_id, seg_start, n, L.nchunks, pfirst,
-                                                         plast, 1, out_vals, status);
-        SPOPT_LAUNCHED();
-    } else if (V == 4) {
-        k_dupsum_rows<4><<<grid, 256, 0, st>>>(sorted, seg_id, seg_start, n, L.pos_bits, vals,
-                                               width, out_vals, out_counts, pfirst, plast, status);
-        SPOPT_LAUNCHED();
-        k_dupsum_fixup<4><<<fgrid, kFixThreads, 0, st>>>(seg_id, seg_start, n, L.nchunks, pfirst,
-                                                         plast, width, out_vals, status);
-        SPOPT_LAUNCHED();
-    } else if (V == 2) {
-        k_dupsum_rows<2><<<grid, 256, 0, st>>>(sorted, seg_id, seg_start, n, L.pos_bits, vals,
-                                               width, out_vals, out_counts, pfirst, plast, status);
-        SPOPT_LAUNCHED();
-        k_dupsum_fixup<2><<<fgrid, kFixThreads, 0, st>>>(seg_id, seg_start, n, L.nchunks, pfirst,
-                                                         plast, width, out_vals, status);
-        SPOPT_LAUNCHED();
-    } else {
-        k_dupsum_rows<1><<<grid, 256, 0, st>>>(sorted, seg_id, seg_start, n, L.pos_bits, vals,
-                                               width, out_vals, out_counts, pfirst, plast, status);
-        SPOPT_LAUNCHED();
-        k_dupsum_fixup<1><<<fgrid, kFixThreads, 0, st>>>(seg_id, seg_start, n, L.nchunks, pfirst,
-                                                         plast, width, out_vals, status);
-        SPOPT_LAUNCHED();
-    }
+    const int V = (width % 4 == 0 && (al & 15u) == 0) ? 4 : (width % 2 == 0 && (al & 7u) == 0) ? 2 : 1;
+    const int lpr = width <= 16 * V ? 16 : (width <= 32 * V ? 32 : 64);
+    uint32_t* big_count = tickets + kMaxPasses + 1;
+    auto rows = [&](auto kernel) {
+        kernel<<<(unsigned)ceil_div(L.nchunks, 4), 256, 0, st>>>(
+            sorted, seg_id, seg_start, n, L.pos_bits, vals, width, out_vals, out_counts, pfirst,
+            plast, cross, big, big_count, status);
+    };
+    if (V == 4)
+        lpr == 16 ? rows(k_dupsum_rows<4, 16>) : lpr == 32 ? rows(k_dupsum_rows<4, 32>)
+                                                          : rows(k_dupsum_rows<4, 64>);
+    else if (V == 2)
+        lpr == 16 ? rows(k_dupsum_rows<2, 16>) : lpr == 32 ? rows(k_dupsum_rows<2, 32>)
+                                                          : rows(k_dupsum_rows<2, 64>);
+    else
+        lpr == 16 ? rows(k_dupsum_rows<1, 16>) : lpr == 32 ? rows(k_dupsum_rows<1, 32>)
+                                                          : rows(k_dupsum_rows<1, 64>);
+    SPOPT_LAUNCHED();
+
+    // The combine: V doubles per lane over blocks of 64*V columns.
+    const int FV = (width % 4 == 0 && width >= 256 && (al & 15u) == 0) ? 4
+                   : (width % 2 == 0 && width >= 128 && (al & 7u) == 0) ? 2 : 1;
+    const int64_t fblocks = ceil_div(L.nchunks, kFixWaves);
+    const unsigned fgrid = (unsigned)(fblocks < 1024 ? fblocks : 1024);
+    auto fix = [&](auto kernel) {
+        kernel<<<fgrid, kFixThreads, 0, st>>>(cross, big, big_count, L.nchunks, pfirst, plast,
+                                              width, out_vals, status);
+    };
+    if (FV == 4)
+        fix(k_dupsum_fixup<4>);
+    else if (FV == 2)
+        fix(k_dupsum_fixup<2>);
+    else
+        fix(k_dupsum_fixup<1>);
+    SPOPT_LAUNCHED();
     return SPOPT_OK;
 }

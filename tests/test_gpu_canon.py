@@ -41,6 +41,13 @@ CASES = [
     ("four_passes", 2048, 1 << 30, 2, 0.0),
     ("33bit_keys", 1500, 6_400_000_000, 1, 0.3),
     ("all_distinct", 4096, 4096, 8, 0.0),
+    # every row-sum layout: 4-, 2- and 1-float lanes over 16-, 32- and 64-lane
+    # groups, and rows wider than one group's columns
+    ("width17", 3000, 5000, 17, 0.3),
+    ("width50", 3000, 5000, 50, 0.3),
+    ("width67", 2500, 3000, 67, 0.3),
+    ("width130", 2500, 3000, 130, 0.3),
+    ("width384", 1500, 100000, 384, 0.5),
 ]
 
 
@@ -56,6 +63,41 @@ def test_coo_from_lookups_matches_oracle(name, n, key_space, width, hot):
     assert u == ok.size
     assert np.array_equal(gk, ok) and np.array_equal(gc, oc)
     assert_sums_close(gv, ov, ids, ok, oc, vals)
+
+
+@pytest.mark.parametrize("run", [1, 7, 15, 16, 17, 33])
+def test_runs_on_chunk_edges(run):
+    """Runs of equal ids of fixed length, so segment ends fall on every offset of
+    the 16-row summing chunks (and exactly on their edges for 16)."""
+    rng = np.random.default_rng(run)
+    n_ids, width = 700, 128
+    ids = np.repeat(rng.permutation(100000)[:n_ids].astype(np.int64), run)
+    ids = ids[rng.permutation(ids.size)]
+    vals = rng.standard_normal((ids.size, width)).astype(np.float32)
+    gk, gv, gc, u = _run(ids, vals, 100000)
+    ok, ov, oc = oracle.coo_from_lookups(ids, vals, 100000)
+    assert u == ok.size == n_ids and (oc == run).all()
+    assert np.array_equal(gk, ok) and np.array_equal(gc, oc)
+    assert_sums_close(gv, ov, ids, ok, oc, vals)
+
+
+def test_unaligned_values():
+    """Value rows that are only 4-byte aligned take the one-float path."""
+    rng = np.random.default_rng(5)
+    n, width, ks = 5000, 128, 3000
+    ids = rng.integers(0, ks, size=n, dtype=np.int64)
+    vals = rng.standard_normal((n, width)).astype(np.float32)
+    buf = torch.zeros(n * width + 1, dtype=torch.float32, device="cuda")
+    buf[1:] = torch.from_numpy(vals.reshape(-1)).to("cuda")
+    out = torch.zeros(n * width + 1, dtype=torch.float32, device="cuda")
+    keys, sums, counts, U = L.coo_from_lookups(dev(ids), buf[1:].view(n, width), ks,
+                                               out_vals=out[1:].view(n, width))
+    torch.cuda.synchronize()
+    u = int(host(U)[0])
+    ok, ov, oc = oracle.coo_from_lookups(ids, vals, ks)
+    assert u == ok.size
+    assert np.array_equal(host(keys)[:u], ok) and np.array_equal(host(counts)[:u], oc)
+    assert_sums_close(host(sums)[:u], ov, ids, ok, oc, vals)
 
 
 def test_empty_lookups():
