@@ -11,9 +11,13 @@ resident in HBM before the timed region starts.
 Prints one JSON line:  value = touched coordinates updated per second over the
 whole timed region (G/s); roofline = the update kernel's algorithmic bytes per
 launch / its mean duration (HIP events around every update launch of the timed
-region, on the launch stream) against 8 TB/s; breakdown_us = median time of
-each call from a second, separately timed pass over the same inputs;
-cpu_baseline = the CPU oracle on a bounded sample of the same workload.
+region, on the launch stream) against 8 TB/s, with a plain 1 GiB device copy
+measured alongside as the practical bandwidth ceiling; breakdown_us = p10 /
+median / p90 of each call and of the whole step from a second, separately
+timed pass over the same inputs; cold = the update again in a third pass that
+writes a 512 MB buffer before every step, so the state rows come from HBM
+rather than the 256 MB last-level cache; cpu_baseline = the CPU oracle on a
+bounded sample of the same workload.
 
 Events are created through the HIP runtime with hipEventDisableSystemFence:
 they only take timestamps, and skipping the system-scope release (an L2
@@ -139,6 +143,33 @@ def calibrate_sleep(torch, stream, hold_ms: float) -> int:
     torch.cuda.synchronize()
     ms = max(e0.elapsed_time(e1), 1e-3)
     return int(min(probe * hold_ms / ms, 1 << 40))
+
+
+def device_copy_gbs(torch, stream) -> float:
+    """Best of 5 plain 1 GiB device-to-device copies (torch's copy kernel), in
+    GB/s of bytes read + written: the practical ceiling next to the peak."""
+    n = 1 << 28
+    a = torch.ones(n, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    ev = HipEvents(2)
+    best = float("inf")
+    for _ in range(5):
+        ev.record(0, stream)
+        b.copy_(a)
+        ev.record(1, stream)
+        torch.cuda.synchronize()
+        best = min(best, ev.ms(0, 1))
+    ev.close()
+    return 2.0 * 4 * n / (best * 1e-3) / 1e9
+
+
+def pcts(x_ms) -> dict:
+    """p10 / median / p90 of per-launch milliseconds, in microseconds."""
+    import numpy as np
+
+    p10, p50, p90 = np.percentile(np.asarray(x_ms) * 1e3, [10, 50, 90])
+    return {"p10": float(p10), "p50": float(p50), "p90": float(p90)}
 
 
 def copy_probe(steps: int) -> None:
@@ -281,12 +312,32 @@ def main() -> int:
     canon_t = np.array([bev.ms(4 * k, 4 * k + 1) for k in range(K)])
     csr_t = np.array([bev.ms(4 * k + 1, 4 * k + 2) for k in range(K)])
     upd_b = np.array([bev.ms(4 * k + 2, 4 * k + 3) for k in range(K)])
+    step_t = np.array([bev.ms(4 * k, 4 * k + 3) for k in range(K)])
     bev.close()
+
+    # Cold regime (not part of the value): the same K inputs, a 512 MB buffer
+    # written between steps to evict the last-level cache, update timed.
+    log("cold pass (512 MB written between steps)")
+    scrub = torch.empty(128 << 20, dtype=torch.float32, device="cuda")
+    cev = HipEvents(2 * K)
+    for k, s in enumerate(range(W, W + K)):
+        scrub.fill_(float(k))
+        canon(s)
+        g = csr(s)
+        cev.record(2 * k, stream)
+        opt.step(g, stream=stream)
+        cev.record(2 * k + 1, stream)
+    torch.cuda.synchronize()
+    upd_cold = np.array([cev.ms(2 * k, 2 * k + 1) for k in range(K)])
+    cev.close()
+    del scrub
+    copy_gbs = device_copy_gbs(torch, stream)
 
     U = nuniq.cpu().numpy()[W:]
     coords = int(U.sum()) * Cc
     upd_bytes = BYTES_PER_COORD * U * Cc + BYTES_PER_ROW * U
     achieved = float((upd_bytes / (upd * 1e-3)).mean() / 1e9)
+    cold_achieved = float((upd_bytes / (upd_cold * 1e-3)).mean() / 1e9)
     traffic = None
     if sources_sha256() == UPDATE_TRAFFIC["sources_sha256"]:
         traffic = UPDATE_TRAFFIC["fetch_bytes"] + UPDATE_TRAFFIC["write_bytes"]
@@ -312,11 +363,14 @@ def main() -> int:
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled)",
                      "algorithmic_bytes_per_launch": float(upd_bytes.mean()),
                      "kernel": "k_update_rows<AdamOp<DormancyDecay>, SrcCsrTouched, 32>",
-                     "mean_us": float(upd.mean() * 1e3),
-                     "coords_per_s_G": float((U * Cc / (upd * 1e-3)).mean() / 1e9)},
-        "breakdown_us": {"coo_from_lookups": float(np.median(canon_t) * 1e3),
-                         "csr_from_coo": float(np.median(csr_t) * 1e3),
-                         "sparse_adam_step": float(np.median(upd_b) * 1e3)},
+                     "mean_us": float(upd.mean() * 1e3), "us": pcts(upd),
+                     "coords_per_s_G": float((U * Cc / (upd * 1e-3)).mean() / 1e9),
+                     "device_copy_GBs": copy_gbs,
+                     "frac_of_device_copy": achieved / copy_gbs,
+                     "cold": {"achieved": cold_achieved, "frac": cold_achieved / HBM_PEAK_GBS,
+                              "mean_us": float(upd_cold.mean() * 1e3), "us": pcts(upd_cold)}},
+        "breakdown_us": {"coo_from_lookups": pcts(canon_t), "csr_from_coo": pcts(csr_t),
+                         "sparse_adam_step": pcts(upd_b), "step": pcts(step_t)},
     }
     if args.cpu_seconds > 0:
         log("cpu baseline (oracle)")

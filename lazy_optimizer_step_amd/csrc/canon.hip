@@ -125,18 +125,22 @@ __device__ __forceinline__ bool lb_wait(const uint32_t* p, uint32_t* out) {
 }
 
 // Sum of the counts published by tiles tile-1, tile-2, ... (words at
-// lb[j * stride]) back to the nearest inclusive prefix.  Reads 8 words at a
-// time so that one memory round trip covers 8 predecessors.
+// lb[j * stride]) back to the nearest inclusive prefix.  Reads kLookDepth
+// words at a time so that one memory round trip covers that many
+// predecessors: every tile starts at once, so inclusive prefixes are still
+// scarce when most tiles look back.
+constexpr int kLookDepth = 4;
 __device__ __forceinline__ bool look_back(const uint32_t* lb, int64_t tile, int64_t stride,
                                           uint32_t* excl_out) {
     uint32_t excl = 0;
     int64_t j = tile - 1;
     while (j >= 0) {
-        uint32_t v[8];
+        uint32_t v[kLookDepth];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = (j - u >= 0) ? ld_dev(lb + (j - u) * stride) : kLbInc;
+        for (int u = 0; u < kLookDepth; ++u)
+            v[u] = (j - u >= 0) ? ld_dev(lb + (j - u) * stride) : kLbInc;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < kLookDepth; ++u) {
             if (j - u < 0) {
                 *excl_out = excl;
                 return true;
@@ -149,7 +153,7 @@ __device__ __forceinline__ bool look_back(const uint32_t* lb, int64_t tile, int6
                 return true;
             }
         }
-        j -= 8;
+        j -= kLookDepth;
     }
     *excl_out = excl;
     return true;
@@ -643,22 +647,22 @@ __global__ __launch_bounds__(256) void k_dupsum_rows(
 
 
 // Adds partials q in [lo, hi) of a segment whose start chunk is `chunk`
-// (q = 0: plast[chunk], q > 0: pfirst[chunk + q]) in increasing q, 8 loads in
+// (q = 0: plast[chunk], q > 0: pfirst[chunk + q]) in increasing q, D loads in
 // flight (past hi, partial lo is reloaded and unused).
-template <int V>
+template <int V, int D>
 __device__ __forceinline__ void add_partials(double (&acc)[V], const double* pfirst,
                                              const double* plast, int64_t chunk, int64_t lo,
                                              int64_t hi, int64_t width, int64_t col) {
-    for (int64_t q0 = lo; q0 < hi; q0 += 8) {
-        double row[8][V];
+    for (int64_t q0 = lo; q0 < hi; q0 += D) {
+        double row[D][V];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < D; ++u) {
             const int64_t q = q0 + u < hi ? q0 + u : lo;
             const double* src = (q == 0) ? plast + chunk * width : pfirst + (chunk + q) * width;
             load_part<V>(row[u], src + col, col, width);
         }
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
+        for (int u = 0; u < D; ++u)
             if (q0 + u < hi) {
 #pragma unroll
                 for (int v = 0; v < V; ++v) acc[v] += row[u][v];
@@ -674,7 +678,8 @@ __device__ __forceinline__ void add_partials(double (&acc)[V], const double* pfi
 // in chunk order by one wave (one chunk's record per wave); beyond, by a
 // whole block from the list of such chunks (blocks stride over the list):
 // [0, m) is cut into 16 equal runs, wave r adds run r in chunk order with 8
-// loads in flight, and wave 0 adds the 16 run sums in run order.
+// loads in flight (4 when V = 4, within the register budget of a 1024-thread
+// block), and wave 0 adds the 16 run sums in run order.
 template <int V>
 __global__ __launch_bounds__(kFixThreads) void k_dupsum_fixup(
     const int32_t* __restrict__ cross, const int32_t* __restrict__ big,
@@ -695,7 +700,7 @@ __global__ __launch_bounds__(kFixThreads) void k_dupsum_fixup(
             double tot[V];
 #pragma unroll
             for (int v = 0; v < V; ++v) tot[v] = 0.0;
-            add_partials<V>(tot, pfirst, plast, chunk, 0, m, width, col);
+            add_partials<V, (V == 4 ? 4 : 8)>(tot, pfirst, plast, chunk, 0, m, width, col);
             store_row<V>(out_vals + (int64_t)seg * width + col, tot, col, width);
         }
     }
@@ -710,7 +715,7 @@ __global__ __launch_bounds__(kFixThreads) void k_dupsum_fixup(
             double acc[V];
 #pragma unroll
             for (int v = 0; v < V; ++v) acc[v] = 0.0;
-            add_partials<V>(acc, pfirst, plast, chunk, lo, hi, width, col);
+            add_partials<V, (V == 4 ? 4 : 8)>(acc, pfirst, plast, chunk, lo, hi, width, col);
 #pragma unroll
             for (int v = 0; v < V; ++v) part[w][lane * V + v] = acc[v];
             __syncthreads();
