@@ -27,6 +27,7 @@ ERROR_NAMES = {OK: "OK", EINVAL: "EINVAL", ERANGE: "ERANGE", ENOTCANON: "ENOTCAN
                ESHAPE: "ESHAPE", ENONFINITE: "ENONFINITE", EOVERFLOW: "EOVERFLOW",
                EWORKSPACE: "EWORKSPACE", EDEVICE: "EDEVICE", ENOMEM: "ENOMEM"}
 MODE_LAZY, MODE_DORMANCY = 0, 1
+WD_L2, WD_DECOUPLED = 0, 1
 CHECK_FINITE = 1
 
 
@@ -49,7 +50,15 @@ def build(force: bool = False) -> str:
 
 class _AdamCfg(C.Structure):
     _fields_ = [("lr", C.c_double), ("beta1", C.c_double), ("beta2", C.c_double),
-                ("eps", C.c_double), ("mode", C.c_int)]
+                ("eps", C.c_double), ("mode", C.c_int), ("weight_decay", C.c_double),
+                ("wd_mode", C.c_int)]
+
+
+def _adam_cfg(lr, beta1, beta2, eps, mode, weight_decay, weight_decay_mode):
+    if weight_decay_mode not in ("l2", "decoupled"):
+        raise ValueError(f"weight_decay_mode {weight_decay_mode!r}: 'l2' or 'decoupled'")
+    return _AdamCfg(lr, beta1, beta2, eps, MODE_DORMANCY if mode == "dormancy" else MODE_LAZY,
+                    weight_decay, WD_DECOUPLED if weight_decay_mode == "decoupled" else WD_L2)
 
 
 class _SgdCfg(C.Structure):
@@ -155,14 +164,14 @@ class Adam:
     table of which only a few rows are ever touched)."""
 
     def __init__(self, params, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, mode="dormancy",
-                 m=None, v=None, last_step=None):
+                 m=None, v=None, last_step=None, weight_decay=0.0, weight_decay_mode="l2"):
         self.p = params
         self.rows = params.shape[0]
         self.cols = params.shape[1] if params.ndim == 2 else 1
         self.m = np.zeros_like(params) if m is None else m
         self.v = np.zeros_like(params) if v is None else v
         self.ls = np.zeros(params.shape, np.int32) if last_step is None else last_step
-        self.cfg = _AdamCfg(lr, beta1, beta2, eps, MODE_DORMANCY if mode == "dormancy" else MODE_LAZY)
+        self.cfg = _adam_cfg(lr, beta1, beta2, eps, mode, weight_decay, weight_decay_mode)
         self.t = 0
 
     def _state(self):
@@ -227,12 +236,13 @@ class Sgd:
 class Adam64:
     """1-D sparse / lazy Adam with double state."""
 
-    def __init__(self, params, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, mode="dormancy"):
+    def __init__(self, params, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, mode="dormancy",
+                 weight_decay=0.0, weight_decay_mode="l2"):
         self.p = np.array(params, dtype=np.float64)
         self.m = np.zeros_like(self.p)
         self.v = np.zeros_like(self.p)
         self.ls = np.zeros(self.p.shape, np.int32)
-        self.cfg = _AdamCfg(lr, beta1, beta2, eps, MODE_DORMANCY if mode == "dormancy" else MODE_LAZY)
+        self.cfg = _adam_cfg(lr, beta1, beta2, eps, mode, weight_decay, weight_decay_mode)
         self.t = 0
 
     def step(self, idx, vals):

@@ -18,6 +18,9 @@
  * From the DiskSparseAdam README (page 2), only where page 1 is silent:
  *   - "Safe Duplicate Aggregation & Sorted I/O": duplicate indices are summed
  *     and the result is sorted;
+ *   - "Explicit Weight Decay Semantics" (Euclidean case): Adam weight decay
+ *     "l2" adds wd * w to the gradient, "decoupled" adds it to the descent
+ *     direction (AdamW);
  *   - "Validated Inputs": out-of-range indices, wrong shapes and non-finite
  *     gradients are errors;
  *   - active rows computed in float64, storage float32.
@@ -197,20 +200,31 @@ int orc_csr_to_coo(const int32_t* row_offsets, const int32_t* col_indices, const
  * Lazy: one decay factor beta per touch.  DormancyDecay: beta^(t - last_step),
  * i.e. what the moments would hold had the dormant steps carried zero
  * gradients.  Bias correction uses the global t; eps is added after the square
- * root of the bias-corrected second moment. */
+ * root of the bias-corrected second moment.
+ * Weight decay, on the touched coordinate only (as page 1 applies SGD's
+ * coupled decay), with p0 the value before the step:
+ *   "l2":        g <- g + wd * p0 before the moments;
+ *   "decoupled": p <- p - lr * (m_hat / (sqrt(v_hat) + eps) + wd * p0),
+ *                evaluated as the Adam move followed by  - (lr * wd) * p0.
+ * With wd == 0 neither term is applied, so the result is the undecayed one
+ * bit for bit. */
 static void adam_coord(double* p, double* m, double* v, int32_t* ls, double g, int64_t t,
                        const orc_adam_cfg* c) {
+    const double p0 = *p;
     double d1 = c->beta1, d2 = c->beta2;
     if (c->mode == ORC_MODE_DORMANCY) {
         double gap = (double)(t - (int64_t)*ls);
         d1 = pow(c->beta1, gap);
         d2 = pow(c->beta2, gap);
     }
+    if (c->weight_decay != 0.0 && c->wd_mode == ORC_WD_L2) g = g + c->weight_decay * p0;
     *m = d1 * *m + (1.0 - c->beta1) * g;
     *v = d2 * *v + (1.0 - c->beta2) * (g * g);
     double m_hat = *m / (1.0 - pow(c->beta1, (double)t));
     double v_hat = *v / (1.0 - pow(c->beta2, (double)t));
-    *p = *p - c->lr * m_hat / (sqrt(v_hat) + c->eps);
+    *p = p0 - c->lr * m_hat / (sqrt(v_hat) + c->eps);
+    if (c->weight_decay != 0.0 && c->wd_mode == ORC_WD_DECOUPLED)
+        *p = *p - (c->lr * c->weight_decay) * p0;
     *ls = (int32_t)t;
 }
 
@@ -233,6 +247,8 @@ static int check_adam_cfg(const orc_adam_cfg* c) {
         !isfinite(c->eps))
         return ORC_EINVAL;
     if (c->mode != ORC_MODE_LAZY && c->mode != ORC_MODE_DORMANCY) return ORC_EINVAL;
+    if (!(c->weight_decay >= 0.0) || !isfinite(c->weight_decay)) return ORC_EINVAL;
+    if (c->wd_mode != ORC_WD_L2 && c->wd_mode != ORC_WD_DECOUPLED) return ORC_EINVAL;
     return ORC_OK;
 }
 

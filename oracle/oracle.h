@@ -28,11 +28,16 @@ enum {
 };
 
 enum { ORC_MODE_LAZY = 0, ORC_MODE_DORMANCY = 1 };
+enum { ORC_WD_L2 = 0, ORC_WD_DECOUPLED = 1 };
 enum { ORC_CHECK_FINITE = 1 };
 
+/* weight_decay >= 0; wd_mode ORC_WD_L2 (into the gradient) or
+ * ORC_WD_DECOUPLED (beside the Adam move, AdamW). */
 typedef struct {
     double lr, beta1, beta2, eps;
     int mode;
+    double weight_decay;
+    int wd_mode;
 } orc_adam_cfg;
 
 typedef struct {
