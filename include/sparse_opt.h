@@ -80,13 +80,24 @@ typedef enum spopt_status {
 #define SPOPT_MODE_LAZY 0      /* LazyAdamMode::Lazy */
 #define SPOPT_MODE_DORMANCY 1  /* LazyAdamMode::DormancyDecay */
 
-/* Sparse / lazy Adam.  lr >= 0, beta1 and beta2 in [0, 1), eps > 0 (ranges of
- * the DiskSparseAdam API reference; lr >= 0 is this library's own rule).
- * Doubles: every derived scalar (1 - beta, bias corrections, log2 beta) is
- * formed in double on the host and rounded once. */
+#define SPOPT_WD_L2 0         /* weight decay added to the gradient (Adam L2) */
+#define SPOPT_WD_DECOUPLED 1  /* weight decay beside the Adam move (AdamW) */
+
+/* Sparse / lazy Adam.  lr >= 0, beta1 and beta2 in [0, 1), eps > 0,
+ * weight_decay >= 0 (ranges of the DiskSparseAdam API reference; lr >= 0 is
+ * this library's own rule).  Doubles: every derived scalar (1 - beta, bias
+ * corrections, log2 beta, lr * weight_decay) is formed in double on the host
+ * and rounded once.
+ * Weight decay (DiskSparseAdam README, "Explicit Weight Decay Semantics", its
+ * Euclidean case), applied to touched coordinates only, with p0 the value
+ * before the step: SPOPT_WD_L2 adds weight_decay * p0 to the gradient before
+ * the moments; SPOPT_WD_DECOUPLED subtracts lr * weight_decay * p0 after the
+ * Adam move (AdamW).  weight_decay == 0 is the undecayed step bit for bit. */
 typedef struct spopt_adam_config {
     double lr, beta1, beta2, eps;
     int32_t mode; /* SPOPT_MODE_LAZY or SPOPT_MODE_DORMANCY */
+    double weight_decay;
+    int32_t weight_decay_mode; /* SPOPT_WD_L2 or SPOPT_WD_DECOUPLED */
 } spopt_adam_config;
 
 /* Sparse SGD.  lr >= 0, momentum in [0, 1), weight_decay >= 0.  Coupled weight

@@ -267,14 +267,18 @@ class SparseAdam:
     allocates on the device (m = v = 0, last_step = 0)."""
 
     def __init__(self, params: torch.Tensor, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8,
-                 mode="dormancy"):
+                 mode="dormancy", weight_decay=0.0, weight_decay_mode="l2"):
+        if weight_decay_mode not in ("l2", "decoupled"):
+            raise ValueError(f"weight_decay_mode {weight_decay_mode!r}: 'l2' or 'decoupled'")
         self.params = params
         self.rows = params.shape[0]
         self.cols = params.shape[1] if params.dim() == 2 else 1
         self.m = torch.zeros_like(params)
         self.v = torch.zeros_like(params)
         self.last_step = torch.zeros(params.shape, dtype=torch.int32, device=params.device)
-        cfg = _lib.AdamConfig(lr, beta1, beta2, eps, MODE_DORMANCY if mode == "dormancy" else MODE_LAZY)
+        cfg = _lib.AdamConfig(lr, beta1, beta2, eps,
+                              MODE_DORMANCY if mode == "dormancy" else MODE_LAZY, weight_decay,
+                              _lib.WD_DECOUPLED if weight_decay_mode == "decoupled" else _lib.WD_L2)
         self.handle = sparse_opt_create(KIND_ADAM, cfg, self.rows, self.cols, params, self.m, self.v,
                                         self.last_step)
 

@@ -22,12 +22,14 @@ ERROR_NAMES = {OK: "OK", EINVAL: "EINVAL", ERANGE: "ERANGE", ENOTCANON: "ENOTCAN
 TRUSTED, VALIDATE = 0, 1
 KIND_ADAM, KIND_SGD = 0, 1
 MODE_LAZY, MODE_DORMANCY = 0, 1
+WD_L2, WD_DECOUPLED = 0, 1
 FORMAT_COO, FORMAT_CSR = 0, 1
 
 
 class AdamConfig(C.Structure):
     _fields_ = [("lr", C.c_double), ("beta1", C.c_double), ("beta2", C.c_double),
-                ("eps", C.c_double), ("mode", C.c_int32)]
+                ("eps", C.c_double), ("mode", C.c_int32), ("weight_decay", C.c_double),
+                ("weight_decay_mode", C.c_int32)]
 
 
 class SgdConfig(C.Structure):

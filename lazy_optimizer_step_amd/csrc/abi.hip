@@ -105,6 +105,11 @@ static int check_adam_config(const spopt_adam_config* c) {
         return fail(SPOPT_EINVAL, "adam config: eps must be finite and > 0");
     if (c->mode != SPOPT_MODE_LAZY && c->mode != SPOPT_MODE_DORMANCY)
         return fail(SPOPT_EINVAL, "adam config: unknown mode %d", c->mode);
+    if (!(c->weight_decay >= 0.0) || !isfinite(c->weight_decay))
+        return fail(SPOPT_EINVAL, "adam config: weight_decay must be finite and >= 0");
+    if (c->weight_decay_mode != SPOPT_WD_L2 && c->weight_decay_mode != SPOPT_WD_DECOUPLED)
+        return fail(SPOPT_EINVAL, "adam config: unknown weight_decay_mode %d",
+                    c->weight_decay_mode);
     return SPOPT_OK;
 }
 
@@ -261,7 +266,11 @@ extern "C" int sparse_adam_step(spopt_t h, const spopt_grad* g, void* stream, ui
     a.pow1 = h->d_pow;
     a.pow2 = h->d_pow + kPowTable;
     a.t = (int32_t)t;
-    rc = launch_adam(h->p, h->m, h->v, h->ls, a, c.mode, g, h->rows, h->cols, s);
+    a.wd = c.weight_decay;
+    a.lr_wd = c.lr * c.weight_decay;
+    const int wd_kind = c.weight_decay == 0.0 ? kWdNone
+                        : c.weight_decay_mode == SPOPT_WD_L2 ? kWdL2 : kWdDecoupled;
+    rc = launch_adam(h->p, h->m, h->v, h->ls, a, c.mode, wd_kind, g, h->rows, h->cols, s);
     if (rc) return rc;
     h->t = t;
     return SPOPT_OK;

@@ -149,14 +149,19 @@ int launch_check_csr(const spopt_csr* c, int check_finite, const int32_t* ls, in
 constexpr int kPowTable = 1024;
 
 // Per-step scalars of Adam, formed in double on the host.
+// Weight decay of an Adam step: none (weight_decay == 0), into the gradient,
+// or beside the move.
+enum : int { kWdNone = 0, kWdL2 = 1, kWdDecoupled = 2 };
+
 struct AdamScalars {
     double lr, c1, c2, bc1, bc2, eps, beta1, beta2, l2b1, l2b2;
+    double wd, lr_wd;    // weight_decay and lr * weight_decay
     const double* pow1;  // device [kPowTable]: beta1^k
     const double* pow2;  // device [kPowTable]: beta2^k
     int32_t t;
 };
 int launch_adam(float* p, float* m, float* v, int32_t* ls, const AdamScalars& a, int mode,
-                const spopt_grad* gr, int64_t rows, int64_t cols, hipStream_t s);
+                int wd_kind, const spopt_grad* gr, int64_t rows, int64_t cols, hipStream_t s);
 int launch_sgd(float* p, float* b, double lr, double mu, double wd, const spopt_grad* gr,
                int64_t rows, int64_t cols, hipStream_t s);
 

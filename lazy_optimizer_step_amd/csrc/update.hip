@@ -5,6 +5,10 @@
 //     d = beta (Lazy) or beta^(t - last_step) (DormancyDecay)
 //     m = d1*m + (1-beta1)*g,  v = d2*v + (1-beta2)*g^2
 //     p -= lr * (m/(1-beta1^t)) / (sqrt(v/(1-beta2^t)) + eps),  last_step = t
+//   with the optional weight decay of the DiskSparseAdam README ("Explicit
+//   Weight Decay Semantics", Euclidean case) on the touched coordinate, p0 its
+//   value before the step: "l2" g += wd*p0 first; "decoupled" p -= lr*wd*p0
+//   after the move (AdamW).
 //   SGD, section "Sparse SGD": g' = g + wd*p; with momentum b = mu*b + g',
 //     p -= lr*b; without, p -= lr*g'.
 // Arithmetic is double with contraction off, state loaded from and rounded
@@ -32,7 +36,7 @@ namespace spopt {
 //   load(i, r)      p, m, v (and last_step) of 4 coordinates,
 //   prep(r, x)      loads that depend on them (beta^gap from the table),
 //   compute(r, x, g), store(i, r).
-template <int MODE>
+template <int MODE, int WD = kWdNone>
 struct AdamOp {
     float* __restrict__ p;
     float* __restrict__ m;
@@ -55,7 +59,9 @@ struct AdamOp {
                                           double t2, float g) const {
 #pragma clang fp contract(off)
         double d1 = a.beta1, d2 = a.beta2;
-        const double m0 = mm, v0 = vv, gd = g;
+        const double p0 = pp, m0 = mm, v0 = vv;
+        double gd = g;
+        if (WD == kWdL2) gd = gd + a.wd * p0;
         if (MODE == SPOPT_MODE_DORMANCY) {
             const int32_t gap = a.t - last;
             if (gap != 1) {
@@ -72,7 +78,8 @@ struct AdamOp {
         const double v1 = d2 * v0 + a.c2 * (gd * gd);
         const double m_hat = m1 / a.bc1;
         const double v_hat = v1 / a.bc2;
-        const double p1 = (double)pp - a.lr * m_hat / (sqrt(v_hat) + a.eps);
+        double p1 = p0 - a.lr * m_hat / (sqrt(v_hat) + a.eps);
+        if (WD == kWdDecoupled) p1 = p1 - a.lr_wd * p0;
         pp = (float)p1;
         mm = (float)m1;
         vv = (float)v1;
@@ -376,8 +383,8 @@ template <class Op>
 struct RowBatch {
     static constexpr int kIters = 4;  // full rows per sub-group in flight
 };
-template <int MODE>
-struct RowBatch<AdamOp<MODE>> {
+template <int MODE, int WD>
+struct RowBatch<AdamOp<MODE, WD>> {
     static constexpr int kIters = 2;  // Adam holds more state per row in registers
 };
 
@@ -443,12 +450,24 @@ static int launch_update(const Op& op, bool state_aligned, const spopt_grad* gr,
     return SPOPT_OK;
 }
 
+template <int MODE>
+static int launch_adam_mode(float* p, float* m, float* v, int32_t* ls, const AdamScalars& a,
+                            int wd_kind, bool al, const spopt_grad* gr, int64_t rows, int64_t cols,
+                            hipStream_t s) {
+    if (wd_kind == kWdL2)
+        return launch_update(AdamOp<MODE, kWdL2>{p, m, v, ls, a}, al, gr, rows, cols, s);
+    if (wd_kind == kWdDecoupled)
+        return launch_update(AdamOp<MODE, kWdDecoupled>{p, m, v, ls, a}, al, gr, rows, cols, s);
+    return launch_update(AdamOp<MODE, kWdNone>{p, m, v, ls, a}, al, gr, rows, cols, s);
+}
+
 int launch_adam(float* p, float* m, float* v, int32_t* ls, const AdamScalars& a, int mode,
-                const spopt_grad* gr, int64_t rows, int64_t cols, hipStream_t s) {
+                int wd_kind, const spopt_grad* gr, int64_t rows, int64_t cols, hipStream_t s) {
     const bool al = aligned16(p) && aligned16(m) && aligned16(v) && aligned16(ls);
     if (mode == SPOPT_MODE_DORMANCY)
-        return launch_update(AdamOp<SPOPT_MODE_DORMANCY>{p, m, v, ls, a}, al, gr, rows, cols, s);
-    return launch_update(AdamOp<SPOPT_MODE_LAZY>{p, m, v, ls, a}, al, gr, rows, cols, s);
+        return launch_adam_mode<SPOPT_MODE_DORMANCY>(p, m, v, ls, a, wd_kind, al, gr, rows, cols,
+                                                     s);
+    return launch_adam_mode<SPOPT_MODE_LAZY>(p, m, v, ls, a, wd_kind, al, gr, rows, cols, s);
 }
 
 int launch_sgd(float* p, float* b, double lr, double mu, double wd, const spopt_grad* gr,

@@ -53,7 +53,10 @@ FAKE = 256  # a non-NULL address that create() stores but never dereferences
 @pytest.mark.parametrize("cfg", [
     _lib.AdamConfig(1e-3, 1.0, 0.999, 1e-8, 1), _lib.AdamConfig(1e-3, 0.9, -0.1, 1e-8, 1),
     _lib.AdamConfig(1e-3, 0.9, 0.999, 0.0, 1), _lib.AdamConfig(-1.0, 0.9, 0.999, 1e-8, 1),
-    _lib.AdamConfig(1e-3, 0.9, 0.999, 1e-8, 7)])
+    _lib.AdamConfig(1e-3, 0.9, 0.999, 1e-8, 7),
+    _lib.AdamConfig(1e-3, 0.9, 0.999, 1e-8, 1, -0.1, _lib.WD_L2),
+    _lib.AdamConfig(1e-3, 0.9, 0.999, 1e-8, 1, float("nan"), _lib.WD_DECOUPLED),
+    _lib.AdamConfig(1e-3, 0.9, 0.999, 1e-8, 1, 0.01, 5)])
 def test_create_rejects_bad_adam_config(cfg):
     h = C.c_void_p()
     rc = _lib.lib().sparse_opt_create(C.byref(h), _lib.KIND_ADAM, C.byref(cfg), 10, 4, FAKE, FAKE,
