@@ -79,6 +79,7 @@ def lib():
         L.orc_csr_to_coo.argtypes = [P, P, P, I64, I64, P, P]
         L.orc_adam_coo_f32.argtypes = [P, P, P, P, I64, I64, P, P, I64, I64, P, C.c_int]
         L.orc_adam_csr_f32.argtypes = [P, P, P, P, I64, I64, P, P, P, I64, P, C.c_int]
+        L.orc_adam_rows_csr_f32.argtypes = [P, P, P, P, I64, I64, P, P, P, I64, P, C.c_int]
         L.orc_adam_coo_f64.argtypes = [P, P, P, P, I64, P, P, I64, I64, P]
         L.orc_sgd_coo_f32.argtypes = [P, P, I64, I64, P, P, I64, P, C.c_int]
         L.orc_sgd_csr_f32.argtypes = [P, P, I64, I64, P, P, P, P, C.c_int]
@@ -196,6 +197,36 @@ class Adam:
                                     _p(vals), self.t + 1, C.byref(self.cfg),
                                     CHECK_FINITE if check_finite else 0)
         _check(rc, "adam_csr")
+        self.t += 1
+
+
+class AdamRows(Adam):
+    """Sparse / lazy Adam with one last_step per row (full-row gradients only)."""
+
+    def __init__(self, params, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, mode="dormancy",
+                 m=None, v=None, last_step=None, weight_decay=0.0, weight_decay_mode="l2"):
+        rows = params.shape[0]
+        super().__init__(params, lr, beta1, beta2, eps, mode, m, v,
+                         np.zeros(rows, np.int32) if last_step is None else last_step,
+                         weight_decay, weight_decay_mode)
+
+    def step_coo(self, idx, vals, width: int = 1, check_finite=False):
+        """Full-row COO (width == cols): keys are row ids."""
+        if width != self.cols:
+            raise ValueError("a row-granular table takes full-row gradients only")
+        idx = _arr(idx, np.int64).reshape(-1)
+        vals = _arr(vals, np.float32).reshape(-1)
+        ro, ci, cv = csr_from_coo(idx, vals, self.rows, self.cols, self.rows, self.cols)
+        self.step_csr(ro, ci, cv, check_finite)
+
+    def step_csr(self, row_offsets, col_indices, vals, check_finite=False):
+        ro = _arr(row_offsets, np.int32)
+        ci = _arr(col_indices, np.int32)
+        vals = _arr(vals, np.float32)
+        rc = lib().orc_adam_rows_csr_f32(*self._state(), self.rows, self.cols, _p(ro), _p(ci),
+                                         _p(vals), self.t + 1, C.byref(self.cfg),
+                                         CHECK_FINITE if check_finite else 0)
+        _check(rc, "adam_rows_csr")
         self.t += 1
 
 

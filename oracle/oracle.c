@@ -341,6 +341,41 @@ int orc_adam_csr_f32(float* p, float* m, float* v, int32_t* ls, int64_t rows, in
     return ORC_OK;
 }
 
+/* Row-granular last_step.  The optirs page's SparseAdam ("Lazy Adam") keeps
+ * last_step per coordinate; in a table whose gradients always cover whole
+ * rows every coordinate of a row carries the same value, so one int32 per row
+ * stores the same state, and a full-row step is the per-coordinate step with
+ * the row's value broadcast across the row. */
+int orc_adam_rows_csr_f32(float* p, float* m, float* v, int32_t* ls, int64_t rows, int64_t cols,
+                          const int32_t* row_offsets, const int32_t* col_indices, const float* g,
+                          int64_t t, const orc_adam_cfg* cfg, int flags) {
+    int rc;
+    if ((rc = check_adam_cfg(cfg)) || (rc = check_step(t)) ||
+        (rc = check_csr_grad(row_offsets, col_indices, g, rows, cols, flags)))
+        return rc;
+    if (p == NULL || m == NULL || v == NULL || ls == NULL) return ORC_EINVAL;
+    for (int64_t r = 0; r < rows; ++r) {
+        int64_t len = (int64_t)row_offsets[r + 1] - row_offsets[r];
+        if (len != 0 && len != cols) return ORC_ESHAPE;
+        if (len != 0 && ls[r] >= t) return ORC_EINVAL;
+    }
+    for (int64_t r = 0; r < rows; ++r) {
+        if (row_offsets[r + 1] == row_offsets[r]) continue;
+        const int32_t before = ls[r];
+        for (int32_t j = row_offsets[r]; j < row_offsets[r + 1]; ++j) {
+            int64_t i = r * cols + col_indices[j];
+            double pp = p[i], mm = m[i], vv = v[i];
+            int32_t l = before;
+            adam_coord(&pp, &mm, &vv, &l, (double)g[j], t, cfg);
+            p[i] = (float)pp;
+            m[i] = (float)mm;
+            v[i] = (float)vv;
+        }
+        ls[r] = (int32_t)t;
+    }
+    return ORC_OK;
+}
+
 /* ---- Adam, double storage (for the pins) -------------------------------- */
 
 int orc_adam_coo_f64(double* p, double* m, double* v, int32_t* ls, int64_t dim,

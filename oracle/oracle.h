@@ -69,6 +69,13 @@ int orc_adam_coo_f32(float* p, float* m, float* v, int32_t* ls, int64_t dim, int
 int orc_adam_csr_f32(float* p, float* m, float* v, int32_t* ls, int64_t rows, int64_t cols,
                      const int32_t* row_offsets, const int32_t* col_indices, const float* g,
                      int64_t t, const orc_adam_cfg* cfg, int flags);
+/* Row-granular last_step (one int32 per row, ls[rows]): every non-empty row
+ * of the CSR gradient must be full (cols entries), else ORC_ESHAPE.  Each
+ * coordinate of a touched row uses the row's gap, and the row's last_step
+ * becomes t. */
+int orc_adam_rows_csr_f32(float* p, float* m, float* v, int32_t* ls, int64_t rows, int64_t cols,
+                          const int32_t* row_offsets, const int32_t* col_indices, const float* g,
+                          int64_t t, const orc_adam_cfg* cfg, int flags);
 int orc_adam_coo_f64(double* p, double* m, double* v, int32_t* ls, int64_t dim,
                      const int64_t* idx, const double* g, int64_t nnz, int64_t t,
                      const orc_adam_cfg* cfg);
