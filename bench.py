@@ -40,9 +40,12 @@ METRIC = "touched coords updated/sec (G/s) + achieved HBM GB/s % of peak, 10M x 
 HBM_PEAK_GBS = 8000.0
 # Algorithmic bytes of the DormancyDecay update: per touched coordinate read p, m, v,
 # last_step, g (20 B) and write p, m, v, last_step (16 B); per touched row read its id
-# (8 B) and two row offsets (8 B).
+# (8 B) and two row offsets (8 B).  With one last_step per row (--last-step-per-row):
+# 28 B per coordinate, and the row's last_step read and written (8 B more per row).
 BYTES_PER_COORD = 36
 BYTES_PER_ROW = 16
+BYTES_PER_COORD_ROW_LS = 28
+BYTES_PER_ROW_ROW_LS = 24
 
 # HBM bytes per launch of the update kernel on this workload, from two
 # rocprofv3 --pmc passes of this command (FETCH_SIZE scaled by 2.0 and
@@ -78,6 +81,8 @@ def parse():
                     help="budget of the CPU-oracle sample (0 disables it)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling HBM counters)")
+    ap.add_argument("--last-step-per-row", action="store_true",
+                    help="keep one last_step per table row instead of one per coordinate")
     return ap.parse_args()
 
 
@@ -185,7 +190,7 @@ def copy_probe(steps: int) -> None:
                       "launches": steps}), flush=True)
 
 
-def cpu_baseline(w, host_p0, batches, budget_s: float):
+def cpu_baseline(w, host_p0, batches, budget_s: float, per_row: bool = False):
     """The oracle, as it stands, on the first steps of the same workload until the
     time budget is spent (at least 2 steps); single thread."""
     import numpy as np
@@ -195,9 +200,10 @@ def cpu_baseline(w, host_p0, batches, budget_s: float):
     h = w.hyper
     m = np.zeros((w.rows, w.cols), np.float32)       # zero pages are mapped lazily
     v = np.zeros((w.rows, w.cols), np.float32)
-    ls = np.zeros((w.rows, w.cols), np.int32)
-    opt = oracle.Adam(host_p0, lr=h["lr"], beta1=h["beta1"], beta2=h["beta2"], eps=h["eps"],
-                      mode=w.mode, m=m, v=v, last_step=ls)
+    ls = np.zeros((w.rows,) if per_row else (w.rows, w.cols), np.int32)
+    cls = oracle.AdamRows if per_row else oracle.Adam
+    opt = cls(host_p0, lr=h["lr"], beta1=h["beta1"], beta2=h["beta2"], eps=h["eps"],
+              mode=w.mode, m=m, v=v, last_step=ls)
     coords = 0
     steps = 0
     t0 = time.perf_counter()
@@ -243,8 +249,9 @@ def main() -> int:
     log(f"initial table {R}x{Cc} float32 (N(0, {w.init_std}))")
     host_p0 = synth.init_params(w)
     params = torch.from_numpy(host_p0).to("cuda")
+    per_row = args.last_step_per_row
     opt = L.SparseAdam(params, lr=h["lr"], beta1=h["beta1"], beta2=h["beta2"], eps=h["eps"],
-                       mode=w.mode)
+                       mode=w.mode, last_step_per_row=per_row)
     log(f"inputs of {W + K} steps ({n} lookups each)")
     batches = synth.lookups_many(w, range(W + K))
     ids_d = [torch.from_numpy(i).to("cuda") for i, _ in batches]
@@ -335,11 +342,14 @@ def main() -> int:
 
     U = nuniq.cpu().numpy()[W:]
     coords = int(U.sum()) * Cc
-    upd_bytes = BYTES_PER_COORD * U * Cc + BYTES_PER_ROW * U
+    if per_row:
+        upd_bytes = BYTES_PER_COORD_ROW_LS * U * Cc + BYTES_PER_ROW_ROW_LS * U
+    else:
+        upd_bytes = BYTES_PER_COORD * U * Cc + BYTES_PER_ROW * U
     achieved = float((upd_bytes / (upd * 1e-3)).mean() / 1e9)
     cold_achieved = float((upd_bytes / (upd_cold * 1e-3)).mean() / 1e9)
     traffic = None
-    if sources_sha256() == UPDATE_TRAFFIC["sources_sha256"]:
+    if not per_row and sources_sha256() == UPDATE_TRAFFIC["sources_sha256"]:
         traffic = UPDATE_TRAFFIC["fetch_bytes"] + UPDATE_TRAFFIC["write_bytes"]
 
     result = {
@@ -356,13 +366,15 @@ def main() -> int:
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "rows": R, "cols": Cc, "lookups_per_step": n,
-                   "zipf_s": w.zipf_s, "mode": w.mode, "state": "p,m,v float32 + last_step int32",
+                   "zipf_s": w.zipf_s, "mode": w.mode, "state": "p,m,v float32 + last_step int32 per " + ("row" if per_row else "coordinate"),
                    "mean_unique_rows": float(U.mean())},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled)",
                      "algorithmic_bytes_per_launch": float(upd_bytes.mean()),
-                     "kernel": "k_update_rows<AdamOp<DormancyDecay>, SrcCsrTouched, 32>",
+                     "kernel": "k_update_rows<AdamOp<DormancyDecay, no decay, "
+                               + ("last_step per row" if per_row else "last_step per coordinate")
+                               + ">, SrcCsrTouched, 32>",
                      "mean_us": float(upd.mean() * 1e3), "us": pcts(upd),
                      "coords_per_s_G": float((U * Cc / (upd * 1e-3)).mean() / 1e9),
                      "device_copy_GBs": copy_gbs,
@@ -374,7 +386,7 @@ def main() -> int:
     }
     if args.cpu_seconds > 0:
         log("cpu baseline (oracle)")
-        result["cpu_baseline"] = cpu_baseline(w, host_p0, batches, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(w, host_p0, batches, args.cpu_seconds, per_row)
     print(json.dumps(result), flush=True)
     return 0
 

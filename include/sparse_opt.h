@@ -98,6 +98,15 @@ typedef struct spopt_adam_config {
     int32_t mode; /* SPOPT_MODE_LAZY or SPOPT_MODE_DORMANCY */
     double weight_decay;
     int32_t weight_decay_mode; /* SPOPT_WD_L2 or SPOPT_WD_DECOUPLED */
+    /* 0: last_step holds one int32 per coordinate (rows x cols), the form of
+     * the optirs_gpu sparse_optimizer page ("Lazy Adam").  1: one int32 per
+     * row (rows), for tables whose gradients always cover whole rows: every
+     * coordinate of a row then holds the same value, so this stores the same
+     * state in fewer bytes.  Such a table takes full-row gradients only: a COO
+     * over the flattened view (width 1 with cols > 1) is SPOPT_ESHAPE; a CSR
+     * row with some but not all of its columns is SPOPT_ESHAPE under
+     * SPOPT_VALIDATE and leaves the table unspecified in trusted mode. */
+    int32_t last_step_per_row;
 } spopt_adam_config;
 
 /* Sparse SGD.  lr >= 0, momentum in [0, 1), weight_decay >= 0.  Coupled weight

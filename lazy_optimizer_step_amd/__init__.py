@@ -244,11 +244,13 @@ class _Handle:
 def sparse_opt_create(kind: int, config, rows: int, cols: int, params, m_or_momentum=None, v=None,
                       last_step=None) -> _Handle:
     n = rows * cols
+    per_row = kind == KIND_ADAM and getattr(config, "last_step_per_row", 0) != 0
     _need(params, torch.float32, "params", n)
-    for t, name, dt in ((m_or_momentum, "m_or_momentum", torch.float32), (v, "v", torch.float32),
-                        (last_step, "last_step", torch.int32)):
+    for t, name, dt, size in ((m_or_momentum, "m_or_momentum", torch.float32, n),
+                              (v, "v", torch.float32, n),
+                              (last_step, "last_step", torch.int32, rows if per_row else n)):
         if t is not None:
-            _need(t, dt, name, n)
+            _need(t, dt, name, size)
     return _Handle(kind, config, rows, cols, params, m_or_momentum, v, last_step)
 
 
@@ -267,7 +269,8 @@ class SparseAdam:
     allocates on the device (m = v = 0, last_step = 0)."""
 
     def __init__(self, params: torch.Tensor, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8,
-                 mode="dormancy", weight_decay=0.0, weight_decay_mode="l2"):
+                 mode="dormancy", weight_decay=0.0, weight_decay_mode="l2",
+                 last_step_per_row=False):
         if weight_decay_mode not in ("l2", "decoupled"):
             raise ValueError(f"weight_decay_mode {weight_decay_mode!r}: 'l2' or 'decoupled'")
         self.params = params
@@ -275,10 +278,12 @@ class SparseAdam:
         self.cols = params.shape[1] if params.dim() == 2 else 1
         self.m = torch.zeros_like(params)
         self.v = torch.zeros_like(params)
-        self.last_step = torch.zeros(params.shape, dtype=torch.int32, device=params.device)
+        shape = (self.rows,) if last_step_per_row else params.shape
+        self.last_step = torch.zeros(shape, dtype=torch.int32, device=params.device)
         cfg = _lib.AdamConfig(lr, beta1, beta2, eps,
                               MODE_DORMANCY if mode == "dormancy" else MODE_LAZY, weight_decay,
-                              _lib.WD_DECOUPLED if weight_decay_mode == "decoupled" else _lib.WD_L2)
+                              _lib.WD_DECOUPLED if weight_decay_mode == "decoupled" else _lib.WD_L2,
+                              1 if last_step_per_row else 0)
         self.handle = sparse_opt_create(KIND_ADAM, cfg, self.rows, self.cols, params, self.m, self.v,
                                         self.last_step)
 

@@ -29,7 +29,7 @@ FORMAT_COO, FORMAT_CSR = 0, 1
 class AdamConfig(C.Structure):
     _fields_ = [("lr", C.c_double), ("beta1", C.c_double), ("beta2", C.c_double),
                 ("eps", C.c_double), ("mode", C.c_int32), ("weight_decay", C.c_double),
-                ("weight_decay_mode", C.c_int32)]
+                ("weight_decay_mode", C.c_int32), ("last_step_per_row", C.c_int32)]
 
 
 class SgdConfig(C.Structure):

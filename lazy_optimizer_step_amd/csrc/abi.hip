@@ -43,6 +43,9 @@ int status_to_code(uint32_t bits, const char* what) {
     if (bits & kStatusNonFinite) return fail(SPOPT_ENONFINITE, "%s: non-finite gradient", what);
     if (bits & kStatusStep)
         return fail(SPOPT_EINVAL, "%s: a touched coordinate has last_step >= t", what);
+    if (bits & kStatusPartial)
+        return fail(SPOPT_ESHAPE, "%s: a partial row for a table with one last_step per row",
+                    what);
     if (bits & kStatusTimeout)
         return fail(SPOPT_EDEVICE, "%s: a device-side wait timed out", what);
     return fail(SPOPT_EINVAL, "%s: status 0x%x", what, bits);
@@ -110,6 +113,8 @@ static int check_adam_config(const spopt_adam_config* c) {
     if (c->weight_decay_mode != SPOPT_WD_L2 && c->weight_decay_mode != SPOPT_WD_DECOUPLED)
         return fail(SPOPT_EINVAL, "adam config: unknown weight_decay_mode %d",
                     c->weight_decay_mode);
+    if (c->last_step_per_row != 0 && c->last_step_per_row != 1)
+        return fail(SPOPT_EINVAL, "adam config: last_step_per_row must be 0 or 1");
     return SPOPT_OK;
 }
 
@@ -201,6 +206,10 @@ extern "C" int sparse_opt_set_step(spopt_t h, int64_t t) {
 }
 
 // Shape checks of a gradient against the state (host side, no device access).
+static bool row_last_step(const spopt_optimizer* h) {
+    return h->kind == SPOPT_KIND_ADAM && h->adam.last_step_per_row != 0;
+}
+
 static int check_grad_shape(const spopt_optimizer* h, const spopt_grad* g, const char* what) {
     if (g == nullptr) return fail(SPOPT_EINVAL, "%s: NULL gradient", what);
     if (g->format == SPOPT_FORMAT_COO) {
@@ -215,6 +224,10 @@ static int check_grad_shape(const spopt_optimizer* h, const spopt_grad* g, const
                         "%s: COO dim %lld width %lld matches neither %lld x 1 nor %lld x %lld",
                         what, (long long)c.dim, (long long)c.width,
                         (long long)(h->rows * h->cols), (long long)h->rows, (long long)h->cols);
+        if (row_last_step(h) && !full)
+            return fail(SPOPT_ESHAPE,
+                        "%s: a table with one last_step per row takes full-row gradients only",
+                        what);
         return SPOPT_OK;
     }
     if (g->format == SPOPT_FORMAT_CSR) {
@@ -233,9 +246,17 @@ static int check_grad_shape(const spopt_optimizer* h, const spopt_grad* g, const
 static int validate_grad(const spopt_optimizer* h, const spopt_grad* g, const int32_t* ls,
                          int32_t t, hipStream_t s, const char* what) {
     const bool touched = g->format == SPOPT_FORMAT_CSR && g->csr.touched_rows != nullptr;
+    const bool per_row = row_last_step(h);
+    // last_step of (row, col): per coordinate row*cols + col; per row, row.  A
+    // COO's index is a row (width == cols) or a flattened coordinate (width 1).
+    LastStepView lv{ls, t, per_row ? 1 : h->cols, per_row ? 0 : 1, per_row ? 1 : 0};
     return validate_on_device(s, touched, what, [&](uint32_t* status) {
-        if (g->format == SPOPT_FORMAT_COO) return launch_check_coo(&g->coo, 1, ls, t, status, s);
-        return launch_check_csr(&g->csr, 1, ls, t, status, s);
+        if (g->format == SPOPT_FORMAT_COO) {
+            LastStepView cv = lv;
+            cv.ls_rs = per_row ? 1 : g->coo.width;
+            return launch_check_coo(&g->coo, 1, cv, status, s);
+        }
+        return launch_check_csr(&g->csr, 1, lv, status, s);
     });
 }
 
@@ -270,7 +291,8 @@ extern "C" int sparse_adam_step(spopt_t h, const spopt_grad* g, void* stream, ui
     a.lr_wd = c.lr * c.weight_decay;
     const int wd_kind = c.weight_decay == 0.0 ? kWdNone
                         : c.weight_decay_mode == SPOPT_WD_L2 ? kWdL2 : kWdDecoupled;
-    rc = launch_adam(h->p, h->m, h->v, h->ls, a, c.mode, wd_kind, g, h->rows, h->cols, s);
+    rc = launch_adam(h->p, h->m, h->v, h->ls, c.last_step_per_row != 0, a, c.mode, wd_kind, g,
+                     h->rows, h->cols, s);
     if (rc) return rc;
     h->t = t;
     return SPOPT_OK;

@@ -20,7 +20,8 @@ enum : uint32_t {
     kStatusNonFinite = 4u, // NaN or inf gradient value
     kStatusStep = 8u,      // last_step >= t on a touched coordinate
     kStatusTouched = 16u,  // touched-row list inconsistent with row_offsets
-    kStatusTimeout = 32u   // a bounded device-side wait gave up (a library bug)
+    kStatusTimeout = 32u,  // a bounded device-side wait gave up (a library bug)
+    kStatusPartial = 64u   // a partial row given to a table with one last_step per row
 };
 
 // ---------------------------------------------------------------- device ---
@@ -140,9 +141,19 @@ int device_status_check(uint32_t* d_status, hipStream_t s, bool check_touched,
 
 // Launchers shared between the sources.
 int launch_status_clear(uint32_t* d_status, int nwords, hipStream_t s);
-int launch_check_coo(const spopt_coo* c, int check_finite, const int32_t* ls, int32_t t,
+// last_step of the coordinate (row, col) is ls[row * ls_rs + col * ls_cs]:
+// (cols, 1) per coordinate, (1, 0) per row.  full_rows: a row with some but
+// not all of its columns sets kStatusPartial.
+struct LastStepView {
+    const int32_t* ls;
+    int32_t t;
+    int64_t ls_rs, ls_cs;
+    int full_rows;
+};
+
+int launch_check_coo(const spopt_coo* c, int check_finite, const LastStepView& lv,
                      uint32_t* status, hipStream_t s);
-int launch_check_csr(const spopt_csr* c, int check_finite, const int32_t* ls, int32_t t,
+int launch_check_csr(const spopt_csr* c, int check_finite, const LastStepView& lv,
                      uint32_t* status, hipStream_t s);
 
 // beta^gap for gap < kPowTable comes from a table built on the host with pow().
@@ -160,8 +171,9 @@ struct AdamScalars {
     const double* pow2;  // device [kPowTable]: beta2^k
     int32_t t;
 };
-int launch_adam(float* p, float* m, float* v, int32_t* ls, const AdamScalars& a, int mode,
-                int wd_kind, const spopt_grad* gr, int64_t rows, int64_t cols, hipStream_t s);
+int launch_adam(float* p, float* m, float* v, int32_t* ls, bool ls_per_row, const AdamScalars& a,
+                int mode, int wd_kind, const spopt_grad* gr, int64_t rows, int64_t cols,
+                hipStream_t s);
 int launch_sgd(float* p, float* b, double lr, double mu, double wd, const spopt_grad* gr,
                int64_t rows, int64_t cols, hipStream_t s);
 

@@ -252,8 +252,8 @@ __global__ __launch_bounds__(256) void k_csr_to_coo(const int32_t* __restrict__ 
 // COO canonical form, ranges, finiteness, and (for Adam) last_step < t.
 __global__ void k_check_coo(const int64_t* __restrict__ idx, const float* __restrict__ vals,
                             const int64_t* d_nnz, int64_t nnz_host, int64_t dim, int64_t width,
-                            int check_finite, const int32_t* __restrict__ ls, int32_t t,
-                            uint32_t* status) {
+                            int check_finite, LastStepView lv, uint32_t* status) {
+    const int32_t* __restrict__ ls = lv.ls;
     const int64_t nnz = d_nnz ? (*d_nnz < nnz_host ? *d_nnz : nnz_host) : nnz_host;
     uint32_t bad = 0;
     for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < nnz;
@@ -266,7 +266,7 @@ __global__ void k_check_coo(const int64_t* __restrict__ idx, const float* __rest
         if (k > 0 && idx[k - 1] >= i) bad |= kStatusNotCanon;
         for (int64_t c = 0; c < width; ++c) {
             if (check_finite && !finite_f(vals[k * width + c])) bad |= kStatusNonFinite;
-            if (ls && ls[i * width + c] >= t) bad |= kStatusStep;
+            if (ls && ls[i * lv.ls_rs + c * lv.ls_cs] >= lv.t) bad |= kStatusStep;
         }
     }
     if (bad) atomicOr(status, bad);
@@ -278,8 +278,8 @@ __global__ __launch_bounds__(256) void k_check_csr(const int32_t* __restrict__ r
                                                    const int32_t* __restrict__ ci,
                                                    const float* __restrict__ vals, int64_t rows,
                                                    int64_t cols, int check_finite,
-                                                   const int32_t* __restrict__ ls, int32_t t,
-                                                   uint32_t* status) {
+                                                   LastStepView lv, uint32_t* status) {
+    const int32_t* __restrict__ ls = lv.ls;
     const int lane = lane_id();
     const int64_t nw = ((int64_t)gridDim.x * blockDim.x) >> 6;
     uint32_t bad = 0;
@@ -306,6 +306,7 @@ __global__ __launch_bounds__(256) void k_check_csr(const int32_t* __restrict__ r
             const int st = read_lane(a, bit), en = read_lane(b, bit);
             const int64_t row = tile * kWave + bit;
             if (ci == nullptr && en - st != cols) bad |= kStatusNotCanon;
+            if (lv.full_rows && en - st != cols) bad |= kStatusPartial;
             for (int j = st + lane; j < en; j += kWave) {
                 const int64_t c = ci ? (int64_t)ci[j] : (int64_t)(j - st);
                 if (c < 0 || c >= cols) {
@@ -314,7 +315,7 @@ __global__ __launch_bounds__(256) void k_check_csr(const int32_t* __restrict__ r
                 }
                 if (ci && j > st && ci[j - 1] >= c) bad |= kStatusNotCanon;
                 if (check_finite && !finite_f(vals[j])) bad |= kStatusNonFinite;
-                if (ls && ls[row * cols + c] >= t) bad |= kStatusStep;
+                if (ls && ls[row * lv.ls_rs + c * lv.ls_cs] >= lv.t) bad |= kStatusStep;
             }
         }
     }
@@ -348,20 +349,18 @@ static unsigned grid_for(int64_t work, int64_t per_block, int64_t cap = 4096) {
     return (unsigned)(g < cap ? g : cap);
 }
 
-int launch_check_coo(const spopt_coo* c, int check_finite, const int32_t* ls, int32_t t,
+int launch_check_coo(const spopt_coo* c, int check_finite, const LastStepView& lv,
                      uint32_t* status, hipStream_t s) {
     k_check_coo<<<grid_for(c->nnz, 256), 256, 0, s>>>(c->indices, c->values, c->d_nnz, c->nnz,
-                                                      c->dim, c->width, check_finite, ls, t,
-                                                      status);
+                                                      c->dim, c->width, check_finite, lv, status);
     SPOPT_LAUNCHED();
     return SPOPT_OK;
 }
 
-int launch_check_csr(const spopt_csr* c, int check_finite, const int32_t* ls, int32_t t,
+int launch_check_csr(const spopt_csr* c, int check_finite, const LastStepView& lv,
                      uint32_t* status, hipStream_t s) {
     k_check_csr<<<grid_for(ceil_div(c->rows, kWave), 4), 256, 0, s>>>(
-        c->row_offsets, c->col_indices, c->values, c->rows, c->cols, check_finite, ls, t,
-        status);
+        c->row_offsets, c->col_indices, c->values, c->rows, c->cols, check_finite, lv, status);
     SPOPT_LAUNCHED();
     if (c->touched_rows) {
         k_check_touched<<<grid_for(c->n_touched, 256), 256, 0, s>>>(
@@ -407,7 +406,7 @@ extern "C" int csr_from_coo(const spopt_coo* in, int64_t rows, int64_t cols,
                     (long long)(in->nnz * in->width));
     if (flags & SPOPT_VALIDATE) {
         const int rc = validate_on_device(st, false, "csr_from_coo", [&](uint32_t* status) {
-            return launch_check_coo(in, 0, nullptr, 0, status, st);
+            return launch_check_coo(in, 0, LastStepView{nullptr, 0, 0, 0, 0}, status, st);
         });
         if (rc) return rc;
     }
@@ -464,7 +463,7 @@ extern "C" int csr_to_coo(const spopt_csr* in, int64_t* out_indices, float* out_
         return fail(SPOPT_EINVAL, "csr_to_coo: values requested but CSR has none");
     if (flags & SPOPT_VALIDATE) {
         const int rc = validate_on_device(st, false, "csr_to_coo", [&](uint32_t* status) {
-            return launch_check_csr(in, 0, nullptr, 0, status, st);
+            return launch_check_csr(in, 0, LastStepView{nullptr, 0, 0, 0, 0}, status, st);
         });
         if (rc) return rc;
     }

@@ -33,11 +33,17 @@ namespace spopt {
 
 // Per-coordinate ops.  A vector step is split into phases so that a kernel can
 // issue every load of a batch as straight-line code before it computes:
-//   load(i, r)      p, m, v (and last_step) of 4 coordinates,
-//   prep(r, x)      loads that depend on them (beta^gap from the table),
-//   compute(r, x, g), store(i, r).
-template <int MODE, int WD = kWdNone>
+//   load(i, row, r)   p, m, v (and last_step) of 4 coordinates of row `row`,
+//   prep(r, x)        loads that depend on them (beta^gap from the table),
+//   compute(r, x, g), store(i, row, r).
+// One coordinate at a time: rl = row_last(row) before any coordinate of the
+// row, scalar(i, rl, g) per coordinate, row_done(row) after them all.  With
+// one last_step per row (LSROW) the row's value is read once and written
+// once, so every coordinate of the row sees the value from before the step;
+// with one per coordinate, row_last and row_done do nothing.
+template <int MODE, int WD = kWdNone, bool LSROW = false>
 struct AdamOp {
+    static constexpr bool kLsRow = LSROW;
     float* __restrict__ p;
     float* __restrict__ m;
     float* __restrict__ v;
@@ -90,17 +96,26 @@ struct AdamOp {
         return gap < 0 ? 0 : (gap >= kPowTable ? kPowTable - 1 : gap);
     }
 
-    __device__ __forceinline__ void load(int64_t i, Vec& r) const {
+    __device__ __forceinline__ void load(int64_t i, int64_t row, Vec& r) const {
         r.p = *reinterpret_cast<const float4*>(p + i);
         r.m = *reinterpret_cast<const float4*>(m + i);
         r.v = *reinterpret_cast<const float4*>(v + i);
-        if (MODE == SPOPT_MODE_DORMANCY)
+        if (MODE == SPOPT_MODE_DORMANCY && LSROW) {
+            const int32_t l = ls[row];  // one address per row: a broadcast
+            r.ls = make_int4(l, l, l, l);
+        } else if (MODE == SPOPT_MODE_DORMANCY) {
             r.ls = *reinterpret_cast<const int4*>(ls + i);
-        else
+        } else {
             r.ls = make_int4(0, 0, 0, 0);
+        }
     }
     __device__ __forceinline__ void prep(const Vec& r, Aux& x) const {
-        if (MODE == SPOPT_MODE_DORMANCY) {
+        if (MODE == SPOPT_MODE_DORMANCY && LSROW) {
+            const int k = table_index(r.ls.x);
+            const double d1 = a.pow1[k], d2 = a.pow2[k];
+            x.d1[0] = x.d1[1] = x.d1[2] = x.d1[3] = d1;
+            x.d2[0] = x.d2[1] = x.d2[2] = x.d2[3] = d2;
+        } else if (MODE == SPOPT_MODE_DORMANCY) {
             const int i0 = table_index(r.ls.x), i1 = table_index(r.ls.y);
             const int i2 = table_index(r.ls.z), i3 = table_index(r.ls.w);
             x.d1[0] = a.pow1[i0]; x.d2[0] = a.pow2[i0];
@@ -115,15 +130,24 @@ struct AdamOp {
         coord(r.p.z, r.m.z, r.v.z, r.ls.z, x.d1[2], x.d2[2], g.z);
         coord(r.p.w, r.m.w, r.v.w, r.ls.w, x.d1[3], x.d2[3], g.w);
     }
-    __device__ __forceinline__ void store(int64_t i, const Vec& r) const {
+    __device__ __forceinline__ void store(int64_t i, int64_t row, const Vec& r) const {
         *reinterpret_cast<float4*>(p + i) = r.p;
         *reinterpret_cast<float4*>(m + i) = r.m;
         *reinterpret_cast<float4*>(v + i) = r.v;
-        *reinterpret_cast<int4*>(ls + i) = make_int4(a.t, a.t, a.t, a.t);
+        if (LSROW)
+            ls[row] = a.t;  // every lane of the row stores the same value
+        else
+            *reinterpret_cast<int4*>(ls + i) = make_int4(a.t, a.t, a.t, a.t);
     }
-    __device__ __forceinline__ void scalar(int64_t i, float g) const {
+    __device__ __forceinline__ int32_t row_last(int64_t row) const {
+        return LSROW ? ls[row] : 0;
+    }
+    __device__ __forceinline__ void row_done(int64_t row) const {
+        if (LSROW) ls[row] = a.t;
+    }
+    __device__ __forceinline__ void scalar(int64_t i, int32_t rl, float g) const {
         float pp = p[i], mm = m[i], vv = v[i];
-        const int32_t last = (MODE == SPOPT_MODE_DORMANCY) ? ls[i] : 0;
+        const int32_t last = (MODE != SPOPT_MODE_DORMANCY) ? 0 : (LSROW ? rl : ls[i]);
         double t1 = 1.0, t2 = 1.0;
         if (MODE == SPOPT_MODE_DORMANCY) {
             const int k = table_index(last);
@@ -134,7 +158,7 @@ struct AdamOp {
         p[i] = pp;
         m[i] = mm;
         v[i] = vv;
-        ls[i] = a.t;
+        if (!LSROW) ls[i] = a.t;
     }
 };
 
@@ -161,7 +185,10 @@ struct SgdOp {
             pp = (float)(p0 - lr * gg);
         }
     }
-    __device__ __forceinline__ void load(int64_t i, Vec& r) const {
+    static constexpr bool kLsRow = false;
+    __device__ __forceinline__ int32_t row_last(int64_t) const { return 0; }
+    __device__ __forceinline__ void row_done(int64_t) const {}
+    __device__ __forceinline__ void load(int64_t i, int64_t, Vec& r) const {
         r.p = *reinterpret_cast<const float4*>(p + i);
         if (MOM)
             r.b = *reinterpret_cast<const float4*>(b + i);
@@ -175,11 +202,11 @@ struct SgdOp {
         coord(r.p.z, r.b.z, g.z);
         coord(r.p.w, r.b.w, g.w);
     }
-    __device__ __forceinline__ void store(int64_t i, const Vec& r) const {
+    __device__ __forceinline__ void store(int64_t i, int64_t, const Vec& r) const {
         *reinterpret_cast<float4*>(p + i) = r.p;
         if (MOM) *reinterpret_cast<float4*>(b + i) = r.b;
     }
-    __device__ __forceinline__ void scalar(int64_t i, float g) const {
+    __device__ __forceinline__ void scalar(int64_t i, int32_t, float g) const {
         float pp = p[i], bb = MOM ? b[i] : 0.f;
         coord(pp, bb, g);
         p[i] = pp;
@@ -267,7 +294,7 @@ __global__ __launch_bounds__(256) void k_update_rows(Op op, Src src, const int64
                 act[it] = len[it] == cols && (st[it] & 3) == 0 && sl < nvec;
                 const int64_t off = act[it] ? row[it] * cols + 4 * sl : 0;
                 const int64_t goff = act[it] ? st[it] + 4 * sl : 0;
-                op.load(off, r[it]);
+                op.load(off, act[it] ? row[it] : 0, r[it]);
                 gv[it] = *reinterpret_cast<const float4*>(g + goff);
             }
 #pragma unroll
@@ -276,7 +303,7 @@ __global__ __launch_bounds__(256) void k_update_rows(Op op, Src src, const int64
             for (int it = 0; it < ITERS; ++it) {
                 if (act[it]) {
                     op.compute(r[it], x[it], gv[it]);
-                    op.store(row[it] * cols + 4 * sl, r[it]);
+                    op.store(row[it] * cols + 4 * sl, row[it], r[it]);
                 }
             }
             bool full[ITERS];
@@ -286,32 +313,41 @@ __global__ __launch_bounds__(256) void k_update_rows(Op op, Src src, const int64
             for (int it = 0; it < ITERS; ++it) {
                 if (full[it] || len[it] <= 0) continue;
                 const int64_t n = len[it] < cols ? len[it] : cols;
+                const int32_t rl = op.row_last(row[it]);
                 for (int64_t j = sl; j < n; j += LPR) {
                     const int64_t c = src.col(st[it], j);
-                    if ((uint64_t)c < (uint64_t)cols) op.scalar(row[it] * cols + c, g[st[it] + j]);
+                    if ((uint64_t)c < (uint64_t)cols)
+                        op.scalar(row[it] * cols + c, rl, g[st[it] + j]);
                 }
+                op.row_done(row[it]);
             }
         } else {
 #pragma unroll
             for (int it = 0; it < ITERS; ++it) {
                 if (len[it] <= 0) continue;
                 const int64_t base = row[it] * cols;
+                // One last_step per row: every lane reads it before any lane
+                // of the row writes it (the loads of the first pass below, or
+                // row_last), and it is written once the row is done.
+                const int32_t rl = op.row_last(row[it]);
                 if (vec_ok && len[it] == cols && (st[it] & 3) == 0) {
                     for (int64_t c4 = sl; c4 < nvec; c4 += LPR) {
                         typename Op::Vec r;
                         typename Op::Aux x;
-                        op.load(base + 4 * c4, r);
+                        op.load(base + 4 * c4, row[it], r);
+                        if constexpr (Op::kLsRow) r.ls = make_int4(rl, rl, rl, rl);
                         const float4 gv = *reinterpret_cast<const float4*>(g + st[it] + 4 * c4);
                         op.prep(r, x);
                         op.compute(r, x, gv);
-                        op.store(base + 4 * c4, r);
+                        op.store(base + 4 * c4, row[it], r);
                     }
                 } else {
                     const int64_t n = len[it] < cols ? len[it] : cols;
                     for (int64_t j = sl; j < n; j += LPR) {
                         const int64_t c = src.col(st[it], j);
-                        if ((uint64_t)c < (uint64_t)cols) op.scalar(base + c, g[st[it] + j]);
+                        if ((uint64_t)c < (uint64_t)cols) op.scalar(base + c, rl, g[st[it] + j]);
                     }
+                    op.row_done(row[it]);
                 }
             }
         }
@@ -342,10 +378,12 @@ __global__ __launch_bounds__(256) void k_update_csr_scan(Op op, const int32_t* _
             const int st = read_lane(a, bit), en = read_lane(b, bit);
             const int64_t row = tile * kWave + bit;
             const int64_t base = row * cols;
+            const int32_t rl = op.row_last(row);
             for (int j = st + lane; j < en && j - st < cols; j += kWave) {
                 const int64_t c = ci ? (int64_t)ci[j] : (int64_t)(j - st);
-                if ((uint64_t)c < (uint64_t)cols) op.scalar(base + c, g[j]);
+                if ((uint64_t)c < (uint64_t)cols) op.scalar(base + c, rl, g[j]);
             }
+            op.row_done(row);
         }
     }
 }
@@ -360,7 +398,12 @@ __global__ __launch_bounds__(256) void k_update_coo_scalar(Op op, const int64_t*
     for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < count;
          k += (int64_t)gridDim.x * blockDim.x) {
         const int64_t i = idx[k];
-        if ((uint64_t)i < (uint64_t)dim) op.scalar(i, g[k]);
+        // A table with one last_step per row reaches this kernel only with one
+        // column, where row and coordinate coincide.
+        if ((uint64_t)i < (uint64_t)dim) {
+            op.scalar(i, op.row_last(i), g[k]);
+            op.row_done(i);
+        }
     }
 }
 
@@ -383,8 +426,8 @@ template <class Op>
 struct RowBatch {
     static constexpr int kIters = 4;  // full rows per sub-group in flight
 };
-template <int MODE, int WD>
-struct RowBatch<AdamOp<MODE, WD>> {
+template <int MODE, int WD, bool LSROW>
+struct RowBatch<AdamOp<MODE, WD, LSROW>> {
     static constexpr int kIters = 2;  // Adam holds more state per row in registers
 };
 
@@ -450,24 +493,34 @@ static int launch_update(const Op& op, bool state_aligned, const spopt_grad* gr,
     return SPOPT_OK;
 }
 
-template <int MODE>
+template <int MODE, bool LSROW>
 static int launch_adam_mode(float* p, float* m, float* v, int32_t* ls, const AdamScalars& a,
                             int wd_kind, bool al, const spopt_grad* gr, int64_t rows, int64_t cols,
                             hipStream_t s) {
     if (wd_kind == kWdL2)
-        return launch_update(AdamOp<MODE, kWdL2>{p, m, v, ls, a}, al, gr, rows, cols, s);
+        return launch_update(AdamOp<MODE, kWdL2, LSROW>{p, m, v, ls, a}, al, gr, rows, cols, s);
     if (wd_kind == kWdDecoupled)
-        return launch_update(AdamOp<MODE, kWdDecoupled>{p, m, v, ls, a}, al, gr, rows, cols, s);
-    return launch_update(AdamOp<MODE, kWdNone>{p, m, v, ls, a}, al, gr, rows, cols, s);
+        return launch_update(AdamOp<MODE, kWdDecoupled, LSROW>{p, m, v, ls, a}, al, gr, rows,
+                             cols, s);
+    return launch_update(AdamOp<MODE, kWdNone, LSROW>{p, m, v, ls, a}, al, gr, rows, cols, s);
 }
 
-int launch_adam(float* p, float* m, float* v, int32_t* ls, const AdamScalars& a, int mode,
-                int wd_kind, const spopt_grad* gr, int64_t rows, int64_t cols, hipStream_t s) {
-    const bool al = aligned16(p) && aligned16(m) && aligned16(v) && aligned16(ls);
+int launch_adam(float* p, float* m, float* v, int32_t* ls, bool ls_per_row, const AdamScalars& a,
+                int mode, int wd_kind, const spopt_grad* gr, int64_t rows, int64_t cols,
+                hipStream_t s) {
+    // With one last_step per row, only p, m and v are moved 16 bytes at a time.
+    const bool al = aligned16(p) && aligned16(m) && aligned16(v) && (ls_per_row || aligned16(ls));
+    if (ls_per_row) {
+        if (mode == SPOPT_MODE_DORMANCY)
+            return launch_adam_mode<SPOPT_MODE_DORMANCY, true>(p, m, v, ls, a, wd_kind, al, gr,
+                                                               rows, cols, s);
+        return launch_adam_mode<SPOPT_MODE_LAZY, true>(p, m, v, ls, a, wd_kind, al, gr, rows, cols,
+                                                       s);
+    }
     if (mode == SPOPT_MODE_DORMANCY)
-        return launch_adam_mode<SPOPT_MODE_DORMANCY>(p, m, v, ls, a, wd_kind, al, gr, rows, cols,
-                                                     s);
-    return launch_adam_mode<SPOPT_MODE_LAZY>(p, m, v, ls, a, wd_kind, al, gr, rows, cols, s);
+        return launch_adam_mode<SPOPT_MODE_DORMANCY, false>(p, m, v, ls, a, wd_kind, al, gr, rows,
+                                                            cols, s);
+    return launch_adam_mode<SPOPT_MODE_LAZY, false>(p, m, v, ls, a, wd_kind, al, gr, rows, cols, s);
 }
 
 int launch_sgd(float* p, float* b, double lr, double mu, double wd, const spopt_grad* gr,
