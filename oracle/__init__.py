@@ -80,6 +80,7 @@ def lib():
         L.orc_adam_coo_f32.argtypes = [P, P, P, P, I64, I64, P, P, I64, I64, P, C.c_int]
         L.orc_adam_csr_f32.argtypes = [P, P, P, P, I64, I64, P, P, P, I64, P, C.c_int]
         L.orc_adam_rows_csr_f32.argtypes = [P, P, P, P, I64, I64, P, P, P, I64, P, C.c_int]
+        L.orc_read_rows.argtypes = [P, I64, I64, P, I64, P, C.c_int]
         L.orc_adam_coo_f64.argtypes = [P, P, P, P, I64, P, P, I64, I64, P]
         L.orc_sgd_coo_f32.argtypes = [P, P, I64, I64, P, P, I64, P, C.c_int]
         L.orc_sgd_csr_f32.argtypes = [P, P, I64, I64, P, P, P, P, C.c_int]
@@ -157,6 +158,19 @@ def csr_to_coo(row_offsets, col_indices, vals, rows: int, cols: int):
 # --------------------------------------------------------------------------
 # Optimizers (float32 state, double arithmetic)
 # --------------------------------------------------------------------------
+
+def read_rows(params, idx, check_finite=False):
+    """Forward gather of table rows (duplicates allowed)."""
+    params = _arr(params, np.float32)
+    rows = params.shape[0]
+    cols = params.shape[1] if params.ndim == 2 else 1
+    idx = _arr(idx, np.int64).reshape(-1)
+    out = np.zeros((idx.size, cols), np.float32)
+    rc = lib().orc_read_rows(_p(params), rows, cols, _p(idx), idx.size, _p(out),
+                             CHECK_FINITE if check_finite else 0)
+    _check(rc, "read_rows")
+    return out
+
 
 class Adam:
     """Sparse / lazy Adam over a dense (rows x cols) float32 state.

@@ -376,6 +376,26 @@ int orc_adam_rows_csr_f32(float* p, float* m, float* v, int32_t* ls, int64_t row
     return ORC_OK;
 }
 
+/* ---- forward gather ------------------------------------------------------ */
+
+/* DiskSparseAdam README, API reference, read_rows(indices): the rows of the
+ * current table for the given indices, with the indices validated and
+ * corrupted (non-finite) rows refused. */
+int orc_read_rows(const float* params, int64_t rows, int64_t cols, const int64_t* idx, int64_t n,
+                  float* out, int flags) {
+    if (rows < 1 || cols < 1 || n < 0 || params == NULL) return ORC_EINVAL;
+    if (n > 0 && (idx == NULL || out == NULL)) return ORC_EINVAL;
+    for (int64_t k = 0; k < n; ++k) {
+        if (idx[k] < 0 || idx[k] >= rows) return ORC_ERANGE;
+        if (flags & ORC_CHECK_FINITE)
+            for (int64_t c = 0; c < cols; ++c)
+                if (!isfinite(params[idx[k] * cols + c])) return ORC_ENONFINITE;
+    }
+    for (int64_t k = 0; k < n; ++k)
+        memcpy(out + k * cols, params + idx[k] * cols, sizeof(float) * (size_t)cols);
+    return ORC_OK;
+}
+
 /* ---- Adam, double storage (for the pins) -------------------------------- */
 
 int orc_adam_coo_f64(double* p, double* m, double* v, int32_t* ls, int64_t dim,

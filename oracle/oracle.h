@@ -80,6 +80,13 @@ int orc_adam_coo_f64(double* p, double* m, double* v, int32_t* ls, int64_t dim,
                      const int64_t* idx, const double* g, int64_t nnz, int64_t t,
                      const orc_adam_cfg* cfg);
 
+/* Forward gather: out[k, :] = params[idx[k], :] for k < n, duplicates
+ * allowed.  ORC_ERANGE for an index outside [0, rows); with ORC_CHECK_FINITE,
+ * ORC_ENONFINITE when a gathered row holds a NaN or inf.  Nothing is written
+ * on error. */
+int orc_read_rows(const float* params, int64_t rows, int64_t cols, const int64_t* idx, int64_t n,
+                  float* out, int flags);
+
 /* One SGD step on the touched coordinates (b may be NULL when momentum == 0). */
 int orc_sgd_coo_f32(float* p, float* b, int64_t dim, int64_t width, const int64_t* idx,
                     const float* g, int64_t nnz, const orc_sgd_cfg* cfg, int flags);
