@@ -16,7 +16,8 @@ measured alongside as the practical bandwidth ceiling; breakdown_us = p10 /
 median / p90 of each call and of the whole step from a second, separately
 timed pass over the same inputs; cold = the update again in a third pass that
 writes a 512 MB buffer before every step, so the state rows come from HBM
-rather than the 256 MB last-level cache; cpu_baseline = the CPU oracle on a
+rather than the 256 MB last-level cache; read_rows = the forward gather of each
+step's lookups, timed in a pass of its own; cpu_baseline = the CPU oracle on a
 bounded sample of the same workload.
 
 Events are created through the HIP runtime with hipEventDisableSystemFence:
@@ -340,6 +341,19 @@ def main() -> int:
     del scrub
     copy_gbs = device_copy_gbs(torch, stream)
 
+    # Forward gather (not part of the value): read_rows of each step's lookups.
+    gathered = torch.empty((n, Cc), dtype=torch.float32, device="cuda")
+    rev = HipEvents(2 * K)
+    torch.cuda._sleep(cycles)
+    for k, s in enumerate(range(W, W + K)):
+        rev.record(2 * k, stream)
+        L.read_rows(params, ids_d[s], out=gathered, stream=stream)
+        rev.record(2 * k + 1, stream)
+    torch.cuda.synchronize()
+    rr = np.array([rev.ms(2 * k, 2 * k + 1) for k in range(K)])
+    rev.close()
+    rr_bytes = n * (8 + 2 * 4 * Cc)
+
     U = nuniq.cpu().numpy()[W:]
     coords = int(U.sum()) * Cc
     if per_row:
@@ -383,6 +397,9 @@ def main() -> int:
                               "mean_us": float(upd_cold.mean() * 1e3), "us": pcts(upd_cold)}},
         "breakdown_us": {"coo_from_lookups": pcts(canon_t), "csr_from_coo": pcts(csr_t),
                          "sparse_adam_step": pcts(upd_b), "step": pcts(step_t)},
+        "read_rows": {"us": pcts(rr), "lookups": n,
+                      "achieved_GBs": float((rr_bytes / (rr * 1e-3)).mean() / 1e9),
+                      "bytes_per_lookup": 8 + 2 * 4 * Cc},
     }
     if args.cpu_seconds > 0:
         log("cpu baseline (oracle)")

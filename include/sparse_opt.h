@@ -272,6 +272,22 @@ SPOPT_API int sparse_adam_step(spopt_t h, const spopt_grad* g, void* stream, uin
  * error rules as sparse_adam_step).  t advances as well. */
 SPOPT_API int sparse_sgd_step(spopt_t h, const spopt_grad* g, void* stream, uint32_t flags);
 
+/* ---- forward gather ----------------------------------------------------- */
+
+/* DiskSparseAdam README, API reference, read_rows(indices): the current rows of
+ * a table for a batch of lookups.  out[k*cols + j] = params[indices[k]*cols + j]
+ * for k < n, j < cols; duplicates allowed.
+ * params: device, rows x cols float32 (e.g. the params of an optimizer handle);
+ * indices: device int64[n]; out: device float32[n x cols], caller-owned.
+ * Stream-ordered after any step on the same stream, so it reads the updated
+ * table.  Trusted mode: an index outside [0, rows) gives a row of zeros and
+ * nothing outside the table is read.  SPOPT_VALIDATE: SPOPT_ERANGE for such an
+ * index and SPOPT_ENONFINITE for a gathered row holding a NaN or inf (a
+ * corrupted row), nothing written.  n == 0 does nothing.
+ * Errors: SPOPT_EINVAL (NULL pointers, rows or cols < 1, n < 0). */
+SPOPT_API int read_rows(const float* params, int64_t rows, int64_t cols, const int64_t* indices,
+                        int64_t n, float* out, void* stream, uint32_t flags);
+
 #ifdef __cplusplus
 }
 #endif

@@ -23,7 +23,8 @@ from ._lib import (FORMAT_COO, FORMAT_CSR, KIND_ADAM, KIND_SGD, MODE_DORMANCY, M
 
 __all__ = ["coo_from_lookups", "csr_from_coo", "csr_to_coo", "sparse_opt_workspace_size",
            "sparse_opt_create", "sparse_adam_step", "sparse_sgd_step", "CooGradient",
-           "CsrGradient", "SparseAdam", "SparseSgd", "SparseOptError", "TRUSTED", "VALIDATE"]
+           "CsrGradient", "SparseAdam", "SparseSgd", "SparseOptError", "TRUSTED", "VALIDATE",
+           "read_rows"]
 
 
 def _stream(stream) -> int:
@@ -264,6 +265,22 @@ def sparse_sgd_step(h: _Handle, grad, *, stream=None, validate: bool = False) ->
     check(h._L.sparse_sgd_step(h._h, C.byref(g), _stream(stream), _flags(validate)))
 
 
+def read_rows(params: torch.Tensor, indices: torch.Tensor, *, out=None, stream=None,
+              validate: bool = False) -> torch.Tensor:
+    """Forward gather: out[k] = params[indices[k]] (rows of a 2-D float32 table)."""
+    rows = params.shape[0]
+    cols = params.shape[1] if params.dim() == 2 else 1
+    _need(params, torch.float32, "params", rows * cols)
+    _need(indices, torch.int64, "indices")
+    n = indices.numel()
+    if out is None:
+        out = torch.empty((n, cols), dtype=torch.float32, device=params.device)
+    _need(out, torch.float32, "out", n * cols)
+    check(_lib.lib().read_rows(_ptr(params), rows, cols, _ptr(indices), n, _ptr(out),
+                               _stream(stream), _flags(validate)))
+    return out
+
+
 class SparseAdam:
     """Sparse / lazy Adam over a (rows x cols) float32 table that this object
     allocates on the device (m = v = 0, last_step = 0)."""
@@ -293,6 +310,10 @@ class SparseAdam:
 
     def step(self, grad, *, stream=None, validate=False) -> None:
         sparse_adam_step(self.handle, grad, stream=stream, validate=validate)
+
+    def read_rows(self, indices: torch.Tensor, *, out=None, stream=None, validate=False):
+        """The current rows of the table for a batch of lookups (forward pass)."""
+        return read_rows(self.params, indices, out=out, stream=stream, validate=validate)
 
 
 class SparseSgd:

@@ -92,6 +92,8 @@ def lib() -> C.CDLL:
         L.sparse_adam_step.argtypes = [P, C.POINTER(Grad), P, U32]
         L.sparse_adam_step.restype = C.c_int
         L.sparse_sgd_step.argtypes = [P, C.POINTER(Grad), P, U32]
+        L.read_rows.restype = C.c_int
+        L.read_rows.argtypes = [P, I64, I64, P, I64, P, P, U32]
         L.sparse_sgd_step.restype = C.c_int
         _lib = L
     return _lib
@@ -104,4 +106,4 @@ def check(rc: int) -> None:
 
 EXPORTED = ("sparse_opt_create", "sparse_opt_destroy", "sparse_opt_get_step", "sparse_opt_set_step",
             "sparse_opt_last_error", "sparse_opt_workspace_size", "coo_from_lookups",
-            "csr_from_coo", "csr_to_coo", "sparse_adam_step", "sparse_sgd_step")
+            "csr_from_coo", "csr_to_coo", "sparse_adam_step", "sparse_sgd_step", "read_rows")
