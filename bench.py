@@ -84,6 +84,8 @@ def parse():
                     help="only run a plain 1 GiB device copy (for scaling HBM counters)")
     ap.add_argument("--last-step-per-row", action="store_true",
                     help="keep one last_step per table row instead of one per coordinate")
+    ap.add_argument("--host-state", action="store_true",
+                    help="keep the table and its state in mapped pinned host memory")
     return ap.parse_args()
 
 
@@ -170,6 +172,27 @@ def device_copy_gbs(torch, stream) -> float:
     return 2.0 * 4 * n / (best * 1e-3) / 1e9
 
 
+def host_link_gbs(torch, stream) -> dict:
+    """Best of 3 copies of 1 GiB between pinned host memory and the device, each
+    direction, in GB/s: the host link's practical rate."""
+    n = 1 << 28
+    h = torch.ones(n, dtype=torch.float32).pin_memory()
+    d = torch.empty(n, dtype=torch.float32, device="cuda")
+    ev = HipEvents(2)
+    out = {}
+    for name, dst, src in (("host_to_device", d, h), ("device_to_host", h, d)):
+        best = float("inf")
+        for _ in range(3):
+            ev.record(0, stream)
+            dst.copy_(src, non_blocking=True)
+            ev.record(1, stream)
+            torch.cuda.synchronize()
+            best = min(best, ev.ms(0, 1))
+        out[name] = 4.0 * n / (best * 1e-3) / 1e9
+    ev.close()
+    return out
+
+
 def pcts(x_ms) -> dict:
     """p10 / median / p90 of per-launch milliseconds, in microseconds."""
     import numpy as np
@@ -249,10 +272,15 @@ def main() -> int:
 
     log(f"initial table {R}x{Cc} float32 (N(0, {w.init_std}))")
     host_p0 = synth.init_params(w)
-    params = torch.from_numpy(host_p0).to("cuda")
     per_row = args.last_step_per_row
-    opt = L.SparseAdam(params, lr=h["lr"], beta1=h["beta1"], beta2=h["beta2"], eps=h["eps"],
-                       mode=w.mode, last_step_per_row=per_row)
+    akw = dict(lr=h["lr"], beta1=h["beta1"], beta2=h["beta2"], eps=h["eps"], mode=w.mode,
+               last_step_per_row=per_row)
+    if args.host_state:
+        log("table and state in mapped pinned host memory")
+        opt = L.SparseAdam.host_resident(host_p0, **akw)
+    else:
+        opt = L.SparseAdam(torch.from_numpy(host_p0).to("cuda"), **akw)
+    params = opt.params
     log(f"inputs of {W + K} steps ({n} lookups each)")
     batches = synth.lookups_many(w, range(W + K))
     ids_d = [torch.from_numpy(i).to("cuda") for i, _ in batches]
@@ -363,7 +391,7 @@ def main() -> int:
     achieved = float((upd_bytes / (upd * 1e-3)).mean() / 1e9)
     cold_achieved = float((upd_bytes / (upd_cold * 1e-3)).mean() / 1e9)
     traffic = None
-    if not per_row and sources_sha256() == UPDATE_TRAFFIC["sources_sha256"]:
+    if not per_row and not args.host_state and sources_sha256() == UPDATE_TRAFFIC["sources_sha256"]:
         traffic = UPDATE_TRAFFIC["fetch_bytes"] + UPDATE_TRAFFIC["write_bytes"]
 
     result = {
@@ -380,7 +408,8 @@ def main() -> int:
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "rows": R, "cols": Cc, "lookups_per_step": n,
-                   "zipf_s": w.zipf_s, "mode": w.mode, "state": "p,m,v float32 + last_step int32 per " + ("row" if per_row else "coordinate"),
+                   "zipf_s": w.zipf_s, "mode": w.mode, "state": "p,m,v float32 + last_step int32 per " + ("row" if per_row else "coordinate")
+                   + (", in mapped pinned host memory" if args.host_state else ", in HBM"),
                    "mean_unique_rows": float(U.mean())},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
@@ -401,6 +430,15 @@ def main() -> int:
                       "achieved_GBs": float((rr_bytes / (rr * 1e-3)).mean() / 1e9),
                       "bytes_per_lookup": 8 + 2 * 4 * Cc},
     }
+    if args.host_state:
+        # The state crosses the host link, not HBM: the roofline that bounds the
+        # update is the link's, measured here with plain pinned copies.
+        link = host_link_gbs(torch, stream)
+        result["roofline"]["bound"] = "host link"
+        result["roofline"]["peak"] = link["host_to_device"] + link["device_to_host"]
+        result["roofline"]["frac"] = achieved / result["roofline"]["peak"]
+        result["roofline"]["host_link_copy_GBs"] = link
+        result["roofline"]["peak_note"] = "sum of the measured pinned copy rates, each direction"
     if args.cpu_seconds > 0:
         log("cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(w, host_p0, batches, args.cpu_seconds, per_row)

@@ -65,7 +65,8 @@ typedef enum spopt_status {
     SPOPT_ENONFINITE = -5,  /* a gradient value is NaN or infinite (SPOPT_VALIDATE) */
     SPOPT_EOVERFLOW = -6,   /* a count does not fit its index type */
     SPOPT_EWORKSPACE = -7,  /* workspace missing or too small */
-    SPOPT_EDEVICE = -8      /* a HIP runtime call failed */
+    SPOPT_EDEVICE = -8,     /* a HIP runtime call failed */
+    SPOPT_ENOMEM = -9       /* an allocation the call was asked to make failed */
 } spopt_status;
 
 /* ---- flags -------------------------------------------------------------- */
@@ -194,6 +195,27 @@ SPOPT_API int sparse_opt_set_step(spopt_t h, int64_t t);
 SPOPT_API const char* sparse_opt_last_error(void);
 
 /* ---- canonicalisation --------------------------------------------------- */
+
+/* ---- host-resident state ------------------------------------------------ */
+
+/* State for tables larger than device memory (the DiskSparseAdam README keeps
+ * w, m, v and its step counters out of core and moves only the rows a batch
+ * touches).  Here the state lives in pinned host memory mapped into the
+ * device's address space; the step kernels then read and write, over the
+ * host link, only the touched rows.  Pass the device pointers to
+ * sparse_opt_create and read_rows as for device memory; the host pointers
+ * are for the caller (initial values, checkpoints), and the state they show
+ * is current after the stream has been synchronised.
+ * sparse_opt_host_alloc: `bytes` of pinned, mapped host memory, zero-filled;
+ * *host_ptr for the host, *device_ptr for kernels.  The caller owns it and
+ * frees it with sparse_opt_host_free (after the last use on any stream).
+ * Errors: SPOPT_EINVAL (NULL outputs, bytes == 0), SPOPT_ENOMEM.
+ * sparse_opt_host_device_pointer: the device address of pinned host memory
+ * allocated elsewhere (mapped pinned allocations only); SPOPT_EINVAL when the
+ * runtime has no device mapping for host_ptr. */
+SPOPT_API int sparse_opt_host_alloc(size_t bytes, void** host_ptr, void** device_ptr);
+SPOPT_API void sparse_opt_host_free(void* host_ptr);
+SPOPT_API int sparse_opt_host_device_pointer(void* host_ptr, void** device_ptr);
 
 /* Bytes of device workspace coo_from_lookups needs for n lookups of `width`
  * values over keys in [0, key_space).  SPOPT_EINVAL for n < 0, width < 1,

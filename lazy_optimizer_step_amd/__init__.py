@@ -15,6 +15,7 @@ from __future__ import annotations
 import ctypes as C
 from dataclasses import dataclass
 
+import numpy as np
 import torch
 
 from . import _lib
@@ -24,7 +25,7 @@ from ._lib import (FORMAT_COO, FORMAT_CSR, KIND_ADAM, KIND_SGD, MODE_DORMANCY, M
 __all__ = ["coo_from_lookups", "csr_from_coo", "csr_to_coo", "sparse_opt_workspace_size",
            "sparse_opt_create", "sparse_adam_step", "sparse_sgd_step", "CooGradient",
            "CsrGradient", "SparseAdam", "SparseSgd", "SparseOptError", "TRUSTED", "VALIDATE",
-           "read_rows"]
+           "read_rows", "HostArray"]
 
 
 def _stream(stream) -> int:
@@ -35,11 +36,59 @@ def _stream(stream) -> int:
     return int(stream)
 
 
+class HostArray:
+    """Pinned host memory mapped into the device's address space, for state of
+    tables larger than device memory.  ``numpy()`` is the host view (current
+    after the stream is synchronised); the library's kernels use the device
+    address.  Zero-filled at allocation; freed when the object goes."""
+
+    _NP = {torch.float32: np.float32, torch.int32: np.int32}
+
+    def __init__(self, shape, dtype=torch.float32):
+        import ctypes as C
+
+        self.shape = tuple(int(x) for x in shape)
+        self.dtype = dtype
+        n = 1
+        for x in self.shape:
+            n *= x
+        self._numel = n
+        nbytes = n * torch.tensor([], dtype=dtype).element_size()
+        h, d = C.c_void_p(), C.c_void_p()
+        check(_lib.lib().sparse_opt_host_alloc(max(nbytes, 1), C.byref(h), C.byref(d)))
+        self._host, self._dev = h.value, d.value
+        ct = C.c_float if dtype == torch.float32 else C.c_int32
+        self._array = np.ctypeslib.as_array((ct * max(n, 1)).from_address(self._host))[:n]
+        self._array = self._array.reshape(self.shape)
+
+    def numpy(self) -> np.ndarray:
+        return self._array
+
+    def numel(self) -> int:
+        return self._numel
+
+    def data_ptr(self) -> int:
+        return self._dev
+
+    def __del__(self):
+        host = getattr(self, "_host", None)
+        if host:
+            self._array = None
+            _lib.lib().sparse_opt_host_free(host)
+            self._host = None
+
+
 def _ptr(t) -> int | None:
     return None if t is None else t.data_ptr()
 
 
 def _need(t, dtype, name, numel=None):
+    if isinstance(t, HostArray):
+        if t.dtype != dtype:
+            raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+        if numel is not None and t.numel() < numel:
+            raise ValueError(f"{name} holds {t.numel()} elements, needs {numel}")
+        return t
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.dtype != dtype:
@@ -269,12 +318,12 @@ def read_rows(params: torch.Tensor, indices: torch.Tensor, *, out=None, stream=N
               validate: bool = False) -> torch.Tensor:
     """Forward gather: out[k] = params[indices[k]] (rows of a 2-D float32 table)."""
     rows = params.shape[0]
-    cols = params.shape[1] if params.dim() == 2 else 1
+    cols = params.shape[1] if len(params.shape) == 2 else 1
     _need(params, torch.float32, "params", rows * cols)
     _need(indices, torch.int64, "indices")
     n = indices.numel()
     if out is None:
-        out = torch.empty((n, cols), dtype=torch.float32, device=params.device)
+        out = torch.empty((n, cols), dtype=torch.float32, device=indices.device)
     _need(out, torch.float32, "out", n * cols)
     check(_lib.lib().read_rows(_ptr(params), rows, cols, _ptr(indices), n, _ptr(out),
                                _stream(stream), _flags(validate)))
@@ -288,20 +337,28 @@ class SparseAdam:
     def __init__(self, params: torch.Tensor, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8,
                  mode="dormancy", weight_decay=0.0, weight_decay_mode="l2",
                  last_step_per_row=False):
-        if weight_decay_mode not in ("l2", "decoupled"):
-            raise ValueError(f"weight_decay_mode {weight_decay_mode!r}: 'l2' or 'decoupled'")
         self.params = params
-        self.rows = params.shape[0]
-        self.cols = params.shape[1] if params.dim() == 2 else 1
+        rows = params.shape[0]
+        cols = params.shape[1] if params.dim() == 2 else 1
         self.m = torch.zeros_like(params)
         self.v = torch.zeros_like(params)
-        shape = (self.rows,) if last_step_per_row else params.shape
+        shape = (rows,) if last_step_per_row else params.shape
         self.last_step = torch.zeros(shape, dtype=torch.int32, device=params.device)
+        self._init_handle(rows, cols, lr=lr, beta1=beta1, beta2=beta2, eps=eps, mode=mode,
+                          weight_decay=weight_decay, weight_decay_mode=weight_decay_mode,
+                          last_step_per_row=last_step_per_row)
+
+    def _init_handle(self, rows, cols, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8,
+                     mode="dormancy", weight_decay=0.0, weight_decay_mode="l2",
+                     last_step_per_row=False):
+        if weight_decay_mode not in ("l2", "decoupled"):
+            raise ValueError(f"weight_decay_mode {weight_decay_mode!r}: 'l2' or 'decoupled'")
+        self.rows, self.cols = rows, cols
         cfg = _lib.AdamConfig(lr, beta1, beta2, eps,
                               MODE_DORMANCY if mode == "dormancy" else MODE_LAZY, weight_decay,
                               _lib.WD_DECOUPLED if weight_decay_mode == "decoupled" else _lib.WD_L2,
                               1 if last_step_per_row else 0)
-        self.handle = sparse_opt_create(KIND_ADAM, cfg, self.rows, self.cols, params, self.m, self.v,
+        self.handle = sparse_opt_create(KIND_ADAM, cfg, rows, cols, self.params, self.m, self.v,
                                         self.last_step)
 
     @property
@@ -314,6 +371,26 @@ class SparseAdam:
     def read_rows(self, indices: torch.Tensor, *, out=None, stream=None, validate=False):
         """The current rows of the table for a batch of lookups (forward pass)."""
         return read_rows(self.params, indices, out=out, stream=stream, validate=validate)
+
+    @classmethod
+    def host_resident(cls, params_init, **kw) -> "SparseAdam":
+        """Adam whose table and state live in mapped pinned host memory: only the
+        touched rows cross the host link on each step.  params_init: a (rows x
+        cols) array of initial values, copied in.  Gradients and the
+        canonicalisation stay in device memory."""
+        p0 = np.ascontiguousarray(np.asarray(params_init, dtype=np.float32))
+        if p0.ndim == 1:
+            p0 = p0.reshape(-1, 1)
+        self = cls.__new__(cls)
+        rows, cols = p0.shape
+        per_row = kw.get("last_step_per_row", False)
+        self.params = HostArray((rows, cols))
+        self.params.numpy()[...] = p0
+        self.m = HostArray((rows, cols))
+        self.v = HostArray((rows, cols))
+        self.last_step = HostArray((rows,) if per_row else (rows, cols), torch.int32)
+        self._init_handle(rows, cols, **kw)
+        return self
 
 
 class SparseSgd:

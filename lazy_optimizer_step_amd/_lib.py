@@ -13,11 +13,11 @@ import torch  # noqa: F401  (loads the process's HIP runtime before the library)
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsparseopt.so")
 
-OK, EINVAL, ERANGE, ENOTCANON, ESHAPE, ENONFINITE, EOVERFLOW, EWORKSPACE, EDEVICE = (
-    0, -1, -2, -3, -4, -5, -6, -7, -8)
+OK, EINVAL, ERANGE, ENOTCANON, ESHAPE, ENONFINITE, EOVERFLOW, EWORKSPACE, EDEVICE, ENOMEM = (
+    0, -1, -2, -3, -4, -5, -6, -7, -8, -9)
 ERROR_NAMES = {OK: "OK", EINVAL: "EINVAL", ERANGE: "ERANGE", ENOTCANON: "ENOTCANON",
                ESHAPE: "ESHAPE", ENONFINITE: "ENONFINITE", EOVERFLOW: "EOVERFLOW",
-               EWORKSPACE: "EWORKSPACE", EDEVICE: "EDEVICE"}
+               EWORKSPACE: "EWORKSPACE", EDEVICE: "EDEVICE", ENOMEM: "ENOMEM"}
 
 TRUSTED, VALIDATE = 0, 1
 KIND_ADAM, KIND_SGD = 0, 1
@@ -94,6 +94,12 @@ def lib() -> C.CDLL:
         L.sparse_sgd_step.argtypes = [P, C.POINTER(Grad), P, U32]
         L.read_rows.restype = C.c_int
         L.read_rows.argtypes = [P, I64, I64, P, I64, P, P, U32]
+        L.sparse_opt_host_alloc.restype = C.c_int
+        L.sparse_opt_host_alloc.argtypes = [C.c_size_t, C.POINTER(P), C.POINTER(P)]
+        L.sparse_opt_host_free.restype = None
+        L.sparse_opt_host_free.argtypes = [P]
+        L.sparse_opt_host_device_pointer.restype = C.c_int
+        L.sparse_opt_host_device_pointer.argtypes = [P, C.POINTER(P)]
         L.sparse_sgd_step.restype = C.c_int
         _lib = L
     return _lib
@@ -106,4 +112,5 @@ def check(rc: int) -> None:
 
 EXPORTED = ("sparse_opt_create", "sparse_opt_destroy", "sparse_opt_get_step", "sparse_opt_set_step",
             "sparse_opt_last_error", "sparse_opt_workspace_size", "coo_from_lookups",
-            "csr_from_coo", "csr_to_coo", "sparse_adam_step", "sparse_sgd_step", "read_rows")
+            "csr_from_coo", "csr_to_coo", "sparse_adam_step", "sparse_sgd_step", "read_rows",
+            "sparse_opt_host_alloc", "sparse_opt_host_free", "sparse_opt_host_device_pointer")

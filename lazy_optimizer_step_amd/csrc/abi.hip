@@ -130,6 +130,43 @@ static int check_sgd_config(const spopt_sgd_config* c) {
 
 extern "C" const char* sparse_opt_last_error(void) { return g_err; }
 
+extern "C" int sparse_opt_host_alloc(size_t bytes, void** host_ptr, void** device_ptr) {
+    if (host_ptr == nullptr || device_ptr == nullptr || bytes == 0)
+        return fail(SPOPT_EINVAL, "host_alloc: NULL output or zero size");
+    void* h = nullptr;
+    if (hipHostMalloc(&h, bytes, hipHostMallocMapped) != hipSuccess || h == nullptr) {
+        (void)hipGetLastError();
+        return fail(SPOPT_ENOMEM, "host_alloc: %zu bytes of pinned host memory", bytes);
+    }
+    void* d = nullptr;
+    if (hipHostGetDevicePointer(&d, h, 0) != hipSuccess || d == nullptr) {
+        (void)hipGetLastError();
+        (void)hipHostFree(h);
+        return fail(SPOPT_ENOMEM, "host_alloc: no device mapping for the allocation");
+    }
+    memset(h, 0, bytes);
+    *host_ptr = h;
+    *device_ptr = d;
+    return SPOPT_OK;
+}
+
+extern "C" void sparse_opt_host_free(void* host_ptr) {
+    if (host_ptr != nullptr) (void)hipHostFree(host_ptr);
+}
+
+extern "C" int sparse_opt_host_device_pointer(void* host_ptr, void** device_ptr) {
+    if (host_ptr == nullptr || device_ptr == nullptr)
+        return fail(SPOPT_EINVAL, "host_device_pointer: NULL argument");
+    void* d = nullptr;
+    if (hipHostGetDevicePointer(&d, host_ptr, 0) != hipSuccess || d == nullptr) {
+        (void)hipGetLastError();
+        return fail(SPOPT_EINVAL, "host_device_pointer: %p is not mapped pinned host memory",
+                    host_ptr);
+    }
+    *device_ptr = d;
+    return SPOPT_OK;
+}
+
 extern "C" int sparse_opt_create(spopt_t* out, int32_t kind, const void* config, int64_t rows,
                                  int64_t cols, float* params, float* m_or_momentum, float* v,
                                  int32_t* last_step) {
