@@ -9,13 +9,14 @@
 //      lookup order, digits of at most 8 bits): one kernel counts the digits
 //      of every pass, then each pass is one kernel whose tiles find their
 //      offsets by decoupled look-back;
-//   2. mark segment heads (id differs from its predecessor) and number them
-//      in one look-back pass, giving every lookup its segment number and
-//      emitting the distinct ids;
-//   3. sum each segment's value rows in double, in a fixed order, and round
-//      once: chunks of 16 sorted lookups per wave, partial sums for segments
-//      that cross a chunk boundary, then an ordered combine of those partials.
-//      No atomics in any sum, so the result is the same run to run.
+//   2. one kernel per tile of 256 sorted lookups: segment heads (id differs
+//      from its predecessor) numbered by decoupled look-back, distinct ids and
+//      counts emitted, and each segment's value rows summed in double in
+//      sorted (= lookup) order and rounded once; segments that cross waves are
+//      combined inside the tile in wave order;
+//   3. segments that cross tiles leave double partial sums, which a second
+//      kernel adds in tile order.  No atomics in any sum, so the result is the
+//      same run to run.
 #include <stdarg.h>
 #include <stdio.h>
 
@@ -30,9 +31,12 @@ constexpr int kTile = kThreads * kIpt;          // 1024 lookups per sort / segme
 constexpr int kRadixBits = 8;                   // at most 256 buckets per radix pass
 constexpr int kRadix = 1 << kRadixBits;
 constexpr int kMaxPasses = 8;
-constexpr int kRowChunk = 16;                   // sorted lookups per wave, summing
-constexpr int kFixThreads = 1024;               // block of the ordered combine
-constexpr int kFixWaves = kFixThreads / kWave;
+constexpr int kSumWaves = 8;                    // waves per segment-and-sum block
+constexpr int kSumThreads = kSumWaves * kWave;
+constexpr int kSumRows = 32;                    // sorted lookups per wave (lanes 0..31)
+constexpr int kSumTile = kSumWaves * kSumRows;  // sorted lookups per such block
+constexpr int kTilePartials = 32;               // partials one wave adds alone in the combine
+constexpr int kFixWaves2 = 16;                  // waves of the combining block
 
 // Decoupled look-back.  A tile publishes one 32-bit word per count:
 // bits 31..30 its state (aggregate of this tile / inclusive prefix through
@@ -50,10 +54,9 @@ constexpr uint32_t kSpinLimit = 1u << 16;
 
 struct CanonLayout {
     int key_bits, pos_bits, passes, digit_bits;
-    int64_t ntiles, nchunks;
+    int64_t ntiles, nsum;
     size_t off_a, off_b, off_clear, clear_bytes, off_status, off_tickets, off_hist,
-        off_segwords, off_words, off_segid, off_segstart, off_cross, off_big, off_pfirst,
-        off_plast, total;
+        off_sumwords, off_words, off_segstart, off_tcross, off_tfirst, off_tlast, total;
 };
 
 static int bits_for(uint64_t x) {  // bits needed to represent values in [0, x)
@@ -74,7 +77,7 @@ static bool canon_layout(int64_t n, int64_t width, int64_t key_space, CanonLayou
     L->passes = (L->key_bits + kRadixBits - 1) / kRadixBits;
     L->digit_bits = L->passes ? (L->key_bits + L->passes - 1) / L->passes : 0;
     L->ntiles = ceil_div(n, kTile);
-    L->nchunks = ceil_div(n, kRowChunk);
+    L->nsum = ceil_div(n, kSumTile);
     const size_t P = (size_t)(L->passes ? L->passes : 1);
     size_t o = 0;
     auto take = [&](size_t bytes) {
@@ -87,19 +90,16 @@ static bool canon_layout(int64_t n, int64_t width, int64_t key_space, CanonLayou
     // Everything a call must find zeroed sits in one contiguous region.
     L->off_clear = o;
     L->off_status = take(sizeof(uint32_t) * 4);
-    // tickets: one per radix pass, the segment kernel's, and the count of
-    // segments listed for a whole combining block.
-    L->off_tickets = take(sizeof(uint32_t) * (kMaxPasses + 2));
+    // tickets: one per radix pass and the segment-and-sum kernel's.
+    L->off_tickets = take(sizeof(uint32_t) * (kMaxPasses + 1));
     L->off_hist = take(sizeof(uint32_t) * (size_t)kRadix * P);
     L->off_words = take(sizeof(uint32_t) * (size_t)kRadix * (size_t)L->ntiles * P);
-    L->off_segwords = take(sizeof(uint32_t) * (size_t)L->ntiles);
+    L->off_sumwords = take(sizeof(uint32_t) * (size_t)L->nsum);
     L->clear_bytes = o - L->off_clear;
-    L->off_segid = take(sizeof(int32_t) * (size_t)n);
     L->off_segstart = take(sizeof(int32_t) * ((size_t)n + 1));
-    L->off_cross = take(sizeof(int32_t) * 2 * (size_t)L->nchunks);
-    L->off_big = take(sizeof(int32_t) * (size_t)L->nchunks);
-    L->off_pfirst = take(sizeof(double) * (size_t)L->nchunks * (size_t)width);
-    L->off_plast = take(sizeof(double) * (size_t)L->nchunks * (size_t)width);
+    L->off_tcross = take(sizeof(int32_t) * (size_t)L->nsum);
+    L->off_tfirst = take(sizeof(double) * (size_t)L->nsum * (size_t)width);
+    L->off_tlast = take(sizeof(double) * (size_t)L->nsum * (size_t)width);
     L->total = o;
     return true;
 }
@@ -375,87 +375,6 @@ __device__ __forceinline__ bool tile_exclusive_prefix(uint32_t* words, int64_t t
     return ok;
 }
 
-// Segment heads (id differs from its predecessor) of each tile of 1024
-// sorted lookups, counted with ballots and prefixed across tiles by the
-// look-back in one pass: every sorted lookup gets its segment number, every
-// head writes its id and position.  The last tile publishes U (0 when an id
-// was out of range or a wait timed out) and the sentinel seg_start[U] = n.
-__global__ __launch_bounds__(kThreads) void k_segment(
-    const uint64_t* __restrict__ s, int64_t n, int pos_bits, int64_t ntiles, uint32_t* words,
-    uint32_t* ticket, int32_t* __restrict__ seg_id, int32_t* __restrict__ seg_start,
-    int64_t* __restrict__ out_keys, int64_t* __restrict__ d_nunique, uint32_t* status) {
-    if (*status != 0u) {
-        if (blockIdx.x == 0 && threadIdx.x == 0) *d_nunique = 0;
-        return;
-    }
-    __shared__ uint32_t wcount[kWaves];
-    __shared__ uint32_t s_tile, s_excl, s_ok;
-    const int tid = threadIdx.x;
-    const int w = tid >> 6;
-    const int lane = lane_id();
-    if (tid == 0) s_tile = atomicAdd(ticket, 1u);
-    __syncthreads();
-    const int64_t tile = s_tile;
-    // Wave w owns the 256 consecutive lookups [w*256, (w+1)*256) of the tile,
-    // in four rounds of 64.
-    const int64_t first = tile * kTile + (int64_t)w * (kIpt * kWave);
-    const uint64_t lt = lanemask_lt();
-    uint64_t hm[kIpt];
-    uint32_t wave_heads = 0;
-#pragma unroll
-    for (int r = 0; r < kIpt; ++r) {
-        const int64_t i = first + (int64_t)r * kWave + lane;
-        const bool in = i < n;
-        const int64_t ic = in ? i : 0;
-        const uint64_t cur = s[ic], prev = s[ic > 0 ? ic - 1 : 0];
-        hm[r] = ballot(in && (i == 0 || (cur >> pos_bits) != (prev >> pos_bits)));
-        wave_heads += (uint32_t)popc64(hm[r]);
-    }
-    if (lane == 0) wcount[w] = wave_heads;
-    __syncthreads();
-    uint32_t tile_heads = 0, before_wave = 0;
-    for (int ww = 0; ww < kWaves; ++ww) {
-        if (ww < w) before_wave += wcount[ww];
-        tile_heads += wcount[ww];
-    }
-    if (w == 0) {
-        uint32_t excl = 0;
-        const bool ok = tile_exclusive_prefix(words, tile, tile_heads, &excl);
-        if (lane == 0) {
-            s_excl = excl;
-            s_ok = ok ? 1u : 0u;
-        }
-    }
-    __syncthreads();
-    if (!s_ok) {
-        if (tid == 0) {
-            atomicOr(status, kStatusTimeout);
-            *d_nunique = 0;
-        }
-        return;
-    }
-    uint32_t run = s_excl + before_wave;
-#pragma unroll
-    for (int r = 0; r < kIpt; ++r) {
-        const int64_t i = first + (int64_t)r * kWave + lane;
-        const bool h = (hm[r] >> lane) & 1ull;
-        if (i < n) {
-            const uint32_t sg = run + (uint32_t)popc64(hm[r] & lt) + (h ? 1u : 0u) - 1u;
-            seg_id[i] = (int32_t)sg;
-            if (h) {
-                out_keys[sg] = (int64_t)(s[i] >> pos_bits);
-                seg_start[sg] = (int32_t)i;
-            }
-        }
-        run += (uint32_t)popc64(hm[r]);
-    }
-    if (tile == ntiles - 1 && tid == 0) {
-        const uint32_t u = s_excl + tile_heads;
-        *d_nunique = (int64_t)u;
-        seg_start[u] = (int32_t)n;
-    }
-}
-
 // ----------------------------------------------------------- dup sums ---
 
 // V-wide access to a row of floats.  V > 1 is chosen on the host only when the
@@ -495,6 +414,20 @@ __device__ __forceinline__ void store_row(float* dst, const double (&r)[V], int6
     }
 }
 
+template <int V>
+__device__ __forceinline__ void store_row_f(float* dst, const float (&r)[V], int64_t col,
+                                            int64_t width) {
+    if (col < width) {
+        if constexpr (V == 4) {
+            *reinterpret_cast<float4*>(dst) = make_float4(r[0], r[1], r[2], r[3]);
+        } else if constexpr (V == 2) {
+            *reinterpret_cast<float2*>(dst) = make_float2(r[0], r[1]);
+        } else {
+            dst[0] = r[0];
+        }
+    }
+}
+
 // Partial sums of segments that cross a chunk boundary stay in double.
 template <int V>
 __device__ __forceinline__ void load_part(double (&r)[V], const double* src, int64_t col,
@@ -522,91 +455,182 @@ enum : int { kFlushNone = 0, kFlushOut = 1, kFlushFirst = 2, kFlushLast = 3 };
 // (vmcnt 0; the export and LDS/scalar counters are left at their maximum).
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-constexpr int kWavePartials = 32;  // partials one wave adds alone; more go to a whole block
 
-// One wave per chunk of 16 sorted lookups (lane j: lookup i0 + j), value rows
-// of `width` floats.  LPR lanes cover LPR*V consecutive columns of one row, so
-// one load instruction fetches RPI = 64/LPR rows (16-byte loads when V = 4).
-// For each block of columns every row of the chunk is loaded first and the
-// wave then waits once for all of them: stores share the vector memory
-// counter with loads, so a store between them would make later rows wait for
-// it too.  The rows are then added in sorted (= lookup) order: row j goes to
-// the accumulator of lane group j % RPI, and a segment that ends at row j is
-// closed by adding the group accumulators pairwise across lanes (one fixed
-// order, identical on every lane) unless row j is its only row in the chunk.
-// A segment that starts and ends in the chunk is written with its count; one
-// that started earlier leaves its partial in pfirst[chunk], one that goes on
-// in plast[chunk].  Every chunk records in cross[2*chunk..] the segment that
-// starts in it and goes on (-1 if none) and that segment's number of
-// partials m; it also writes that segment's count.  Segments with more than
-// kWavePartials partials are listed for a whole combining block.
+// Segments and their sums in one pass over the sorted lookups.  A block takes
+// the next tile ticket (kSumTile = 256 lookups); wave w owns the 32 lookups
+// [32w, 32w + 32) of the tile, lane j < 32 lookup i0 + j.
+//  1. Heads and segment ends come from the neighbouring sorted keys; the
+//     block counts its heads and wave 0 numbers the segments by decoupled
+//     look-back over earlier tiles (no row load is in flight yet, so the
+//     look-back's round trips do not queue behind row traffic).  Heads write
+//     the distinct id and the segment's first position.
+//  2. Value rows: LPR lanes cover LPR*V consecutive columns of one row
+//     (16-byte loads when V = 4), so one load instruction fetches 64/LPR rows;
+//     all 32 rows of the wave are loaded, the wave waits once (stores share the
+//     vector memory counter, so none is issued before the wait), then adds
+//     them in sorted (= lookup) order: row j to the accumulator of lane group
+//     j % (64/LPR); a segment that ends at row j is closed by adding the group
+//     accumulators pairwise across lanes (one fixed order, the same bits on
+//     every lane) unless row j is its only row in the wave.  A segment inside
+//     the wave is written with its count; the wave's first segment, if it began
+//     before the wave, leaves a double partial in LDS, and so does its last
+//     segment if it goes on past the wave.
+//  3. Wave 0 walks the 8 waves in order, adding partials of segments that
+//     cross waves inside the tile (wave order), and writes those segments with
+//     their counts.  What crosses the tile remains: the tile's first segment,
+//     begun in an earlier tile (partial in tfirst[tile]), and its last, going
+//     on into the next (partial in tlast[tile], and tcross[tile] = its number;
+//     -1 when there is none).
+// The last tile writes U (0 when an id was out of range or a wait timed out)
+// and seg_start[U] = n.
 template <int V, int LPR>
-__global__ __launch_bounds__(256) void k_dupsum_rows(
-    const uint64_t* __restrict__ s, const int32_t* __restrict__ seg_id,
-    const int32_t* __restrict__ seg_start, int64_t n, int pos_bits,
-    const float* __restrict__ vals, int64_t width, float* __restrict__ out_vals,
-    int32_t* __restrict__ out_counts, double* __restrict__ pfirst, double* __restrict__ plast,
-    int32_t* __restrict__ cross, int32_t* __restrict__ big, uint32_t* big_count,
-    const uint32_t* status) {
+__global__ __launch_bounds__(kSumThreads) void k_seg_sum(
+    const uint64_t* __restrict__ s, int64_t n, int pos_bits, int64_t ntiles,
+    const float* __restrict__ vals, int64_t width, int64_t* __restrict__ out_keys,
+    float* __restrict__ out_vals, int32_t* __restrict__ out_counts, int64_t* d_nunique,
+    int32_t* __restrict__ seg_start, double* __restrict__ tfirst, double* __restrict__ tlast,
+    int32_t* __restrict__ tcross, uint32_t* words, uint32_t* ticket, uint32_t* status) {
     constexpr int RPI = kWave / LPR;
-    constexpr int U = kRowChunk / RPI;  // load instructions per block of columns
-    static_assert(RPI >= 1 && kRowChunk % RPI == 0, "lane groups must tile the chunk");
-    if (*status != 0u) return;
+    constexpr int U = kSumRows / RPI;  // load instructions per block of columns
+    constexpr int CB = LPR * V;        // columns per block of columns
+    static_assert(kSumRows % RPI == 0 && kSumRows <= kWave, "lane groups tile the wave's rows");
+    static_assert(CB <= 128, "partials of one block of columns fit the LDS slots");
+    __shared__ double pf[kSumWaves][CB];
+    __shared__ double pl[kSumWaves][CB];
+    __shared__ uint32_t wheads[kSumWaves], wflags[kSumWaves];
+    __shared__ int32_t wfirst_end[kSumWaves], wlast_seg[kSumWaves], wlast_head[kSumWaves];
+    __shared__ uint32_t s_tile, s_excl, s_ok;
+    if (*status != 0u) {
+        if (blockIdx.x == 0 && threadIdx.x == 0) *d_nunique = 0;
+        return;
+    }
+    const int tid = threadIdx.x;
+    const int w = tid >> 6;
     const int lane = lane_id();
     const int sub = lane / LPR, sl = lane % LPR;
-    const int64_t chunk = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
-    const int64_t i0 = chunk * kRowChunk;
-    if (i0 >= n) return;
-    const int cnt = (int)((n - i0) < kRowChunk ? (n - i0) : kRowChunk);
+    if (tid == 0) s_tile = atomicAdd(ticket, 1u);
+    __syncthreads();
+    const int64_t tile = s_tile;
+    const int64_t i0 = tile * kSumTile + (int64_t)w * kSumRows;
+    const int cnt = i0 >= n ? 0 : (int)((n - i0) < kSumRows ? (n - i0) : kSumRows);
 
-    // Lane j < cnt describes lookup i0 + j; the others read valid indices.
-    // Independent loads only: the segment of lookup i0 - 1 tells whether a
-    // segment started before the chunk.
+    // ---- 1. heads, ends, numbering
     const bool in = lane < cnt;
-    const int64_t i = i0 + (in ? lane : 0);
-    const uint32_t pos = (uint32_t)(s[i] & ((1ull << pos_bits) - 1ull));
-    const int32_t seg = seg_id[i];
-    const int32_t seg_next = seg_id[i + 1 < n ? i + 1 : i];
-    const int32_t seg_before = seg_id[i0 > 0 ? i0 - 1 : 0];
-    const bool ends = in && (i + 1 >= n || seg_next != seg);
-    const bool starts_here = i0 == 0 || seg != seg_before;
-    const int32_t seg_up = __shfl_up(seg, 1, kWave);
-    const uint64_t hm = ballot(in && (lane == 0 ? starts_here : seg_up != seg));
+    const int64_t i = in ? i0 + lane : (i0 < n ? i0 : n - 1);
+    const uint64_t key = s[i];
+    const uint64_t prev = s[i > 0 ? i - 1 : 0];
+    const uint64_t next = s[i + 1 < n ? i + 1 : i];
+    const uint64_t id = key >> pos_bits;
+    const bool head = in && (i == 0 || (prev >> pos_bits) != id);
+    const bool ends = in && (i + 1 >= n || (next >> pos_bits) != id);
+    const uint32_t pos = (uint32_t)(key & ((1ull << pos_bits) - 1ull));
+    const uint64_t hm = ballot(head);
+    if (lane == 0) wheads[w] = (uint32_t)popc64(hm);
+    __syncthreads();
+    uint32_t tile_heads = 0, before = 0;
+#pragma unroll
+    for (int ww = 0; ww < kSumWaves; ++ww) {
+        if (ww < w) before += wheads[ww];
+        tile_heads += wheads[ww];
+    }
+    if (w == 0) {
+        uint32_t excl = 0;
+        const bool ok = tile_exclusive_prefix(words, tile, tile_heads, &excl);
+        if (lane == 0) {
+            s_excl = excl;
+            s_ok = ok ? 1u : 0u;
+        }
+    }
+    __syncthreads();
+    if (!s_ok) {
+        if (tid == 0) {
+            atomicOr(status, kStatusTimeout);
+            *d_nunique = 0;
+        }
+        return;
+    }
+    const uint64_t upto = lane == 63 ? ~0ull : ((2ull << lane) - 1ull);
+    const uint32_t heads_upto = (uint32_t)popc64(hm & upto);
+    const int32_t seg = (int32_t)(s_excl + before + heads_upto) - 1;
+    const bool starts_here = heads_upto > 0;  // a head at or before lane j in this wave
     int kind = kFlushNone;
     if (in && (ends || lane == cnt - 1))
         kind = (ends && starts_here) ? kFlushOut : (!starts_here ? kFlushFirst : kFlushLast);
+    const uint64_t first_m = ballot(kind == kFlushFirst);
+    const uint64_t last_m = ballot(kind == kFlushLast);
+    const uint64_t ends_m = ballot(ends);
+    if (lane == 0) {
+        const int fl = first_m ? __builtin_ctzll(first_m) : 0;
+        const int ll = last_m ? __builtin_ctzll(last_m) : 0;
+        const uint64_t upto_ll = ll == 63 ? ~0ull : ((2ull << ll) - 1ull);
+        uint32_t f = 0;
+        if (first_m) f |= 1u | (((ends_m >> fl) & 1ull) ? 2u : 0u);
+        if (last_m) f |= 4u;
+        wflags[w] = f;
+        wfirst_end[w] = (int32_t)(i0 + fl);
+        wlast_head[w] = (int32_t)(i0 + 63 - __builtin_clzll((hm & upto_ll) | 1ull));
+    }
+    const int32_t lseg = read_lane(seg, last_m ? __builtin_ctzll(last_m) : 0);
+    if (lane == 0) wlast_seg[w] = lseg;
+    if (head) {
+        out_keys[seg] = (int64_t)id;
+        seg_start[seg] = (int32_t)i;
+    }
+    if (kind == kFlushOut) {
+        const int first = 63 - __builtin_clzll(hm & upto);
+        out_counts[seg] = lane - first + 1;
+    }
+    if (tile == ntiles - 1 && tid == 0) {
+        const uint32_t u = s_excl + tile_heads;
+        *d_nunique = (int64_t)u;
+        seg_start[u] = (int32_t)n;
+    }
 
-    float row[U][V];
-    auto load_rows = [&](int64_t col) {
+    // ---- 2. and 3., one block of columns at a time
+    for (int64_t c0 = 0; c0 < width; c0 += CB) {
+        const int64_t col = c0 + (int64_t)sl * V;
+        float row[U][V];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            // Past the chunk's last lookup, reload that lookup's row (unused).
+            // Past the wave's last lookup, reload that lookup's row (unused).
             const int j = u * RPI + sub;
-            const uint32_t p = (uint32_t)__shfl((int)pos, j < cnt ? j : cnt - 1, kWave);
+            const int src = j < cnt ? j : (cnt > 0 ? cnt - 1 : 0);
+            const uint32_t p = (uint32_t)__shfl((int)pos, src, kWave);
             load_row<V>(row[u], vals + (int64_t)p * width, col, width);
         }
-    };
-    load_rows((int64_t)sl * V);
-    // End of the segment that goes on past the chunk (read by every lane, used
-    // by the last one; seg + 1 <= U, inside seg_start).
-    const int32_t seg_end = seg_start[seg + 1];
-
-    for (int64_t c0 = 0; c0 < width; c0 += (int64_t)LPR * V) {
-        const int64_t col = c0 + (int64_t)sl * V;
-        if (c0 > 0) load_rows(col);
         wait_vmem_all();
         double acc[V];
 #pragma unroll
         for (int v = 0; v < V; ++v) acc[v] = 0.0;
 #pragma unroll
-        for (int j = 0; j < kRowChunk; ++j) {
+        for (int j = 0; j < kSumRows; ++j) {
             const int k = j < cnt ? read_lane(kind, j) : kFlushNone;
+            const bool single = (hm >> j) & 1ull;  // row j is the segment's only row here
+            if (k != kFlushNone && single) {
+                // The sum of one row is the row itself (0 + x rounds back to x):
+                // no double accumulation.  acc holds zeros here, since every
+                // segment before row j closed at or before row j - 1.
+                if (sub == j % RPI) {
+                    if (k == kFlushOut) {
+                        store_row_f<V>(out_vals + (int64_t)read_lane(seg, j) * width + col,
+                                       row[j / RPI], col, width);
+                    } else {
+#pragma unroll
+                        for (int v = 0; v < V; ++v) {
+                            if (k == kFlushFirst)
+                                pf[w][sl * V + v] = (double)row[j / RPI][v];
+                            else
+                                pl[w][sl * V + v] = (double)row[j / RPI][v];
+                        }
+                    }
+                }
+                continue;
+            }
             if (j < cnt && sub == j % RPI) {
 #pragma unroll
                 for (int v = 0; v < V; ++v) acc[v] += (double)row[j / RPI][v];
             }
             if (k != kFlushNone) {
-                const bool single = (hm >> j) & 1ull;  // row j is the segment's only row here
                 int owner = j % RPI;
                 if (!single) {
                     owner = 0;
@@ -616,49 +640,99 @@ __global__ __launch_bounds__(256) void k_dupsum_rows(
                         for (int v = 0; v < V; ++v) acc[v] += __shfl_xor(acc[v], o, kWave);
                 }
                 if (sub == owner) {
-                    if (k == kFlushOut)
+                    if (k == kFlushOut) {
                         store_row<V>(out_vals + (int64_t)read_lane(seg, j) * width + col, acc,
                                      col, width);
-                    else if (k == kFlushFirst)
-                        store_part<V>(pfirst + chunk * width + col, acc, col, width);
-                    else
-                        store_part<V>(plast + chunk * width + col, acc, col, width);
+                    } else {
+#pragma unroll
+                        for (int v = 0; v < V; ++v) {
+                            if (k == kFlushFirst)
+                                pf[w][sl * V + v] = acc[v];
+                            else
+                                pl[w][sl * V + v] = acc[v];
+                        }
+                    }
                 }
 #pragma unroll
                 for (int v = 0; v < V; ++v) acc[v] = 0.0;
             }
         }
-    }
-
-    const uint64_t upto = lane == 63 ? ~0ull : ((2ull << lane) - 1ull);
-    const int64_t head = i0 + (63 - __builtin_clzll((hm & upto) | 1ull));  // if starts_here
-    if (kind == kFlushOut) out_counts[seg] = (int32_t)(i - head + 1);
-    if (lane == cnt - 1) {
-        int32_t m = 0;
-        if (kind == kFlushLast) {
-            out_counts[seg] = (int32_t)(seg_end - head);
-            m = (int32_t)((seg_end - 1) / kRowChunk - chunk + 1);
-            if (m > kWavePartials) big[atomicAdd(big_count, 1u)] = (int32_t)chunk;
+        __syncthreads();
+        if (w == 0) {
+            // Wave 0 walks the waves in order; lane l holds columns l and l + 64
+            // of this block of columns.
+            const bool tile_head = (wflags[0] & 1u) == 0u;  // tile starts with a head
+            bool open = !tile_head, open_here = false;
+            int32_t open_seg = -1, open_head = 0;
+            double carry[2] = {0.0, 0.0};
+            for (int ww = 0; ww < kSumWaves; ++ww) {
+                const uint32_t f = wflags[ww];
+                if (f & 1u) {
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const int c = lane + h * kWave;
+                        if (c < CB) carry[h] += pf[ww][c];
+                    }
+                    if (f & 2u) {  // the open segment ends in wave ww
+                        if (open_here) {
+#pragma unroll
+                            for (int h = 0; h < 2; ++h) {
+                                const int64_t c = c0 + lane + h * kWave;
+                                if (lane + h * kWave < CB && c < width)
+                                    out_vals[(int64_t)open_seg * width + c] = (float)carry[h];
+                            }
+                            if (lane == 0 && c0 == 0)
+                                out_counts[open_seg] = wfirst_end[ww] - open_head + 1;
+                        } else {
+#pragma unroll
+                            for (int h = 0; h < 2; ++h) {
+                                const int64_t c = c0 + lane + h * kWave;
+                                if (lane + h * kWave < CB && c < width)
+                                    tfirst[tile * width + c] = carry[h];
+                            }
+                        }
+                        carry[0] = carry[1] = 0.0;
+                        open = open_here = false;
+                    }
+                }
+                if (f & 4u) {  // a segment starts in wave ww and goes past it
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const int c = lane + h * kWave;
+                        carry[h] = c < CB ? pl[ww][c] : 0.0;
+                    }
+                    open = open_here = true;
+                    open_seg = wlast_seg[ww];
+                    open_head = wlast_head[ww];
+                }
+            }
+            if (open) {
+                double* dst = open_here ? tlast : tfirst;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int64_t c = c0 + lane + h * kWave;
+                    if (lane + h * kWave < CB && c < width) dst[tile * width + c] = carry[h];
+                }
+            }
+            if (lane == 0 && c0 == 0) tcross[tile] = open && open_here ? open_seg : -1;
         }
-        cross[2 * chunk] = kind == kFlushLast ? seg : -1;
-        cross[2 * chunk + 1] = m;
+        __syncthreads();
     }
 }
 
-
-// Adds partials q in [lo, hi) of a segment whose start chunk is `chunk`
-// (q = 0: plast[chunk], q > 0: pfirst[chunk + q]) in increasing q, D loads in
-// flight (past hi, partial lo is reloaded and unused).
+// Adds partials q in [lo, hi) of a segment whose start tile is `tile` (q = 0:
+// tlast[tile], q > 0: tfirst[tile + q]) in increasing q, D loads in flight
+// (past hi, partial lo is reloaded and unused).
 template <int V, int D>
-__device__ __forceinline__ void add_partials(double (&acc)[V], const double* pfirst,
-                                             const double* plast, int64_t chunk, int64_t lo,
+__device__ __forceinline__ void add_partials(double (&acc)[V], const double* tfirst,
+                                             const double* tlast, int64_t tile, int64_t lo,
                                              int64_t hi, int64_t width, int64_t col) {
     for (int64_t q0 = lo; q0 < hi; q0 += D) {
         double row[D][V];
 #pragma unroll
         for (int u = 0; u < D; ++u) {
             const int64_t q = q0 + u < hi ? q0 + u : lo;
-            const double* src = (q == 0) ? plast + chunk * width : pfirst + (chunk + q) * width;
+            const double* src = (q == 0) ? tlast + tile * width : tfirst + (tile + q) * width;
             load_part<V>(row[u], src + col, col, width);
         }
 #pragma unroll
@@ -670,66 +744,58 @@ __device__ __forceinline__ void add_partials(double (&acc)[V], const double* pfi
     }
 }
 
-// Segments that cross chunk boundaries.  The chunk where such a segment
-// starts holds its partial in plast, each following chunk up to the one where
-// it ends in pfirst: m partials, recorded with the segment in cross[] by the
-// chunk where it starts.  The order of the additions depends on m only, so
-// the result is the same run to run: up to kWavePartials partials are added
-// in chunk order by one wave (one chunk's record per wave); beyond, by a
-// whole block from the list of such chunks (blocks stride over the list):
-// [0, m) is cut into 16 equal runs, wave r adds run r in chunk order with 8
-// loads in flight (4 when V = 4, within the register budget of a 1024-thread
-// block), and wave 0 adds the 16 run sums in run order.
+// Segments that cross tiles, one block per tile that starts one (tcross):
+// m partials (tlast of the start tile, tfirst of each following tile up to
+// the one where it ends).  The order of the additions depends on m only, so
+// the result is the same run to run: up to kTilePartials partials are added in
+// tile order by wave 0; beyond, [0, m) is cut into 16 equal runs, wave r adds
+// run r in tile order, and wave 0 adds the 16 run sums in run order.  The
+// block also writes the segment's count.
 template <int V>
-__global__ __launch_bounds__(kFixThreads) void k_dupsum_fixup(
-    const int32_t* __restrict__ cross, const int32_t* __restrict__ big,
-    const uint32_t* big_count, int64_t nchunks, const double* __restrict__ pfirst,
-    const double* __restrict__ plast, int64_t width, float* __restrict__ out_vals,
-    const uint32_t* status) {
-    __shared__ double part[kFixWaves][kWave * V];
+__global__ __launch_bounds__(kFixWaves2 * kWave) void k_tile_fixup(
+    const int32_t* __restrict__ tcross, const int32_t* __restrict__ seg_start,
+    const double* __restrict__ tfirst, const double* __restrict__ tlast, int64_t width,
+    float* __restrict__ out_vals, int32_t* __restrict__ out_counts, const uint32_t* status) {
+    __shared__ double part[kFixWaves2][kWave * V];
     if (*status != 0u) return;
+    const int64_t tile = blockIdx.x;
+    const int32_t seg = tcross[tile];
+    if (seg < 0) return;
     const int w = (int)(threadIdx.x >> 6);
     const int lane = lane_id();
-    for (int64_t chunk = (int64_t)blockIdx.x * kFixWaves + w; chunk < nchunks;
-         chunk += (int64_t)gridDim.x * kFixWaves) {
-        const int32_t seg = cross[2 * chunk];
-        const int64_t m = cross[2 * chunk + 1];
-        if (seg < 0 || m > kWavePartials) continue;
-        for (int64_t c0 = 0; c0 < width; c0 += (int64_t)kWave * V) {
-            const int64_t col = c0 + (int64_t)lane * V;
-            double tot[V];
-#pragma unroll
-            for (int v = 0; v < V; ++v) tot[v] = 0.0;
-            add_partials<V, (V == 4 ? 4 : 8)>(tot, pfirst, plast, chunk, 0, m, width, col);
-            store_row<V>(out_vals + (int64_t)seg * width + col, tot, col, width);
-        }
-    }
-    const uint32_t nbig = *big_count;
-    for (uint32_t b = blockIdx.x; b < nbig; b += gridDim.x) {
-        const int64_t chunk = big[b];
-        const int32_t seg = cross[2 * chunk];
-        const int64_t m = cross[2 * chunk + 1];
-        const int64_t lo = m * w / kFixWaves, hi = m * (w + 1) / kFixWaves;
-        for (int64_t c0 = 0; c0 < width; c0 += (int64_t)kWave * V) {
-            const int64_t col = c0 + (int64_t)lane * V;
-            double acc[V];
-#pragma unroll
-            for (int v = 0; v < V; ++v) acc[v] = 0.0;
-            add_partials<V, (V == 4 ? 4 : 8)>(acc, pfirst, plast, chunk, lo, hi, width, col);
-#pragma unroll
-            for (int v = 0; v < V; ++v) part[w][lane * V + v] = acc[v];
-            __syncthreads();
+    const int64_t s0 = seg_start[seg], s1 = seg_start[seg + 1];
+    if (threadIdx.x == 0) out_counts[seg] = (int32_t)(s1 - s0);
+    const int64_t m = (s1 - 1) / kSumTile - tile + 1;
+    for (int64_t c0 = 0; c0 < width; c0 += (int64_t)kWave * V) {
+        const int64_t col = c0 + (int64_t)lane * V;
+        if (m <= kTilePartials) {
             if (w == 0) {
                 double tot[V];
 #pragma unroll
-                for (int v = 0; v < V; ++v) tot[v] = part[0][lane * V + v];
-                for (int ww = 1; ww < kFixWaves; ++ww)
-#pragma unroll
-                    for (int v = 0; v < V; ++v) tot[v] += part[ww][lane * V + v];
+                for (int v = 0; v < V; ++v) tot[v] = 0.0;
+                add_partials<V, (V == 4 ? 4 : 8)>(tot, tfirst, tlast, tile, 0, m, width, col);
                 store_row<V>(out_vals + (int64_t)seg * width + col, tot, col, width);
             }
-            __syncthreads();
+            continue;
         }
+        const int64_t lo = m * w / kFixWaves2, hi = m * (w + 1) / kFixWaves2;
+        double acc[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v) acc[v] = 0.0;
+        add_partials<V, (V == 4 ? 4 : 8)>(acc, tfirst, tlast, tile, lo, hi, width, col);
+#pragma unroll
+        for (int v = 0; v < V; ++v) part[w][lane * V + v] = acc[v];
+        __syncthreads();
+        if (w == 0) {
+            double tot[V];
+#pragma unroll
+            for (int v = 0; v < V; ++v) tot[v] = part[0][lane * V + v];
+            for (int ww = 1; ww < kFixWaves2; ++ww)
+#pragma unroll
+                for (int v = 0; v < V; ++v) tot[v] += part[ww][lane * V + v];
+            store_row<V>(out_vals + (int64_t)seg * width + col, tot, col, width);
+        }
+        __syncthreads();
     }
 }
 
@@ -796,13 +862,11 @@ extern "C" int coo_from_lookups(const int64_t* ids, const float* vals, int64_t n
     uint32_t* tickets = (uint32_t*)(ws + L.off_tickets);
     uint32_t* hist = (uint32_t*)(ws + L.off_hist);
     uint32_t* words = (uint32_t*)(ws + L.off_words);
-    uint32_t* segwords = (uint32_t*)(ws + L.off_segwords);
-    int32_t* seg_id = (int32_t*)(ws + L.off_segid);
+    uint32_t* sumwords = (uint32_t*)(ws + L.off_sumwords);
     int32_t* seg_start = (int32_t*)(ws + L.off_segstart);
-    int32_t* cross = (int32_t*)(ws + L.off_cross);
-    int32_t* big = (int32_t*)(ws + L.off_big);
-    double* pfirst = (double*)(ws + L.off_pfirst);
-    double* plast = (double*)(ws + L.off_plast);
+    int32_t* tcross = (int32_t*)(ws + L.off_tcross);
+    double* tfirst = (double*)(ws + L.off_tfirst);
+    double* tlast = (double*)(ws + L.off_tlast);
 
     // Zero the status word, tickets, histograms and look-back words.
     const int64_t n16 = (int64_t)(L.clear_bytes / 16);
@@ -841,50 +905,43 @@ extern "C" int coo_from_lookups(const int64_t* ids, const float* vals, int64_t n
         dst = t;
     }
     const uint64_t* sorted = src;
-    k_segment<<<(unsigned)L.ntiles, kThreads, 0, st>>>(sorted, n, L.pos_bits, L.ntiles, segwords,
-                                                       tickets + kMaxPasses, seg_id, seg_start,
-                                                       out_keys, d_nunique, status);
-    SPOPT_LAUNCHED();
 
-    // Duplicate sums: chunks of 16 sorted lookups, 4 per block, then the
-    // ordered combine of segments that cross chunks.  V floats per lane (16-
-    // or 8-byte accesses when the width and the value arrays allow them), over
-    // the smallest lane group that covers the row, up to the whole wave.
+    // Segments and sums, tiles of kSumTile sorted lookups, then the ordered
+    // combine of segments that cross tiles.  V floats per lane (16- or 8-byte
+    // accesses when the width and the value arrays allow them), over the
+    // smallest lane group that covers up to 128 columns (32 lanes at most for 2 or
+// 4 floats per lane, within the register budget).
     const uintptr_t al = (uintptr_t)vals | (uintptr_t)out_vals;
     const int V = (width % 4 == 0 && (al & 15u) == 0) ? 4 : (width % 2 == 0 && (al & 7u) == 0) ? 2 : 1;
-    const int lpr = width <= 16 * V ? 16 : (width <= 32 * V ? 32 : 64);
-    uint32_t* big_count = tickets + kMaxPasses + 1;
-    auto rows = [&](auto kernel) {
-        kernel<<<(unsigned)ceil_div(L.nchunks, 4), 256, 0, st>>>(
-            sorted, seg_id, seg_start, n, L.pos_bits, vals, width, out_vals, out_counts, pfirst,
-            plast, cross, big, big_count, status);
+    const int lpr = width <= 16 * V ? 16 : ((width <= 32 * V || V >= 2) ? 32 : 64);
+    auto sum = [&](auto kernel) {
+        kernel<<<(unsigned)L.nsum, kSumThreads, 0, st>>>(
+            sorted, n, L.pos_bits, L.nsum, vals, width, out_keys, out_vals, out_counts, d_nunique,
+            seg_start, tfirst, tlast, tcross, sumwords, tickets + kMaxPasses, status);
     };
     if (V == 4)
-        lpr == 16 ? rows(k_dupsum_rows<4, 16>) : lpr == 32 ? rows(k_dupsum_rows<4, 32>)
-                                                          : rows(k_dupsum_rows<4, 64>);
+        lpr == 16 ? sum(k_seg_sum<4, 16>) : sum(k_seg_sum<4, 32>);
     else if (V == 2)
-        lpr == 16 ? rows(k_dupsum_rows<2, 16>) : lpr == 32 ? rows(k_dupsum_rows<2, 32>)
-                                                          : rows(k_dupsum_rows<2, 64>);
+        lpr == 16 ? sum(k_seg_sum<2, 16>) : sum(k_seg_sum<2, 32>);
     else
-        lpr == 16 ? rows(k_dupsum_rows<1, 16>) : lpr == 32 ? rows(k_dupsum_rows<1, 32>)
-                                                          : rows(k_dupsum_rows<1, 64>);
+        lpr == 16 ? sum(k_seg_sum<1, 16>) : lpr == 32 ? sum(k_seg_sum<1, 32>)
+                                                    : sum(k_seg_sum<1, 64>);
     SPOPT_LAUNCHED();
 
     // The combine: V doubles per lane over blocks of 64*V columns.
     const int FV = (width % 4 == 0 && width >= 256 && (al & 15u) == 0) ? 4
                    : (width % 2 == 0 && width >= 128 && (al & 7u) == 0) ? 2 : 1;
-    const int64_t fblocks = ceil_div(L.nchunks, kFixWaves);
-    const unsigned fgrid = (unsigned)(fblocks < 1024 ? fblocks : 1024);
     auto fix = [&](auto kernel) {
-        kernel<<<fgrid, kFixThreads, 0, st>>>(cross, big, big_count, L.nchunks, pfirst, plast,
-                                              width, out_vals, status);
+        kernel<<<(unsigned)L.nsum, kFixWaves2 * kWave, 0, st>>>(tcross, seg_start, tfirst, tlast,
+                                                                width, out_vals, out_counts,
+                                                                status);
     };
     if (FV == 4)
-        fix(k_dupsum_fixup<4>);
+        fix(k_tile_fixup<4>);
     else if (FV == 2)
-        fix(k_dupsum_fixup<2>);
+        fix(k_tile_fixup<2>);
     else
-        fix(k_dupsum_fixup<1>);
+        fix(k_tile_fixup<1>);
     SPOPT_LAUNCHED();
     return SPOPT_OK;
 }
