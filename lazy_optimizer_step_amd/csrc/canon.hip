@@ -35,7 +35,7 @@ constexpr int kSumWaves = 8;                    // waves per segment-and-sum blo
 constexpr int kSumThreads = kSumWaves * kWave;
 constexpr int kSumRows = 32;                    // sorted lookups per wave (lanes 0..31)
 constexpr int kSumTile = kSumWaves * kSumRows;  // sorted lookups per such block
-constexpr int kTilePartials = 32;               // partials one wave adds alone in the combine
+constexpr int kTilePartials = 8;                // partials one wave adds alone in the combine
 constexpr int kFixWaves2 = 16;                  // waves of the combining block
 
 // Decoupled look-back.  A tile publishes one 32-bit word per count:
