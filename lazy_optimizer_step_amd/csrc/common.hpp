@@ -80,29 +80,6 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, uint32_t* warp_t
     return before + inc - x;
 }
 
-// Wave-cooperative lower bound: first index i in [0, n) with a[i] >= x (n if
-// none), for ascending a.  Each round probes 64 evenly spaced positions, so a
-// search over 2^18 keys takes 3 dependent loads.  All lanes return the result.
-__device__ __forceinline__ int64_t wave_lower_bound(const int64_t* a, int64_t n, int64_t x) {
-    const int l = lane_id();
-    int64_t lo = 0, hi = n;  // answer in [lo, hi]
-    while (hi - lo > kWave) {
-        const int64_t step = (hi - lo + kWave - 1) / kWave;
-        const int64_t q = lo + (int64_t)(l + 1) * step - 1;
-        const bool valid = q < hi;
-        const bool less = valid && a[q] < x;
-        const int cnt = popc64(ballot(less));
-        const int nvalid = popc64(ballot(valid));
-        const int64_t new_lo = lo + (int64_t)cnt * step;
-        if (cnt < nvalid) hi = lo + (int64_t)(cnt + 1) * step - 1;
-        lo = new_lo;
-        if (hi > n) hi = n;
-    }
-    const int64_t q = lo + l;
-    const bool less = (q < hi) && a[q] < x;
-    return lo + popc64(ballot(less));
-}
-
 __device__ __forceinline__ bool finite_f(float x) { return __builtin_isfinite(x); }
 
 // ------------------------------------------------------------------ host ---

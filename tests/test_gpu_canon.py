@@ -162,7 +162,10 @@ def test_workspace_too_small():
     (1000, 64, 3000, 0), (50000, 128, 20000, 0), (7, 4, 30, 0), (9000, 3, 500, 0),
     # row_offsets blocks of 8192 entries: a full last block, a one-entry last
     # block, and a row_offsets array that is not 16-byte aligned (scalar stores)
-    (8191, 8, 4000, 0), (8192, 8, 4000, 0), (50000, 128, 20000, 1), (24577, 4, 9000, 3)])
+    (8191, 8, 4000, 0), (8192, 8, 4000, 0), (50000, 128, 20000, 1), (24577, 4, 9000, 3),
+    # every row touched: blocks holding 8192 keys each; 200,000 entries make
+    # the search over the keys take three rounds
+    (16384, 4, 200000, 0)])
 def test_csr_from_full_row_coo(rows, cols, n, ro_shift):
     rng = np.random.default_rng(rows)
     ids = rng.integers(0, rows, size=n, dtype=np.int64)
