@@ -20,6 +20,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+
 #include "common.hpp"
 
 namespace spopt {
@@ -47,15 +48,23 @@ constexpr uint32_t kLbAgg = 1u << 30;
 constexpr uint32_t kLbInc = 2u << 30;
 constexpr uint32_t kLbState = 3u << 30;
 constexpr uint32_t kLbCount = (1u << 30) - 1u;
-// A tile waits only for tiles that took their ticket earlier, which publish
-// their own counts before they wait on anybody; the bound only turns a bug
-// into a reported error instead of a hang.
+// Tiles are numbered by an atomic ticket, in the order blocks start, so a
+// tile waits only for tiles that are already running and publish their own
+// counts before they wait on anybody; the bound only turns a bug into a
+// reported error instead of a hang.
 constexpr uint32_t kSpinLimit = 1u << 16;
+// The pack kernel: at most this many blocks, each counting the digits of its
+// share of the lookups into its own histograms (plain stores, nothing to zero
+// beforehand); every radix pass sums them.  kPackIpt lookups per thread are
+// loaded before any is used.
+constexpr int kPackBlocks = 32;
+constexpr int kPackIpt = 8;
 
 struct CanonLayout {
     int key_bits, pos_bits, passes, digit_bits;
     int64_t ntiles, nsum;
-    size_t off_a, off_b, off_clear, clear_bytes, off_status, off_tickets, off_hist,
+    int64_t npack;  // blocks of the pack kernel
+    size_t off_a, off_b, off_part, off_pflag, off_clear, clear_bytes, off_status, off_tickets,
         off_sumwords, off_words, off_segstart, off_tcross, off_tfirst, off_tlast, total;
 };
 
@@ -78,6 +87,9 @@ static bool canon_layout(int64_t n, int64_t width, int64_t key_space, CanonLayou
     L->digit_bits = L->passes ? (L->key_bits + L->passes - 1) / L->passes : 0;
     L->ntiles = ceil_div(n, kTile);
     L->nsum = ceil_div(n, kSumTile);
+    L->npack = ceil_div(n, (int64_t)kPackIpt * kThreads);
+    if (L->npack > kPackBlocks) L->npack = kPackBlocks;
+    if (L->npack < 1) L->npack = 1;
     const size_t P = (size_t)(L->passes ? L->passes : 1);
     size_t o = 0;
     auto take = [&](size_t bytes) {
@@ -87,12 +99,15 @@ static bool canon_layout(int64_t n, int64_t width, int64_t key_space, CanonLayou
     };
     L->off_a = take(sizeof(uint64_t) * (size_t)n);
     L->off_b = take(sizeof(uint64_t) * (size_t)n);
-    // Everything a call must find zeroed sits in one contiguous region.
+    // Digit histograms and range flag of each pack block.
+    L->off_part = take(sizeof(uint32_t) * (size_t)kPackBlocks * kRadix * P);
+    L->off_pflag = take(sizeof(uint32_t) * (size_t)kPackBlocks);
+    // Everything the kernels after the pack kernel must find zeroed sits in
+    // one contiguous region, which the pack kernel zeroes.
     L->off_clear = o;
     L->off_status = take(sizeof(uint32_t) * 4);
     // tickets: one per radix pass and the segment-and-sum kernel's.
     L->off_tickets = take(sizeof(uint32_t) * (kMaxPasses + 1));
-    L->off_hist = take(sizeof(uint32_t) * (size_t)kRadix * P);
     L->off_words = take(sizeof(uint32_t) * (size_t)kRadix * (size_t)L->ntiles * P);
     L->off_sumwords = take(sizeof(uint32_t) * (size_t)L->nsum);
     L->clear_bytes = o - L->off_clear;
@@ -159,14 +174,6 @@ __device__ __forceinline__ bool look_back(const uint32_t* lb, int64_t tile, int6
     return true;
 }
 
-// ----------------------------------------------------------------- clear ---
-
-__global__ void k_clear(uint4* p, int64_t n16) {
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
-         i += (int64_t)gridDim.x * blockDim.x)
-        p[i] = make_uint4(0u, 0u, 0u, 0u);
-}
-
 __global__ void k_status_clear(uint32_t* st, int nwords) {
     if ((int)threadIdx.x < nwords) st[threadIdx.x] = 0u;
 }
@@ -174,41 +181,58 @@ __global__ void k_status_clear(uint32_t* st, int nwords) {
 // ------------------------------------------------------------------ sort ---
 
 // Range-check ids, pack (id << pos_bits | position), and count the digits of
-// every radix pass into the global per-pass histograms (LDS first).
+// every radix pass, in LDS first.  The grid (at most kPackBlocks blocks)
+// strides over the lookups; block g writes its histograms to part[g] and its
+// range flag to pflag[g] with plain stores.  The blocks also zero the region
+// the later kernels of the call need zeroed (status, tickets, look-back
+// words): those kernels start after this one has ended.
 __global__ __launch_bounds__(kThreads) void k_pack(const int64_t* __restrict__ ids, int64_t n,
                                                    int64_t key_space, int pos_bits, int passes,
                                                    int digit_bits, uint64_t* __restrict__ out,
-                                                   uint32_t* __restrict__ hist,
-                                                   uint32_t* status) {
+                                                   uint32_t* __restrict__ part,
+                                                   uint32_t* __restrict__ pflag,
+                                                   uint4* __restrict__ zero, int64_t nzero16) {
     __shared__ uint32_t h[kMaxPasses * kRadix];
+    const int tid = threadIdx.x;
     const int words = passes * kRadix;
-    for (int i = threadIdx.x; i < words; i += kThreads) h[i] = 0;
+    for (int i = tid; i < words; i += kThreads) h[i] = 0;
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + tid; i < nzero16;
+         i += (int64_t)gridDim.x * kThreads)
+        zero[i] = make_uint4(0u, 0u, 0u, 0u);
     __syncthreads();
-    const int64_t base = (int64_t)blockIdx.x * kTile;
     const uint32_t dmask = (1u << digit_bits) - 1u;
     bool bad = false;
+    constexpr int64_t kChunk = (int64_t)kPackIpt * kThreads;
+    for (int64_t base = (int64_t)blockIdx.x * kChunk; base < n;
+         base += (int64_t)gridDim.x * kChunk) {
+        int64_t id[kPackIpt];
 #pragma unroll
-    for (int j = 0; j < kIpt; ++j) {
-        const int64_t i = base + (int64_t)j * kThreads + threadIdx.x;
-        if (i < n) {
-            int64_t id = ids[i];
-            if (id < 0 || id >= key_space) {
-                bad = true;
-                id = 0;  // keep sorting a safe key; the result is discarded
+        for (int j = 0; j < kPackIpt; ++j) {
+            const int64_t i = base + (int64_t)j * kThreads + tid;
+            id[j] = ids[i < n ? i : n - 1];
+        }
+#pragma unroll
+        for (int j = 0; j < kPackIpt; ++j) {
+            const int64_t i = base + (int64_t)j * kThreads + tid;
+            if (i < n) {
+                int64_t x = id[j];
+                if (x < 0 || x >= key_space) {
+                    bad = true;
+                    x = 0;  // keep sorting a safe key; the result is discarded
+                }
+                const uint64_t packed = ((uint64_t)x << pos_bits) | (uint64_t)i;
+                out[i] = packed;
+                for (int p = 0; p < passes; ++p)
+                    atomicAdd(&h[p * kRadix +
+                                 ((uint32_t)(packed >> (pos_bits + p * digit_bits)) & dmask)],
+                              1u);
             }
-            const uint64_t packed = ((uint64_t)id << pos_bits) | (uint64_t)i;
-            out[i] = packed;
-            for (int p = 0; p < passes; ++p)
-                atomicAdd(&h[p * kRadix + ((uint32_t)(packed >> (pos_bits + p * digit_bits)) & dmask)],
-                          1u);
         }
     }
-    if (ballot(bad) != 0ull && lane_id() == 0) atomicOr(status, kStatusRange);
-    __syncthreads();
-    for (int i = threadIdx.x; i < words; i += kThreads) {
-        const uint32_t c = h[i];
-        if (c) atomicAdd(&hist[i], c);
-    }
+    const bool any_bad = __syncthreads_or(bad);
+    uint32_t* mine = part + (int64_t)blockIdx.x * words;
+    for (int i = tid; i < words; i += kThreads) mine[i] = h[i];
+    if (tid == 0) pflag[blockIdx.x] = any_bad ? kStatusRange : 0u;
 }
 
 // One stable radix pass (digits of nbits <= 8 bits) in a single kernel.  A
@@ -221,7 +245,9 @@ __global__ __launch_bounds__(kThreads) void k_pack(const int64_t* __restrict__ i
 // tiles before + prefix of the waves before + rank.
 __global__ __launch_bounds__(kThreads) void k_onesweep(
     const uint64_t* __restrict__ in, uint64_t* __restrict__ out, int64_t n, int shift, int nbits,
-    const uint32_t* __restrict__ hist, uint32_t* lb, uint32_t* ticket, uint32_t* status) {
+    const uint32_t* __restrict__ part, int npack, int part_stride, const uint32_t* pflag,
+    uint32_t* lb, uint32_t* ticket, uint32_t* status) {
+    static_assert(kRadix == kThreads, "thread d owns digit d");
     __shared__ uint32_t cnt[kWaves][kRadix];
     __shared__ uint32_t base[kRadix];
     __shared__ uint32_t wt[kWaves];
@@ -249,6 +275,13 @@ __global__ __launch_bounds__(kThreads) void k_onesweep(
         key[r] = valid[r] ? in[i] : 0ull;
         dig[r] = (uint32_t)(key[r] >> shift) & ((1u << nbits) - 1u);
     }
+    // This pass's count of digit tid: the sum of the pack blocks' counts,
+    // loaded after the keys (loads complete in order, so the ranking below
+    // waits for the keys only) and needed only after the look-back.
+    uint32_t hpart[kPackBlocks];
+#pragma unroll
+    for (int g = 0; g < kPackBlocks; ++g)
+        hpart[g] = part[(int64_t)(g < npack ? g : 0) * part_stride + tid];
 #pragma unroll
     for (int r = 0; r < kIpt; ++r) {
         uint64_t peers = ballot(valid[r]);
@@ -289,7 +322,10 @@ __global__ __launch_bounds__(kThreads) void k_onesweep(
     }
     if (!ok) atomicOr(&s_bad, 1u);
     uint32_t total;
-    const uint32_t gbase = block_excl_scan(hist[d], wt, &total);
+    uint32_t hd = 0;
+#pragma unroll
+    for (int g = 0; g < kPackBlocks; ++g) hd += g < npack ? hpart[g] : 0u;
+    const uint32_t gbase = block_excl_scan(hd, wt, &total);
     base[d] = gbase + excl;
     __syncthreads();
     if (s_bad) {
@@ -302,6 +338,10 @@ __global__ __launch_bounds__(kThreads) void k_onesweep(
         const uint64_t dst = (uint64_t)base[dig[r]] + cnt[w][dig[r]] + rank[r];
         if (dst < (uint64_t)n) out[dst] = key[r];
     }
+    // First pass: the pack blocks' range flags go to the status word, by the
+    // last tile (no tile waits on it), for the kernels after this one.
+    if (pflag != nullptr && tile == (int64_t)gridDim.x - 1 && tid < npack && pflag[tid] != 0u)
+        atomicOr(status, kStatusRange);
 }
 
 // ------------------------------------------------------------- segments ---
@@ -500,14 +540,13 @@ __global__ __launch_bounds__(kSumThreads) void k_seg_sum(
     __shared__ uint32_t wheads[kSumWaves], wflags[kSumWaves];
     __shared__ int32_t wfirst_end[kSumWaves], wlast_seg[kSumWaves], wlast_head[kSumWaves];
     __shared__ uint32_t s_tile, s_excl, s_ok;
-    if (*status != 0u) {
-        if (blockIdx.x == 0 && threadIdx.x == 0) *d_nunique = 0;
-        return;
-    }
     const int tid = threadIdx.x;
     const int w = tid >> 6;
     const int lane = lane_id();
     const int sub = lane / LPR, sl = lane % LPR;
+    // The status word (an id out of range, a wait that timed out) is loaded
+    // while the ticket is taken; nothing is written before it is checked.
+    const uint32_t st0 = *status;
     if (tid == 0) s_tile = atomicAdd(ticket, 1u);
     __syncthreads();
     const int64_t tile = s_tile;
@@ -520,6 +559,10 @@ __global__ __launch_bounds__(kSumThreads) void k_seg_sum(
     const uint64_t key = s[i];
     const uint64_t prev = s[i > 0 ? i - 1 : 0];
     const uint64_t next = s[i + 1 < n ? i + 1 : i];
+    if (st0 != 0u) {
+        if (tile == 0 && tid == 0) *d_nunique = 0;
+        return;
+    }
     const uint64_t id = key >> pos_bits;
     const bool head = in && (i == 0 || (prev >> pos_bits) != id);
     const bool ends = in && (i + 1 >= n || (next >> pos_bits) != id);
@@ -757,10 +800,10 @@ __global__ __launch_bounds__(kFixWaves2 * kWave) void k_tile_fixup(
     const double* __restrict__ tfirst, const double* __restrict__ tlast, int64_t width,
     float* __restrict__ out_vals, int32_t* __restrict__ out_counts, const uint32_t* status) {
     __shared__ double part[kFixWaves2][kWave * V];
-    if (*status != 0u) return;
     const int64_t tile = blockIdx.x;
+    const uint32_t st0 = *status;  // loaded together with the crossing segment
     const int32_t seg = tcross[tile];
-    if (seg < 0) return;
+    if (st0 != 0u || seg < 0) return;
     const int w = (int)(threadIdx.x >> 6);
     const int lane = lane_id();
     const int64_t s0 = seg_start[seg], s1 = seg_start[seg + 1];
@@ -799,8 +842,13 @@ __global__ __launch_bounds__(kFixWaves2 * kWave) void k_tile_fixup(
     }
 }
 
-// Finite check of the lookup values (SPOPT_VALIDATE).
-__global__ void k_check_finite(const float* __restrict__ v, int64_t len, uint32_t* status) {
+// Finite check of the lookup values (SPOPT_VALIDATE), run after the pack
+// kernel (which zeroes the status word); block 0 also moves the pack blocks'
+// range flags into the status word.
+__global__ void k_check_finite(const float* __restrict__ v, int64_t len, const uint32_t* pflag,
+                               int npack, uint32_t* status) {
+    if (blockIdx.x == 0 && (int)threadIdx.x < npack && pflag[threadIdx.x] != 0u)
+        atomicOr(status, kStatusRange);
     bool bad = false;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < len;
          i += (int64_t)gridDim.x * blockDim.x)
@@ -860,7 +908,8 @@ extern "C" int coo_from_lookups(const int64_t* ids, const float* vals, int64_t n
     uint64_t* b = (uint64_t*)(ws + L.off_b);
     uint32_t* status = (uint32_t*)(ws + L.off_status);
     uint32_t* tickets = (uint32_t*)(ws + L.off_tickets);
-    uint32_t* hist = (uint32_t*)(ws + L.off_hist);
+    uint32_t* part = (uint32_t*)(ws + L.off_part);
+    uint32_t* pflag = (uint32_t*)(ws + L.off_pflag);
     uint32_t* words = (uint32_t*)(ws + L.off_words);
     uint32_t* sumwords = (uint32_t*)(ws + L.off_sumwords);
     int32_t* seg_start = (int32_t*)(ws + L.off_segstart);
@@ -868,26 +917,27 @@ extern "C" int coo_from_lookups(const int64_t* ids, const float* vals, int64_t n
     double* tfirst = (double*)(ws + L.off_tfirst);
     double* tlast = (double*)(ws + L.off_tlast);
 
-    // Zero the status word, tickets, histograms and look-back words.
-    const int64_t n16 = (int64_t)(L.clear_bytes / 16);
-    k_clear<<<(unsigned)(ceil_div(n16, 256) < 256 ? ceil_div(n16, 256) : 256), 256, 0, st>>>(
-        (uint4*)(ws + L.off_clear), n16);
+    // Pack and count digits; the pack kernel also zeroes the status word,
+    // tickets and look-back words of the kernels after it.
+    k_pack<<<(unsigned)L.npack, kThreads, 0, st>>>(ids, n, key_space, L.pos_bits, L.passes,
+                                                   L.digit_bits, a, part, pflag,
+                                                   (uint4*)(ws + L.off_clear),
+                                                   (int64_t)(L.clear_bytes / 16));
     SPOPT_LAUNCHED();
     const bool validate = (flags_arg & SPOPT_VALIDATE) != 0;
     if (validate) {
         const int64_t len = n * width;
         const int grid = (int)(ceil_div(len, 256) < 4096 ? ceil_div(len, 256) : 4096);
-        k_check_finite<<<grid, 256, 0, st>>>(vals, len, status);
+        k_check_finite<<<grid, 256, 0, st>>>(vals, len, pflag, (int)L.npack, status);
         SPOPT_LAUNCHED();
-    }
-    k_pack<<<(unsigned)L.ntiles, kThreads, 0, st>>>(ids, n, key_space, L.pos_bits, L.passes,
-                                                    L.digit_bits, a, hist, status);
-    SPOPT_LAUNCHED();
-    if (validate) {
         uint32_t h_status = 0;
         SPOPT_HIP(hipMemcpyAsync(&h_status, status, sizeof(uint32_t), hipMemcpyDeviceToHost, st));
         SPOPT_HIP(hipStreamSynchronize(st));
         if (h_status != 0u) return status_to_code(h_status, "coo_from_lookups");
+    } else if (L.passes == 0) {
+        // No radix pass folds the pack blocks' range flags into the status word.
+        k_check_finite<<<1, 256, 0, st>>>(vals, 0, pflag, (int)L.npack, status);
+        SPOPT_LAUNCHED();
     }
     uint64_t* src = a;
     uint64_t* dst = b;
@@ -896,9 +946,10 @@ extern "C" int coo_from_lookups(const int64_t* ids, const float* vals, int64_t n
         const int nbits = rem < L.digit_bits ? rem : L.digit_bits;
         const int shift = L.pos_bits + p * L.digit_bits;
         uint32_t* pwords = words + (int64_t)p * L.ntiles * kRadix;
-        const uint32_t* phist = hist + (int64_t)p * kRadix;
-        k_onesweep<<<(unsigned)L.ntiles, kThreads, 0, st>>>(src, dst, n, shift, nbits, phist,
-                                                            pwords, tickets + p, status);
+        k_onesweep<<<(unsigned)L.ntiles, kThreads, 0, st>>>(
+            src, dst, n, shift, nbits, part + (int64_t)p * kRadix, (int)L.npack,
+            L.passes * kRadix, p == 0 ? pflag : nullptr, pwords,
+            tickets + p, status);
         SPOPT_LAUNCHED();
         uint64_t* t = src;
         src = dst;
@@ -917,7 +968,8 @@ extern "C" int coo_from_lookups(const int64_t* ids, const float* vals, int64_t n
     auto sum = [&](auto kernel) {
         kernel<<<(unsigned)L.nsum, kSumThreads, 0, st>>>(
             sorted, n, L.pos_bits, L.nsum, vals, width, out_keys, out_vals, out_counts, d_nunique,
-            seg_start, tfirst, tlast, tcross, sumwords, tickets + kMaxPasses, status);
+            seg_start, tfirst, tlast, tcross, sumwords, tickets + kMaxPasses,
+            status);
     };
     if (V == 4)
         lpr == 16 ? sum(k_seg_sum<4, 16>) : sum(k_seg_sum<4, 32>);

@@ -143,6 +143,40 @@ def test_validate_range_and_nonfinite():
 def test_trusted_out_of_range_gives_empty_result():
     gk, gv, gc, u = _run(np.array([0, 9, 2], np.int64), np.ones((3, 2), np.float32), 5)
     assert u == 0
+    # one key only: no radix pass runs
+    gk, gv, gc, u = _run(np.array([0, 3, 0], np.int64), np.ones((3, 2), np.float32), 1)
+    assert u == 0
+
+
+@pytest.mark.parametrize("validate", [False, True])
+def test_out_of_range_in_a_later_pack_chunk(validate):
+    """70,000 lookups: more 2048-lookup chunks than pack blocks, so block 0
+    also packs chunk 32, which holds the bad id."""
+    n = 70000
+    ids = np.arange(n, dtype=np.int64) % 1000
+    ids[66000] = 1000
+    vals = np.ones((n, 1), np.float32)
+    if validate:
+        with pytest.raises(L.SparseOptError) as e:
+            _run(ids, vals, 1000, validate=True)
+        assert e.value.code == oracle.ERANGE
+    else:
+        assert _run(ids, vals, 1000)[3] == 0
+
+
+def test_a_million_lookups():
+    """A million lookups: 977 sort tiles and 3907 segment tiles, more than the
+    device runs at once, and about 15 chunks of 2048 lookups per pack block."""
+    rng = np.random.default_rng(11)
+    n, key_space = 1_000_000, 5_000_000
+    ids = rng.integers(0, key_space, size=n, dtype=np.int64)
+    ids[rng.random(n) < 0.1] = 4321
+    vals = rng.standard_normal((n, 1)).astype(np.float32)
+    gk, gv, gc, u = _run(ids, vals, key_space)
+    ok, ov, oc = oracle.coo_from_lookups(ids, vals, key_space)
+    assert u == ok.size
+    assert np.array_equal(gk, ok) and np.array_equal(gc, oc)
+    assert_sums_close(gv, ov, ids, ok, oc, vals)
 
 
 def test_workspace_too_small():
