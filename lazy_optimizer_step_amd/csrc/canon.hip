@@ -26,9 +26,10 @@
 namespace spopt {
 
 constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / kWave;
-constexpr int kIpt = 4;                         // items per thread
-constexpr int kTile = kThreads * kIpt;          // 1024 lookups per sort / segment tile
+constexpr int kIpt = 2;                         // items per thread (radix passes)
+constexpr int kSortThreads = 1024;              // threads of a radix-pass block
+constexpr int kSortWaves = kSortThreads / kWave;
+constexpr int kTile = kSortThreads * kIpt;      // lookups per radix-pass tile
 constexpr int kRadixBits = 8;                   // at most 256 buckets per radix pass
 constexpr int kRadix = 1 << kRadixBits;
 constexpr int kMaxPasses = 8;
@@ -236,21 +237,23 @@ __global__ __launch_bounds__(kThreads) void k_pack(const int64_t* __restrict__ i
 }
 
 // One stable radix pass (digits of nbits <= 8 bits) in a single kernel.  A
-// block takes the next tile ticket, ranks its 1024 items (wave w owns items [w*256, (w+1)*256) in four
-// rounds of 64: lanes holding the same digit are matched with one ballot per
-// digit bit, a lane's rank is the number of lower lanes with its digit plus
-// the wave's running count of that digit), publishes its per-digit counts,
-// and sums the counts of the tiles before it by decoupled look-back.  Its
-// items then go to  digit base (scan of the pass histogram) + prefix of the
-// tiles before + prefix of the waves before + rank.
-__global__ __launch_bounds__(kThreads) void k_onesweep(
+// block takes the next tile ticket, ranks its kTile items (wave w owns items
+// [w*256, (w+1)*256) in four rounds of 64: lanes holding the same digit are
+// matched with one ballot per digit bit, a lane's rank is the number of lower
+// lanes with its digit plus the wave's running count of that digit), and
+// thread d < kRadix publishes the tile's count of digit d and sums the counts
+// of the tiles before it by decoupled look-back.  Its items then go to
+// digit base (scan of the pass histogram) + prefix of the tiles before +
+// prefix of the waves before + rank.
+__global__ __launch_bounds__(kSortThreads) void k_onesweep(
     const uint64_t* __restrict__ in, uint64_t* __restrict__ out, int64_t n, int shift, int nbits,
     const uint32_t* __restrict__ part, int npack, int part_stride, const uint32_t* pflag,
     uint32_t* lb, uint32_t* ticket, uint32_t* status) {
-    static_assert(kRadix == kThreads, "thread d owns digit d");
-    __shared__ uint32_t cnt[kWaves][kRadix];
+    static_assert(kSortThreads >= kRadix && kRadix % kWave == 0,
+                  "threads 0..kRadix-1 own the digits (whole waves)");
+    __shared__ uint32_t cnt[kSortWaves][kRadix];
     __shared__ uint32_t base[kRadix];
-    __shared__ uint32_t wt[kWaves];
+    __shared__ uint32_t wt[kSortWaves];
     __shared__ uint32_t s_tile, s_bad;
     const int tid = threadIdx.x;
     const int w = tid >> 6;
@@ -259,9 +262,10 @@ __global__ __launch_bounds__(kThreads) void k_onesweep(
         s_tile = atomicAdd(ticket, 1u);
         s_bad = 0u;
     }
-    for (int i = tid; i < kWaves * kRadix; i += kThreads) (&cnt[0][0])[i] = 0;
+    for (int i = tid; i < kSortWaves * kRadix; i += kSortThreads) (&cnt[0][0])[i] = 0;
     __syncthreads();
     const int64_t tile = s_tile;
+    const bool owner = tid < kRadix;  // wave-uniform
 
     const int64_t first = tile * kTile + (int64_t)w * (kIpt * kWave);
     const uint64_t lt = lanemask_lt();
@@ -279,9 +283,11 @@ __global__ __launch_bounds__(kThreads) void k_onesweep(
     // loaded after the keys (loads complete in order, so the ranking below
     // waits for the keys only) and needed only after the look-back.
     uint32_t hpart[kPackBlocks];
+    if (owner) {
 #pragma unroll
-    for (int g = 0; g < kPackBlocks; ++g)
-        hpart[g] = part[(int64_t)(g < npack ? g : 0) * part_stride + tid];
+        for (int g = 0; g < kPackBlocks; ++g)
+            hpart[g] = part[(int64_t)(g < npack ? g : 0) * part_stride + tid];
+    }
 #pragma unroll
     for (int r = 0; r < kIpt; ++r) {
         uint64_t peers = ballot(valid[r]);
@@ -304,29 +310,30 @@ __global__ __launch_bounds__(kThreads) void k_onesweep(
 
     // Thread d owns digit d: prefix over the waves, then over earlier tiles.
     const int d = tid;
-    uint32_t run = 0;
-    for (int ww = 0; ww < kWaves; ++ww) {
-        const uint32_t c = cnt[ww][d];
-        cnt[ww][d] = run;
-        run += c;
-    }
-    uint32_t* mine = lb + tile * kRadix + d;
-    uint32_t excl = 0;
-    bool ok = true;
-    if (tile == 0) {
-        st_dev(mine, kLbInc | run);
-    } else {
-        st_dev(mine, kLbAgg | run);
-        ok = look_back(lb + d, tile, kRadix, &excl);
-        if (ok) st_dev(mine, kLbInc | (excl + run));
-    }
-    if (!ok) atomicOr(&s_bad, 1u);
-    uint32_t total;
-    uint32_t hd = 0;
+    uint32_t excl = 0, hd = 0;
+    if (owner) {
+        uint32_t run = 0;
+        for (int ww = 0; ww < kSortWaves; ++ww) {
+            const uint32_t c = cnt[ww][d];
+            cnt[ww][d] = run;
+            run += c;
+        }
+        uint32_t* mine = lb + tile * kRadix + d;
+        bool ok = true;
+        if (tile == 0) {
+            st_dev(mine, kLbInc | run);
+        } else {
+            st_dev(mine, kLbAgg | run);
+            ok = look_back(lb + d, tile, kRadix, &excl);
+            if (ok) st_dev(mine, kLbInc | (excl + run));
+        }
+        if (!ok) atomicOr(&s_bad, 1u);
 #pragma unroll
-    for (int g = 0; g < kPackBlocks; ++g) hd += g < npack ? hpart[g] : 0u;
-    const uint32_t gbase = block_excl_scan(hd, wt, &total);
-    base[d] = gbase + excl;
+        for (int g = 0; g < kPackBlocks; ++g) hd += g < npack ? hpart[g] : 0u;
+    }
+    uint32_t total;
+    const uint32_t gbase = block_excl_scan(hd, wt, &total);  // all threads; zeros past kRadix
+    if (owner) base[d] = gbase + excl;
     __syncthreads();
     if (s_bad) {
         if (tid == 0) atomicOr(status, kStatusTimeout);
@@ -946,7 +953,7 @@ extern "C" int coo_from_lookups(const int64_t* ids, const float* vals, int64_t n
         const int nbits = rem < L.digit_bits ? rem : L.digit_bits;
         const int shift = L.pos_bits + p * L.digit_bits;
         uint32_t* pwords = words + (int64_t)p * L.ntiles * kRadix;
-        k_onesweep<<<(unsigned)L.ntiles, kThreads, 0, st>>>(
+        k_onesweep<<<(unsigned)L.ntiles, kSortThreads, 0, st>>>(
             src, dst, n, shift, nbits, part + (int64_t)p * kRadix, (int)L.npack,
             L.passes * kRadix, p == 0 ? pflag : nullptr, pwords,
             tickets + p, status);

@@ -41,6 +41,7 @@ CASES = [
     ("four_passes", 2048, 1 << 30, 2, 0.0),
     ("33bit_keys", 1500, 6_400_000_000, 1, 0.3),
     ("all_distinct", 4096, 4096, 8, 0.0),
+    ("sort_tile_plus_one", 2049, 300, 2, 0.5),
     # every row-sum layout: 4-, 2- and 1-float lanes over 16-, 32- and 64-lane
     # groups, and rows wider than one group's columns
     ("width17", 3000, 5000, 17, 0.3),
