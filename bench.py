@@ -1,9 +1,10 @@
 """Benchmark of the sparse / lazy Adam step on one MI355X.
 
 One step is the whole hot path over one batch of raw lookups:
-  coo_from_lookups  (radix sort, dedupe, duplicate sums)
-  csr_from_coo      (row_offsets over every table row, col_indices, touched rows)
+  csr_from_lookups  (radix sort, dedupe, duplicate sums; row_offsets over every
+                     table row, col_indices, touched rows)
   sparse_adam_step  (DormancyDecay update of the touched coordinates)
+(--separate-calls: coo_from_lookups then csr_from_coo in place of the first.)
 on the 10M x 128 float32 table (65,536 Zipf(1.05) lookups per step, last_step
 int32 per coordinate).  Inputs for every step are generated up front and are
 resident in HBM before the timed region starts.
@@ -82,6 +83,9 @@ def parse():
                     help="budget of the CPU-oracle sample (0 disables it)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling HBM counters)")
+    ap.add_argument("--separate-calls", action="store_true",
+                    help="canonicalise with coo_from_lookups + csr_from_coo instead of the "
+                         "fused csr_from_lookups")
     ap.add_argument("--last-step-per-row", action="store_true",
                     help="keep one last_step per table row instead of one per coordinate")
     ap.add_argument("--host-state", action="store_true",
@@ -305,10 +309,28 @@ def main() -> int:
         return L.csr_from_coo(coo, R, Cc, row_offsets=row_offsets, col_indices=col_indices,
                               copy_values=False, stream=stream)
 
+    def fused(s: int):
+        return L.csr_from_lookups(ids_d[s], grads_d[s], R, out_keys=keys, out_vals=sums,
+                                  out_counts=counts, d_nunique=nuniq[s:s + 1],
+                                  row_offsets=row_offsets, col_indices=col_indices,
+                                  workspace=ws, stream=stream)[0]
+
+    # The calls that turn step s's lookups into its gradient, named for the
+    # breakdown; the last one's result is the gradient.
+    if args.separate_calls:
+        calls = [("coo_from_lookups", canon), ("csr_from_coo", csr)]
+    else:
+        calls = [("csr_from_lookups", fused)]
+
+    def prep(s: int):
+        g = None
+        for _, f in calls:
+            g = f(s)
+        return g
+
     log(f"warmup {W} steps")
     for s in range(W):
-        canon(s)
-        opt.step(csr(s), stream=stream)
+        opt.step(prep(s), stream=stream)
     torch.cuda.synchronize()
 
     # Timed region: K whole steps.  Events bracket the region and every update
@@ -321,8 +343,7 @@ def main() -> int:
     torch.cuda._sleep(cycles)
     ev.record(0, stream)
     for k, s in enumerate(range(W, W + K)):
-        canon(s)
-        g = csr(s)
+        g = prep(s)
         ev.record(2 + 2 * k, stream)
         opt.step(g, stream=stream)
         ev.record(3 + 2 * k, stream)
@@ -334,21 +355,24 @@ def main() -> int:
 
     # Breakdown (not part of the value): the same K inputs again, every call
     # bracketed by events.
-    bev = HipEvents(4 * K)
+    E = len(calls) + 2  # events per step: before each call, before and after the update
+    bev = HipEvents(E * K)
     torch.cuda._sleep(cycles)
     for k, s in enumerate(range(W, W + K)):
-        bev.record(4 * k, stream)
-        canon(s)
-        bev.record(4 * k + 1, stream)
-        g = csr(s)
-        bev.record(4 * k + 2, stream)
+        g = None
+        for c, (_, f) in enumerate(calls):
+            bev.record(E * k + c, stream)
+            g = f(s)
+        bev.record(E * k + E - 2, stream)
         opt.step(g, stream=stream)
-        bev.record(4 * k + 3, stream)
+        bev.record(E * k + E - 1, stream)
     torch.cuda.synchronize()
-    canon_t = np.array([bev.ms(4 * k, 4 * k + 1) for k in range(K)])
-    csr_t = np.array([bev.ms(4 * k + 1, 4 * k + 2) for k in range(K)])
-    upd_b = np.array([bev.ms(4 * k + 2, 4 * k + 3) for k in range(K)])
-    step_t = np.array([bev.ms(4 * k, 4 * k + 3) for k in range(K)])
+    breakdown = {}
+    for c, (name, _) in enumerate(calls):
+        breakdown[name] = pcts(np.array([bev.ms(E * k + c, E * k + c + 1) for k in range(K)]))
+    breakdown["sparse_adam_step"] = pcts(
+        np.array([bev.ms(E * k + E - 2, E * k + E - 1) for k in range(K)]))
+    breakdown["step"] = pcts(np.array([bev.ms(E * k, E * k + E - 1) for k in range(K)]))
     bev.close()
 
     # Cold regime (not part of the value): the same K inputs, a 512 MB buffer
@@ -358,8 +382,7 @@ def main() -> int:
     cev = HipEvents(2 * K)
     for k, s in enumerate(range(W, W + K)):
         scrub.fill_(float(k))
-        canon(s)
-        g = csr(s)
+        g = prep(s)
         cev.record(2 * k, stream)
         opt.step(g, stream=stream)
         cev.record(2 * k + 1, stream)
@@ -410,7 +433,8 @@ def main() -> int:
         "config": {"workload": w.name, "rows": R, "cols": Cc, "lookups_per_step": n,
                    "zipf_s": w.zipf_s, "mode": w.mode, "state": "p,m,v float32 + last_step int32 per " + ("row" if per_row else "coordinate")
                    + (", in mapped pinned host memory" if args.host_state else ", in HBM"),
-                   "mean_unique_rows": float(U.mean())},
+                   "mean_unique_rows": float(U.mean()),
+                   "calls": " + ".join([c for c, _ in calls] + ["sparse_adam_step"])},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled)",
@@ -424,8 +448,7 @@ def main() -> int:
                      "frac_of_device_copy": achieved / copy_gbs,
                      "cold": {"achieved": cold_achieved, "frac": cold_achieved / HBM_PEAK_GBS,
                               "mean_us": float(upd_cold.mean() * 1e3), "us": pcts(upd_cold)}},
-        "breakdown_us": {"coo_from_lookups": pcts(canon_t), "csr_from_coo": pcts(csr_t),
-                         "sparse_adam_step": pcts(upd_b), "step": pcts(step_t)},
+        "breakdown_us": breakdown,
         "read_rows": {"us": pcts(rr), "lookups": n,
                       "achieved_GBs": float((rr_bytes / (rr * 1e-3)).mean() / 1e9),
                       "bytes_per_lookup": 8 + 2 * 4 * Cc},

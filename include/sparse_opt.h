@@ -268,6 +268,30 @@ SPOPT_API int csr_from_coo(const spopt_coo* in, int64_t rows, int64_t cols, int3
                  int32_t* col_indices, float* values, int64_t* touched_rows,
                  int64_t* d_n_touched, void* stream, uint32_t flags);
 
+/* Raw lookups of full table rows -> full-row CSR gradient in one call: the
+ * same outputs, bit for bit, as coo_from_lookups(ids, vals, n, cols, rows, ...)
+ * followed by csr_from_coo on that COO with its values and row ids used in
+ * place (DiskSparseAdam "Safe Duplicate Aggregation & Sorted I/O"; P1
+ * CsrGradient::from_coo).  While it numbers the distinct ids, the segment
+ * kernel records how many lie below each block of 8192 rows, so the
+ * row_offsets blocks need no search, and the combine of tile-crossing sums
+ * shares one launch with them.
+ *   ids, vals, out_keys, out_vals, out_counts, d_nunique: as coo_from_lookups
+ *              with width = cols and key_space = rows.  out_keys[0, U) are
+ *              the CSR's touched rows and out_vals its values (U x cols,
+ *              row-major).
+ *   row_offsets device int32 [rows + 1] (required)
+ *   col_indices device int32 [n * cols] or NULL (full rows: 0..cols-1 each)
+ * Workspace: device, at least sparse_opt_workspace_size(n, cols, rows).
+ * Errors: as coo_from_lookups, plus SPOPT_EINVAL for a NULL row_offsets and
+ * SPOPT_EOVERFLOW for n * cols >= 2^31.  In trusted mode an out-of-range id
+ * gives U = 0 and all-zero row_offsets. */
+SPOPT_API int csr_from_lookups(const int64_t* ids, const float* vals, int64_t n, int64_t rows,
+                               int64_t cols, int64_t* out_keys, float* out_vals,
+                               int32_t* out_counts, int64_t* d_nunique, int32_t* row_offsets,
+                               int32_t* col_indices, void* workspace, size_t workspace_bytes,
+                               void* stream, uint32_t flags);
+
 /* CSR -> COO over the flattened rows*cols view: idx[j] = row*cols + col[j],
  * values copied (already ascending, so canonical).
  *   out_indices device int64 [nnz], out_values device float [nnz] or NULL.

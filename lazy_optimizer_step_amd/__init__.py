@@ -22,7 +22,8 @@ from . import _lib
 from ._lib import (FORMAT_COO, FORMAT_CSR, KIND_ADAM, KIND_SGD, MODE_DORMANCY, MODE_LAZY, TRUSTED,
                    VALIDATE, SparseOptError, check)
 
-__all__ = ["coo_from_lookups", "csr_from_coo", "csr_to_coo", "sparse_opt_workspace_size",
+__all__ = ["coo_from_lookups", "csr_from_coo", "csr_from_lookups", "csr_to_coo",
+           "sparse_opt_workspace_size",
            "sparse_opt_create", "sparse_adam_step", "sparse_sgd_step", "CooGradient",
            "CsrGradient", "SparseAdam", "SparseSgd", "SparseOptError", "TRUSTED", "VALIDATE",
            "read_rows", "HostArray"]
@@ -245,6 +246,51 @@ def csr_from_coo(coo: CooGradient, rows: int, cols: int, *, row_offsets=None, co
     return CsrGradient(row_offsets, col_indices, values, rows, cols,
                        touched_rows=tr if full else None,
                        n_touched=c.nnz if full else None, d_n_touched=dn if full else None)
+
+
+def csr_from_lookups(ids: torch.Tensor, vals: torch.Tensor, rows: int, *, out_keys=None,
+                     out_vals=None, out_counts=None, d_nunique=None, row_offsets=None,
+                     col_indices=None, want_col_indices=True, workspace=None, stream=None,
+                     validate: bool = False):
+    """Raw lookups of full table rows -> full-row CSR gradient in one call: the
+    result of coo_from_lookups then csr_from_coo(copy_values=False), bit for bit.
+    vals: (n, cols).  Returns (csr, counts, d_nunique): csr.touched_rows holds the
+    distinct ids and csr.values their summed rows (first U = d_nunique entries)."""
+    n = ids.numel()
+    cols = vals.shape[1] if vals.dim() == 2 else (vals.numel() // n if n else 1)
+    dev = ids.device
+    _need(ids, torch.int64, "ids")
+    _need(vals, torch.float32, "vals", n * cols)
+    if out_keys is None:
+        out_keys = torch.empty(max(n, 1), dtype=torch.int64, device=dev)
+    if out_vals is None:
+        out_vals = torch.empty((max(n, 1), cols), dtype=torch.float32, device=dev)
+    if out_counts is None:
+        out_counts = torch.empty(max(n, 1), dtype=torch.int32, device=dev)
+    if d_nunique is None:
+        d_nunique = torch.empty(1, dtype=torch.int64, device=dev)
+    if row_offsets is None:
+        row_offsets = torch.empty(rows + 1, dtype=torch.int32, device=dev)
+    if col_indices is None and want_col_indices:
+        col_indices = torch.empty(max(n * cols, 1), dtype=torch.int32, device=dev)
+    need = sparse_opt_workspace_size(n, cols, rows)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _need(out_keys, torch.int64, "out_keys", n)
+    _need(out_vals, torch.float32, "out_vals", n * cols)
+    _need(out_counts, torch.int32, "out_counts", n)
+    _need(d_nunique, torch.int64, "d_nunique", 1)
+    _need(row_offsets, torch.int32, "row_offsets", rows + 1)
+    if col_indices is not None:
+        _need(col_indices, torch.int32, "col_indices", n * cols)
+    _need(workspace, torch.uint8, "workspace")
+    check(_lib.lib().csr_from_lookups(_ptr(ids), _ptr(vals), n, rows, cols, _ptr(out_keys),
+                                      _ptr(out_vals), _ptr(out_counts), _ptr(d_nunique),
+                                      _ptr(row_offsets), _ptr(col_indices), _ptr(workspace),
+                                      workspace.numel(), _stream(stream), _flags(validate)))
+    csr = CsrGradient(row_offsets, col_indices, out_vals, rows, cols, touched_rows=out_keys,
+                      n_touched=n, d_n_touched=d_nunique)
+    return csr, out_counts, d_nunique
 
 
 def csr_to_coo(csr: CsrGradient, *, out_indices=None, out_values=None, nnz: int | None = None,

@@ -87,6 +87,9 @@ def lib() -> C.CDLL:
         L.coo_from_lookups.restype = C.c_int
         L.csr_from_coo.argtypes = [C.POINTER(Coo), I64, I64, P, P, P, P, P, P, U32]
         L.csr_from_coo.restype = C.c_int
+        L.csr_from_lookups.argtypes = [P, P, I64, I64, I64, P, P, P, P, P, P, P, C.c_size_t, P,
+                                       U32]
+        L.csr_from_lookups.restype = C.c_int
         L.csr_to_coo.argtypes = [C.POINTER(Csr), P, P, P, U32]
         L.csr_to_coo.restype = C.c_int
         L.sparse_adam_step.argtypes = [P, C.POINTER(Grad), P, U32]
@@ -112,5 +115,6 @@ def check(rc: int) -> None:
 
 EXPORTED = ("sparse_opt_create", "sparse_opt_destroy", "sparse_opt_get_step", "sparse_opt_set_step",
             "sparse_opt_last_error", "sparse_opt_workspace_size", "coo_from_lookups",
-            "csr_from_coo", "csr_to_coo", "sparse_adam_step", "sparse_sgd_step", "read_rows",
+            "csr_from_coo", "csr_from_lookups", "csr_to_coo", "sparse_adam_step",
+            "sparse_sgd_step", "read_rows",
             "sparse_opt_host_alloc", "sparse_opt_host_free", "sparse_opt_host_device_pointer")

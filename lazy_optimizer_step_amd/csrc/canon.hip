@@ -22,6 +22,7 @@
 
 
 #include "common.hpp"
+#include "csr_full.hpp"
 
 namespace spopt {
 
@@ -39,6 +40,9 @@ constexpr int kSumRows = 32;                    // sorted lookups per wave (lane
 constexpr int kSumTile = kSumWaves * kSumRows;  // sorted lookups per such block
 constexpr int kTilePartials = 8;                // partials one wave adds alone in the combine
 constexpr int kFixWaves2 = 16;                  // waves of the combining block
+constexpr int kFixRuns = 16;                    // runs of a segment with more partials
+// Per-block key counts for csr_from_lookups are kept for tables of fewer rows.
+constexpr int64_t kBndMaxRows = ((int64_t)1 << 31) - 1;
 
 // Decoupled look-back.  A tile publishes one 32-bit word per count:
 // bits 31..30 its state (aggregate of this tile / inclusive prefix through
@@ -66,7 +70,8 @@ struct CanonLayout {
     int64_t ntiles, nsum;
     int64_t npack;  // blocks of the pack kernel
     size_t off_a, off_b, off_part, off_pflag, off_clear, clear_bytes, off_status, off_tickets,
-        off_sumwords, off_words, off_segstart, off_tcross, off_tfirst, off_tlast, total;
+        off_sumwords, off_words, off_segstart, off_tcross, off_tfirst, off_tlast, off_bnd,
+        bnd_entries, total;
 };
 
 static int bits_for(uint64_t x) {  // bits needed to represent values in [0, x)
@@ -116,6 +121,9 @@ static bool canon_layout(int64_t n, int64_t width, int64_t key_space, CanonLayou
     L->off_tcross = take(sizeof(int32_t) * (size_t)L->nsum);
     L->off_tfirst = take(sizeof(double) * (size_t)L->nsum * (size_t)width);
     L->off_tlast = take(sizeof(double) * (size_t)L->nsum * (size_t)width);
+    // #ids below each kRoBits-row block of a key_space-row table (csr_from_lookups).
+    L->bnd_entries = key_space <= kBndMaxRows ? (size_t)(key_space / kRoBits + 1) : 0;
+    L->off_bnd = take(sizeof(int32_t) * L->bnd_entries);
     L->total = o;
     return true;
 }
@@ -536,7 +544,8 @@ __global__ __launch_bounds__(kSumThreads) void k_seg_sum(
     const float* __restrict__ vals, int64_t width, int64_t* __restrict__ out_keys,
     float* __restrict__ out_vals, int32_t* __restrict__ out_counts, int64_t* d_nunique,
     int32_t* __restrict__ seg_start, double* __restrict__ tfirst, double* __restrict__ tlast,
-    int32_t* __restrict__ tcross, uint32_t* words, uint32_t* ticket, uint32_t* status) {
+    int32_t* __restrict__ tcross, uint32_t* words, uint32_t* ticket, uint32_t* status,
+    int32_t* __restrict__ bnd, int64_t key_space) {
     constexpr int RPI = kWave / LPR;
     constexpr int U = kSumRows / RPI;  // load instructions per block of columns
     constexpr int CB = LPR * V;        // columns per block of columns
@@ -625,6 +634,12 @@ __global__ __launch_bounds__(kSumThreads) void k_seg_sum(
     if (head) {
         out_keys[seg] = (int64_t)id;
         seg_start[seg] = (int32_t)i;
+        if (bnd != nullptr) {
+            // Row blocks of kRoBits rows whose first row lies in (previous id,
+            // id] have exactly seg ids below them.
+            const int64_t b0 = i == 0 ? 0 : (int64_t)((prev >> pos_bits) / kRoBits) + 1;
+            for (int64_t b = b0; b <= (int64_t)(id / kRoBits); ++b) bnd[b] = seg;
+        }
     }
     if (kind == kFlushOut) {
         const int first = 63 - __builtin_clzll(hm & upto);
@@ -634,6 +649,10 @@ __global__ __launch_bounds__(kSumThreads) void k_seg_sum(
         const uint32_t u = s_excl + tile_heads;
         *d_nunique = (int64_t)u;
         seg_start[u] = (int32_t)n;
+        if (bnd != nullptr) {  // blocks past the last id: all U ids below them
+            const int64_t last = (int64_t)(s[n - 1] >> pos_bits);
+            for (int64_t b = last / kRoBits + 1; b <= key_space / kRoBits; ++b) bnd[b] = (int32_t)u;
+        }
     }
 
     // ---- 2. and 3., one block of columns at a time
@@ -797,17 +816,17 @@ __device__ __forceinline__ void add_partials(double (&acc)[V], const double* tfi
 // Segments that cross tiles, one block per tile that starts one (tcross):
 // m partials (tlast of the start tile, tfirst of each following tile up to
 // the one where it ends).  The order of the additions depends on m only, so
-// the result is the same run to run: up to kTilePartials partials are added in
-// tile order by wave 0; beyond, [0, m) is cut into 16 equal runs, wave r adds
-// run r in tile order, and wave 0 adds the 16 run sums in run order.  The
-// block also writes the segment's count.
-template <int V>
-__global__ __launch_bounds__(kFixWaves2 * kWave) void k_tile_fixup(
-    const int32_t* __restrict__ tcross, const int32_t* __restrict__ seg_start,
+// the result is the same run to run and whatever the block's shape: up to
+// kTilePartials partials are added in tile order by wave 0; beyond, [0, m) is
+// cut into kFixRuns equal runs, each added in tile order (run r by wave
+// r mod W), and wave 0 adds the run sums in run order.  The block also writes
+// the segment's count.  part: LDS, kFixRuns rows.
+template <int V, int W>
+__device__ __forceinline__ void tile_fixup_body(
+    int64_t tile, const int32_t* __restrict__ tcross, const int32_t* __restrict__ seg_start,
     const double* __restrict__ tfirst, const double* __restrict__ tlast, int64_t width,
-    float* __restrict__ out_vals, int32_t* __restrict__ out_counts, const uint32_t* status) {
-    __shared__ double part[kFixWaves2][kWave * V];
-    const int64_t tile = blockIdx.x;
+    float* __restrict__ out_vals, int32_t* __restrict__ out_counts, const uint32_t* status,
+    double (*part)[kWave * V]) {
     const uint32_t st0 = *status;  // loaded together with the crossing segment
     const int32_t seg = tcross[tile];
     if (st0 != 0u || seg < 0) return;
@@ -828,25 +847,66 @@ __global__ __launch_bounds__(kFixWaves2 * kWave) void k_tile_fixup(
             }
             continue;
         }
-        const int64_t lo = m * w / kFixWaves2, hi = m * (w + 1) / kFixWaves2;
-        double acc[V];
+        for (int r = w; r < kFixRuns; r += W) {
+            const int64_t lo = m * r / kFixRuns, hi = m * (r + 1) / kFixRuns;
+            double acc[V];
 #pragma unroll
-        for (int v = 0; v < V; ++v) acc[v] = 0.0;
-        add_partials<V, (V == 4 ? 4 : 8)>(acc, tfirst, tlast, tile, lo, hi, width, col);
+            for (int v = 0; v < V; ++v) acc[v] = 0.0;
+            add_partials<V, (V == 4 ? 4 : 8)>(acc, tfirst, tlast, tile, lo, hi, width, col);
 #pragma unroll
-        for (int v = 0; v < V; ++v) part[w][lane * V + v] = acc[v];
+            for (int v = 0; v < V; ++v) part[r][lane * V + v] = acc[v];
+        }
         __syncthreads();
         if (w == 0) {
             double tot[V];
 #pragma unroll
             for (int v = 0; v < V; ++v) tot[v] = part[0][lane * V + v];
-            for (int ww = 1; ww < kFixWaves2; ++ww)
+            for (int r = 1; r < kFixRuns; ++r)
 #pragma unroll
-                for (int v = 0; v < V; ++v) tot[v] += part[ww][lane * V + v];
+                for (int v = 0; v < V; ++v) tot[v] += part[r][lane * V + v];
             store_row<V>(out_vals + (int64_t)seg * width + col, tot, col, width);
         }
         __syncthreads();
     }
+}
+
+template <int V>
+__global__ __launch_bounds__(kFixWaves2 * kWave) void k_tile_fixup(
+    const int32_t* __restrict__ tcross, const int32_t* __restrict__ seg_start,
+    const double* __restrict__ tfirst, const double* __restrict__ tlast, int64_t width,
+    float* __restrict__ out_vals, int32_t* __restrict__ out_counts, const uint32_t* status) {
+    __shared__ double part[kFixRuns][kWave * V];
+    tile_fixup_body<V, kFixWaves2>(blockIdx.x, tcross, seg_start, tfirst, tlast, width, out_vals,
+                                   out_counts, status, part);
+}
+
+// csr_from_lookups after the segment kernel, in one launch: the tile combine
+// (one block per segment tile, first in dispatch order: a latency chain), then
+// the col_indices blocks, then the row_offsets blocks, which read their ids'
+// bounds from the per-block counts the segment kernel wrote (bnd; NULL: they
+// search the ids).  The combine runs on 4 waves, one double per lane, so that
+// the launch keeps 8 blocks per CU; its additions are the same as above.
+template <bool VEC>
+__global__ __launch_bounds__(kRoThreads) void k_fix_csr(
+    const int32_t* __restrict__ tcross, const int32_t* __restrict__ seg_start,
+    const double* __restrict__ tfirst, const double* __restrict__ tlast, int64_t cols,
+    float* __restrict__ out_vals, int32_t* __restrict__ out_counts, const uint32_t* status,
+    int64_t nfix, const int64_t* __restrict__ keys, const int64_t* d_nnz, int64_t nnz_host,
+    int64_t rows, int32_t* __restrict__ row_offsets, int64_t nblk_ci,
+    int32_t* __restrict__ col_indices, const int32_t* bnd) {
+    __shared__ double part[kFixRuns][kWave];
+    const int64_t b = blockIdx.x;
+    if (b < nfix) {
+        tile_fixup_body<1, kRoThreads / kWave>(b, tcross, seg_start, tfirst, tlast, cols,
+                                               out_vals, out_counts, status, part);
+        return;
+    }
+    const int64_t nnz = *d_nnz < nnz_host ? *d_nnz : nnz_host;
+    if (b < nfix + nblk_ci) {
+        csr_col_block(b - nfix, nblk_ci, nnz, cols, col_indices);
+        return;
+    }
+    csr_row_block<VEC>(b - nfix - nblk_ci, keys, nnz_host, nnz, rows, cols, row_offsets, bnd);
 }
 
 // Finite check of the lookup values (SPOPT_VALIDATE), run after the pack
@@ -886,22 +946,26 @@ extern "C" int sparse_opt_workspace_size(int64_t n, int64_t width, int64_t key_s
     return SPOPT_OK;
 }
 
-extern "C" int coo_from_lookups(const int64_t* ids, const float* vals, int64_t n, int64_t width,
-                                int64_t key_space, int64_t* out_keys, float* out_vals,
-                                int32_t* out_counts, int64_t* d_nunique, void* workspace,
-                                size_t workspace_bytes, void* stream, uint32_t flags_arg) {
-    hipStream_t st = (hipStream_t)stream;
+// The canonicalisation of coo_from_lookups, shared with csr_from_lookups:
+// `what` names the entry point in errors; bnd (NULL: not wanted) receives the
+// per-row-block id counts; with fixup false the tile combine is left to the
+// caller's launch.
+static int canon_run(const char* what, const int64_t* ids, const float* vals, int64_t n,
+                     int64_t width, int64_t key_space, int64_t* out_keys, float* out_vals,
+                     int32_t* out_counts, int64_t* d_nunique, void* workspace,
+                     size_t workspace_bytes, hipStream_t st, uint32_t flags_arg, int32_t* bnd,
+                     bool fixup) {
     CanonLayout L;
-    if (n >= ((int64_t)1 << 30)) return fail(SPOPT_EOVERFLOW, "coo_from_lookups: n >= 2^30");
+    if (n >= ((int64_t)1 << 30)) return fail(SPOPT_EOVERFLOW, "%s: n >= 2^30", what);
     if (!canon_layout(n, width, key_space, &L))
-        return fail(SPOPT_EINVAL, "coo_from_lookups: bad n=%lld width=%lld key_space=%lld",
+        return fail(SPOPT_EINVAL, "%s: bad n=%lld width=%lld key_space=%lld", what,
                     (long long)n, (long long)width, (long long)key_space);
-    if (d_nunique == nullptr) return fail(SPOPT_EINVAL, "coo_from_lookups: d_nunique is NULL");
+    if (d_nunique == nullptr) return fail(SPOPT_EINVAL, "%s: d_nunique is NULL", what);
     if (n > 0 && (ids == nullptr || vals == nullptr || out_keys == nullptr ||
                   out_vals == nullptr || out_counts == nullptr))
-        return fail(SPOPT_EINVAL, "coo_from_lookups: NULL array");
+        return fail(SPOPT_EINVAL, "%s: NULL array", what);
     if (n > 0 && (workspace == nullptr || workspace_bytes < L.total))
-        return fail(SPOPT_EWORKSPACE, "coo_from_lookups: workspace %zu bytes, need %zu",
+        return fail(SPOPT_EWORKSPACE, "%s: workspace %zu bytes, need %zu", what,
                     workspace_bytes, L.total);
     if (n == 0) {
         k_write_i64<<<1, 1, 0, st>>>(d_nunique, 0);
@@ -909,7 +973,7 @@ extern "C" int coo_from_lookups(const int64_t* ids, const float* vals, int64_t n
         return SPOPT_OK;
     }
     if (((uintptr_t)workspace & 255u) != 0)
-        return fail(SPOPT_EWORKSPACE, "coo_from_lookups: workspace must be 256-byte aligned");
+        return fail(SPOPT_EWORKSPACE, "%s: workspace must be 256-byte aligned", what);
     char* ws = (char*)workspace;
     uint64_t* a = (uint64_t*)(ws + L.off_a);
     uint64_t* b = (uint64_t*)(ws + L.off_b);
@@ -940,7 +1004,7 @@ extern "C" int coo_from_lookups(const int64_t* ids, const float* vals, int64_t n
         uint32_t h_status = 0;
         SPOPT_HIP(hipMemcpyAsync(&h_status, status, sizeof(uint32_t), hipMemcpyDeviceToHost, st));
         SPOPT_HIP(hipStreamSynchronize(st));
-        if (h_status != 0u) return status_to_code(h_status, "coo_from_lookups");
+        if (h_status != 0u) return status_to_code(h_status, what);
     } else if (L.passes == 0) {
         // No radix pass folds the pack blocks' range flags into the status word.
         k_check_finite<<<1, 256, 0, st>>>(vals, 0, pflag, (int)L.npack, status);
@@ -976,7 +1040,7 @@ extern "C" int coo_from_lookups(const int64_t* ids, const float* vals, int64_t n
         kernel<<<(unsigned)L.nsum, kSumThreads, 0, st>>>(
             sorted, n, L.pos_bits, L.nsum, vals, width, out_keys, out_vals, out_counts, d_nunique,
             seg_start, tfirst, tlast, tcross, sumwords, tickets + kMaxPasses,
-            status);
+            status, bnd, key_space);
     };
     if (V == 4)
         lpr == 16 ? sum(k_seg_sum<4, 16>) : sum(k_seg_sum<4, 32>);
@@ -987,6 +1051,7 @@ extern "C" int coo_from_lookups(const int64_t* ids, const float* vals, int64_t n
                                                     : sum(k_seg_sum<1, 64>);
     SPOPT_LAUNCHED();
 
+    if (!fixup) return SPOPT_OK;
     // The combine: V doubles per lane over blocks of 64*V columns.
     const int FV = (width % 4 == 0 && width >= 256 && (al & 15u) == 0) ? 4
                    : (width % 2 == 0 && width >= 128 && (al & 7u) == 0) ? 2 : 1;
@@ -1001,6 +1066,72 @@ extern "C" int coo_from_lookups(const int64_t* ids, const float* vals, int64_t n
         fix(k_tile_fixup<2>);
     else
         fix(k_tile_fixup<1>);
+    SPOPT_LAUNCHED();
+    return SPOPT_OK;
+}
+
+extern "C" int coo_from_lookups(const int64_t* ids, const float* vals, int64_t n, int64_t width,
+                                int64_t key_space, int64_t* out_keys, float* out_vals,
+                                int32_t* out_counts, int64_t* d_nunique, void* workspace,
+                                size_t workspace_bytes, void* stream, uint32_t flags) {
+    return canon_run("coo_from_lookups", ids, vals, n, width, key_space, out_keys, out_vals,
+                     out_counts, d_nunique, workspace, workspace_bytes, (hipStream_t)stream, flags,
+                     nullptr, true);
+}
+
+extern "C" int csr_from_lookups(const int64_t* ids, const float* vals, int64_t n, int64_t rows,
+                                int64_t cols, int64_t* out_keys, float* out_vals,
+                                int32_t* out_counts, int64_t* d_nunique, int32_t* row_offsets,
+                                int32_t* col_indices, void* workspace, size_t workspace_bytes,
+                                void* stream, uint32_t flags) {
+    hipStream_t st = (hipStream_t)stream;
+    if (row_offsets == nullptr || rows < 1 || cols < 1)
+        return fail(SPOPT_EINVAL, "csr_from_lookups: NULL row_offsets or bad size");
+    if (n * cols >= ((int64_t)1 << 31))
+        return fail(SPOPT_EOVERFLOW, "csr_from_lookups: %lld entries do not fit int32 offsets",
+                    (long long)(n * cols));
+    CanonLayout L;
+    if (!canon_layout(n, cols, rows, &L))
+        return fail(SPOPT_EINVAL, "csr_from_lookups: bad n=%lld cols=%lld rows=%lld",
+                    (long long)n, (long long)cols, (long long)rows);
+    const bool fused = (cols & 3) == 0 && (col_indices == nullptr || aligned16(col_indices));
+    if (!fused) {
+        // Columns not in 16-byte groups: the two calls one after the other.
+        int rc = canon_run("csr_from_lookups", ids, vals, n, cols, rows, out_keys, out_vals,
+                           out_counts, d_nunique, workspace, workspace_bytes, st, flags, nullptr,
+                           true);
+        if (rc) return rc;
+        spopt_coo coo{rows, cols, n, d_nunique, out_keys, out_vals};
+        return csr_from_coo(&coo, rows, cols, row_offsets, col_indices, out_vals, nullptr,
+                            nullptr, stream, 0u);
+    }
+    char* ws = (char*)workspace;
+    int32_t* bnd = (n > 0 && L.bnd_entries > 0) ? (int32_t*)(ws + L.off_bnd) : nullptr;
+    int rc = canon_run("csr_from_lookups", ids, vals, n, cols, rows, out_keys, out_vals,
+                       out_counts, d_nunique, workspace, workspace_bytes, st, flags, bnd, false);
+    if (rc) return rc;
+    const int64_t nfix = n > 0 ? L.nsum : 0;
+    const int64_t nblk_ro = rows / kRoBits + 1;
+    int64_t nblk_ci = 0;
+    if (col_indices != nullptr) {
+        nblk_ci = ceil_div(n * cols / 4, kRoThreads);
+        if (nblk_ci > 1024) nblk_ci = 1024;
+        if (nblk_ci < 1) nblk_ci = 1;
+    }
+    const int32_t* tcross = n > 0 ? (const int32_t*)(ws + L.off_tcross) : nullptr;
+    const int32_t* seg_start = n > 0 ? (const int32_t*)(ws + L.off_segstart) : nullptr;
+    const double* tfirst = n > 0 ? (const double*)(ws + L.off_tfirst) : nullptr;
+    const double* tlast = n > 0 ? (const double*)(ws + L.off_tlast) : nullptr;
+    const uint32_t* status = n > 0 ? (const uint32_t*)(ws + L.off_status) : nullptr;
+    auto go = [&](auto kernel) {
+        kernel<<<(unsigned)(nfix + nblk_ci + nblk_ro), kRoThreads, 0, st>>>(
+            tcross, seg_start, tfirst, tlast, cols, out_vals, out_counts, status, nfix, out_keys,
+            d_nunique, n, rows, row_offsets, nblk_ci, col_indices, bnd);
+    };
+    if (aligned16(row_offsets))
+        go(k_fix_csr<true>);
+    else
+        go(k_fix_csr<false>);
     SPOPT_LAUNCHED();
     return SPOPT_OK;
 }

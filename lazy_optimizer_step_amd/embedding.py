@@ -4,18 +4,17 @@ The steps either side of the optimizer, as the DiskSparseAdam README's training
 loop uses them (read_rows for the forward pass, then step with the lookup
 indices and the gradient rows): ``forward(ids)`` gathers the current rows with
 ``read_rows``; autograd hands the backward the per-lookup gradient rows, in
-lookup order, which is the value layout ``coo_from_lookups`` sorts and sums
-directly (no re-layout); ``step()`` canonicalises them, assembles the CSR
-gradient over every table row and applies the optimizer to the touched rows
-only.  Every step of the path runs in the library's kernels; this module only
+lookup order, which is the value layout ``csr_from_lookups`` sorts and sums
+directly (no re-layout); ``step()`` canonicalises them and assembles the CSR
+gradient over every table row in that one call, then applies the optimizer to
+the touched rows only.  Every step of the path runs in the library's kernels; this module only
 keeps the buffers and the order of the calls.
 """
 from __future__ import annotations
 
 import torch
 
-from . import (CooGradient, SparseAdam, SparseSgd, coo_from_lookups, csr_from_coo, read_rows,
-               sparse_opt_workspace_size)
+from . import SparseAdam, SparseSgd, csr_from_lookups, read_rows, sparse_opt_workspace_size
 
 
 class _Lookup(torch.autograd.Function):
@@ -101,12 +100,9 @@ class SparseEmbedding(torch.nn.Module):
         self._pending.clear()
         n = ids.numel()
         b = self._buffers_for(n)
-        R, C = self.num_rows, self.dim
-        coo_from_lookups(ids, grads, R, out_keys=b["keys"], out_vals=b["sums"],
-                         out_counts=b["counts"], d_nunique=b["U"], workspace=b["ws"],
-                         stream=stream)
-        coo = CooGradient(b["keys"], b["sums"], dim=R, width=C, nnz=n, d_nnz=b["U"])
-        csr = csr_from_coo(coo, R, C, row_offsets=b["row_offsets"], want_col_indices=False,
-                           copy_values=False, stream=stream)
+        csr, _, _ = csr_from_lookups(ids, grads, self.num_rows, out_keys=b["keys"],
+                                     out_vals=b["sums"], out_counts=b["counts"],
+                                     d_nunique=b["U"], row_offsets=b["row_offsets"],
+                                     want_col_indices=False, workspace=b["ws"], stream=stream)
         self.opt.step(csr, stream=stream)
         return n

@@ -103,6 +103,18 @@ def test_handle_step_counter_and_shape_errors():
         L_.sparse_opt_destroy(h)
 
 
+def test_csr_from_lookups_host_errors():
+    """Argument errors of the fused call are found before any device work."""
+    f = _lib.lib().csr_from_lookups
+    args = lambda n=10, rows=100, cols=4, ro=FAKE, ws=1 << 20: (
+        FAKE, FAKE, n, rows, cols, FAKE, FAKE, FAKE, FAKE, ro, None, FAKE, ws, None, 0)
+    assert f(*args(ro=None)) == _lib.EINVAL
+    assert f(*args(rows=0)) == _lib.EINVAL
+    assert f(*args(n=1 << 24, cols=128)) == _lib.EOVERFLOW      # n * cols >= 2^31
+    assert f(*args(n=1 << 30, cols=1)) == _lib.EOVERFLOW        # n >= 2^30
+    assert f(*args(ws=16)) == _lib.EWORKSPACE
+
+
 def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True)
