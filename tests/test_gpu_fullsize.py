@@ -1,5 +1,6 @@
 """GPU parity at the workloads' full sizes, in the launch configuration the
-benchmark uses (raw lookups -> coo_from_lookups -> csr_from_coo -> step).
+benchmark uses (raw lookups -> csr_from_lookups -> step; the 1M x 64 run takes
+the two calls coo_from_lookups -> csr_from_coo instead).
 
 * 1M x 64 Lazy, 100 steps: every coordinate of the table against the oracle.
 * 2M x 256 partial rows, SGD then DormancyDecay Adam, 100 steps each: every
@@ -41,10 +42,11 @@ def _free_gpu():
 
 
 class LookupPath:
-    """The benchmark's per-step calls with preallocated outputs."""
+    """The benchmark's per-step calls with preallocated outputs: the fused
+    csr_from_lookups, or (fused=False) coo_from_lookups then csr_from_coo."""
 
-    def __init__(self, opt, rows, cols, n):
-        self.opt, self.rows, self.cols, self.n = opt, rows, cols, n
+    def __init__(self, opt, rows, cols, n, fused=True):
+        self.opt, self.rows, self.cols, self.n, self.fused = opt, rows, cols, n, fused
         self.keys = torch.empty(n, dtype=torch.int64, device="cuda")
         self.sums = torch.empty((n, cols), dtype=torch.float32, device="cuda")
         self.counts = torch.empty(n, dtype=torch.int32, device="cuda")
@@ -55,12 +57,19 @@ class LookupPath:
         self.col_indices = torch.empty(n * cols, dtype=torch.int32, device="cuda")
 
     def step(self, ids, grads):
-        L.coo_from_lookups(dev(ids), dev(grads), self.rows, out_keys=self.keys, out_vals=self.sums,
-                           out_counts=self.counts, d_nunique=self.U, workspace=self.ws)
-        coo = L.CooGradient(self.keys, self.sums, dim=self.rows, width=self.cols, nnz=self.n,
-                            d_nnz=self.U)
-        csr = L.csr_from_coo(coo, self.rows, self.cols, row_offsets=self.row_offsets,
-                             col_indices=self.col_indices, copy_values=False)
+        if self.fused:
+            csr, _, _ = L.csr_from_lookups(dev(ids), dev(grads), self.rows, out_keys=self.keys,
+                                           out_vals=self.sums, out_counts=self.counts,
+                                           d_nunique=self.U, row_offsets=self.row_offsets,
+                                           col_indices=self.col_indices, workspace=self.ws)
+        else:
+            L.coo_from_lookups(dev(ids), dev(grads), self.rows, out_keys=self.keys,
+                               out_vals=self.sums, out_counts=self.counts, d_nunique=self.U,
+                               workspace=self.ws)
+            coo = L.CooGradient(self.keys, self.sums, dim=self.rows, width=self.cols,
+                                nnz=self.n, d_nnz=self.U)
+            csr = L.csr_from_coo(coo, self.rows, self.cols, row_offsets=self.row_offsets,
+                                 col_indices=self.col_indices, copy_values=False)
         self.opt.step(csr)
 
 
@@ -72,7 +81,7 @@ def test_table_1M_x_64_lazy_full_compare():
                       mode="lazy")
     gpu = L.SparseAdam(dev(p0), lr=h["lr"], beta1=h["beta1"], beta2=h["beta2"], eps=h["eps"],
                        mode="lazy")
-    path = LookupPath(gpu, w.rows, w.cols, w.n_lookups)
+    path = LookupPath(gpu, w.rows, w.cols, w.n_lookups, fused=False)
     for s, (ids, grads) in enumerate(synth.lookups_many(w, range(w.steps))):
         keys, sums, counts = oracle.coo_from_lookups(ids, grads, w.rows)
         ro, ci, cv = oracle.csr_from_coo(keys, sums, w.rows, w.cols, w.rows, w.cols)
