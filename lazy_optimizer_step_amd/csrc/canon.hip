@@ -34,9 +34,9 @@ constexpr int kTile = kSortThreads * kIpt;      // lookups per radix-pass tile
 constexpr int kRadixBits = 8;                   // at most 256 buckets per radix pass
 constexpr int kRadix = 1 << kRadixBits;
 constexpr int kMaxPasses = 8;
-constexpr int kSumWaves = 8;                    // waves per segment-and-sum block
+constexpr int kSumWaves = 16;                   // waves per segment-and-sum block
 constexpr int kSumThreads = kSumWaves * kWave;
-constexpr int kSumRows = 32;                    // sorted lookups per wave (lanes 0..31)
+constexpr int kSumRows = 16;                    // sorted lookups per wave (lanes 0..15)
 constexpr int kSumTile = kSumWaves * kSumRows;  // sorted lookups per such block
 constexpr int kTilePartials = 8;                // partials one wave adds alone in the combine
 constexpr int kFixWaves2 = 16;                  // waves of the combining block
@@ -512,8 +512,11 @@ __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0
 
 
 // Segments and their sums in one pass over the sorted lookups.  A block takes
-// the next tile ticket (kSumTile = 256 lookups); wave w owns the 32 lookups
-// [32w, 32w + 32) of the tile, lane j < 32 lookup i0 + j.
+// the next tile ticket (kSumTile = 256 lookups); wave w owns the kSumRows =
+// 16 lookups [16w, 16w + 16) of the tile, lane j < 16 lookup i0 + j.  (Sixteen
+// waves of 16 rows keep more row loads in flight per CU than eight of 32: the
+// tiles of the rarest ids, one segment per row, store almost every row they
+// load and set the kernel's length.)
 //  1. Heads and segment ends come from the neighbouring sorted keys; the
 //     block counts its heads and wave 0 numbers the segments by decoupled
 //     look-back over earlier tiles (no row load is in flight yet, so the
@@ -521,7 +524,7 @@ __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0
 //     the distinct id and the segment's first position.
 //  2. Value rows: LPR lanes cover LPR*V consecutive columns of one row
 //     (16-byte loads when V = 4), so one load instruction fetches 64/LPR rows;
-//     all 32 rows of the wave are loaded, the wave waits once (stores share the
+//     all 16 rows of the wave are loaded, the wave waits once (stores share the
 //     vector memory counter, so none is issued before the wait), then adds
 //     them in sorted (= lookup) order: row j to the accumulator of lane group
 //     j % (64/LPR); a segment that ends at row j is closed by adding the group
@@ -530,7 +533,7 @@ __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0
 //     the wave is written with its count; the wave's first segment, if it began
 //     before the wave, leaves a double partial in LDS, and so does its last
 //     segment if it goes on past the wave.
-//  3. Wave 0 walks the 8 waves in order, adding partials of segments that
+//  3. Wave 0 walks the 16 waves in order, adding partials of segments that
 //     cross waves inside the tile (wave order), and writes those segments with
 //     their counts.  What crosses the tile remains: the tile's first segment,
 //     begun in an earlier tile (partial in tfirst[tile]), and its last, going

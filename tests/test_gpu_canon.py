@@ -66,11 +66,11 @@ def test_coo_from_lookups_matches_oracle(name, n, key_space, width, hot):
     assert_sums_close(gv, ov, ids, ok, oc, vals)
 
 
-@pytest.mark.parametrize("run", [1, 7, 16, 33, 63, 64, 65, 511, 512, 513, 1100])
+@pytest.mark.parametrize("run", [1, 7, 15, 16, 17, 31, 32, 33, 63, 64, 65, 511, 512, 513, 1100])
 def test_runs_on_chunk_edges(run):
     """Runs of equal ids of fixed length, so segment ends fall on every offset of
-    the 64-lookup waves and 512-lookup tiles of the summing kernel (exactly on
-    their edges for 64 and 512), and segments cross several tiles."""
+    the 16-lookup waves and 256-lookup tiles of the summing kernel (exactly on
+    their edges for 16, 32, 64 and 512), and segments cross several tiles."""
     rng = np.random.default_rng(run)
     n_ids, width = max(24, 30000 // run), 128
     ids = np.repeat(rng.permutation(100000)[:n_ids].astype(np.int64), run)
