@@ -1,4 +1,5 @@
-// canon.hip - raw lookups -> canonical COO on the GPU.
+// canon.hip - raw lookups -> canonical COO on the GPU (coo_from_lookups), and
+// on to the full-row CSR in the same call (csr_from_lookups).
 //
 // Computes what the DiskSparseAdam README calls "Safe Duplicate Aggregation &
 // Sorted I/O" (duplicates summed, indices sorted) and what the optirs_gpu
@@ -17,6 +18,9 @@
 //   3. segments that cross tiles leave double partial sums, which a second
 //      kernel adds in tile order.  No atomics in any sum, so the result is the
 //      same run to run.
+// csr_from_lookups runs 1 and 2 (the segment kernel also recording how many
+// ids lie below each 8192-row block), then one launch that does 3 and builds
+// the CSR's row_offsets and col_indices (csr_full.hpp) from those counts.
 #include <stdarg.h>
 #include <stdio.h>
 
