@@ -537,12 +537,13 @@ __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0
 //     the wave is written with its count; the wave's first segment, if it began
 //     before the wave, leaves a double partial in LDS, and so does its last
 //     segment if it goes on past the wave.
-//  3. Wave 0 walks the 16 waves in order, adding partials of segments that
-//     cross waves inside the tile (wave order), and writes those segments with
-//     their counts.  What crosses the tile remains: the tile's first segment,
+//  3. A segment that crosses waves inside the tile is summed by the wave where
+//     it ends, which walks back to the wave where it started and adds the
+//     partials in wave order, and written with its count; all waves do this at
+//     once.  What crosses the tile remains: the tile's first segment,
 //     begun in an earlier tile (partial in tfirst[tile]), and its last, going
 //     on into the next (partial in tlast[tile], and tcross[tile] = its number;
-//     -1 when there is none).
+//     -1 when there is none), found by the last wave.
 // The last tile writes U (0 when an id was out of range or a wait timed out)
 // and seg_start[U] = n.
 template <int V, int LPR>
@@ -734,63 +735,72 @@ __global__ __launch_bounds__(kSumThreads) void k_seg_sum(
             }
         }
         __syncthreads();
-        if (w == 0) {
-            // Wave 0 walks the waves in order; lane l holds columns l and l + 64
-            // of this block of columns.
-            const bool tile_head = (wflags[0] & 1u) == 0u;  // tile starts with a head
-            bool open = !tile_head, open_here = false;
-            int32_t open_seg = -1, open_head = 0;
-            double carry[2] = {0.0, 0.0};
-            for (int ww = 0; ww < kSumWaves; ++ww) {
-                const uint32_t f = wflags[ww];
-                if (f & 1u) {
+        // Segments that cross waves, each closed by one wave, all waves at
+        // once; lane l holds columns l and l + 64 of this block of columns.
+        // Wave w's flags: 1 = its first segment began in an earlier wave
+        // (partial pf[w]), 2 = that segment ends in wave w, 4 = a segment
+        // starts in wave w and goes on past it (partial pl[w]).  A segment is
+        // summed as pl[start] (0 if it began before the tile) + pf of every
+        // later wave up to its end, in wave order: one fixed order.
+        const uint32_t fw = wflags[w];
+        // From wave e back over pass-through waves (flag 1 only) to the wave
+        // where the segment reaching e started (-1: before the tile).
+        auto walk_back = [&](int e, double (&carry)[2]) -> int {
+            int j = e;
+            while (j >= 0 && (wflags[j] & 4u) == 0u) --j;
 #pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        const int c = lane + h * kWave;
-                        if (c < CB) carry[h] += pf[ww][c];
-                    }
-                    if (f & 2u) {  // the open segment ends in wave ww
-                        if (open_here) {
+            for (int h = 0; h < 2; ++h) {
+                const int c = lane + h * kWave;
+                carry[h] = (j >= 0 && c < CB) ? pl[j][c] : 0.0;
+            }
+            for (int ww = j + 1; ww <= e; ++ww)
 #pragma unroll
-                            for (int h = 0; h < 2; ++h) {
-                                const int64_t c = c0 + lane + h * kWave;
-                                if (lane + h * kWave < CB && c < width)
-                                    out_vals[(int64_t)open_seg * width + c] = (float)carry[h];
-                            }
-                            if (lane == 0 && c0 == 0)
-                                out_counts[open_seg] = wfirst_end[ww] - open_head + 1;
-                        } else {
-#pragma unroll
-                            for (int h = 0; h < 2; ++h) {
-                                const int64_t c = c0 + lane + h * kWave;
-                                if (lane + h * kWave < CB && c < width)
-                                    tfirst[tile * width + c] = carry[h];
-                            }
-                        }
-                        carry[0] = carry[1] = 0.0;
-                        open = open_here = false;
-                    }
+                for (int h = 0; h < 2; ++h) {
+                    const int c = lane + h * kWave;
+                    if (c < CB) carry[h] += pf[ww][c];
                 }
-                if (f & 4u) {  // a segment starts in wave ww and goes past it
+            return j;
+        };
+        if ((fw & 3u) == 3u) {  // the segment that ends in wave w began earlier
+            double carry[2];
+            const int j = walk_back(w - 1, carry);
 #pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        const int c = lane + h * kWave;
-                        carry[h] = c < CB ? pl[ww][c] : 0.0;
-                    }
-                    open = open_here = true;
-                    open_seg = wlast_seg[ww];
-                    open_head = wlast_head[ww];
+            for (int h = 0; h < 2; ++h) {
+                const int c = lane + h * kWave;
+                if (c < CB) carry[h] += pf[w][c];
+            }
+            if (j >= 0) {
+                const int32_t seg0 = wlast_seg[j];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int64_t c = c0 + lane + h * kWave;
+                    if (lane + h * kWave < CB && c < width)
+                        out_vals[(int64_t)seg0 * width + c] = (float)carry[h];
+                }
+                if (lane == 0 && c0 == 0) out_counts[seg0] = wfirst_end[w] - wlast_head[j] + 1;
+            } else {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int64_t c = c0 + lane + h * kWave;
+                    if (lane + h * kWave < CB && c < width) tfirst[tile * width + c] = carry[h];
                 }
             }
+        }
+        if (w == kSumWaves - 1) {  // what goes on past the tile
+            const bool open = (fw & 4u) != 0u || (fw & 3u) == 1u;
+            int32_t cross = -1;
             if (open) {
-                double* dst = open_here ? tlast : tfirst;
+                double carry[2];
+                const int j = walk_back(w, carry);
+                double* dst = j >= 0 ? tlast : tfirst;
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const int64_t c = c0 + lane + h * kWave;
                     if (lane + h * kWave < CB && c < width) dst[tile * width + c] = carry[h];
                 }
+                if (j >= 0) cross = wlast_seg[j];
             }
-            if (lane == 0 && c0 == 0) tcross[tile] = open && open_here ? open_seg : -1;
+            if (lane == 0 && c0 == 0) tcross[tile] = cross;
         }
         __syncthreads();
     }
