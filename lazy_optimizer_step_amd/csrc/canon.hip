@@ -515,6 +515,29 @@ enum : int { kFlushNone = 0, kFlushOut = 1, kFlushFirst = 2, kFlushLast = 3 };
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 
+// Head count of every segment tile of kSumTile sorted lookups: the lookups
+// whose id differs from their predecessor's, stored with a plain store.  When
+// the tiles are few, k_seg_sum sums the counts of the tiles before its own in
+// place of a look-back.
+__global__ __launch_bounds__(kSumTile) void k_head_count(const uint64_t* __restrict__ s, int64_t n,
+                                                        int pos_bits,
+                                                        uint32_t* __restrict__ counts) {
+    __shared__ uint32_t wc[kSumTile / kWave];
+    const int64_t i = (int64_t)blockIdx.x * kSumTile + threadIdx.x;
+    const int64_t ic = i < n ? i : n - 1;
+    const uint64_t key = s[ic], prev = s[ic > 0 ? ic - 1 : 0];
+    const bool head = i < n && (ic == 0 || (prev >> pos_bits) != (key >> pos_bits));
+    const uint32_t c = (uint32_t)popc64(ballot(head));
+    if (lane_id() == 0) wc[threadIdx.x >> 6] = c;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t t = 0;
+#pragma unroll
+        for (int w = 0; w < kSumTile / kWave; ++w) t += wc[w];
+        counts[blockIdx.x] = t;
+    }
+}
+
 // Segments and their sums in one pass over the sorted lookups.  A block takes
 // the next tile ticket (kSumTile = 256 lookups); wave w owns the kSumRows =
 // 16 lookups [16w, 16w + 16) of the tile, lane j < 16 lookup i0 + j.  (Sixteen
@@ -553,7 +576,7 @@ __global__ __launch_bounds__(kSumThreads) void k_seg_sum(
     float* __restrict__ out_vals, int32_t* __restrict__ out_counts, int64_t* d_nunique,
     int32_t* __restrict__ seg_start, double* __restrict__ tfirst, double* __restrict__ tlast,
     int32_t* __restrict__ tcross, uint32_t* words, uint32_t* ticket, uint32_t* status,
-    int32_t* __restrict__ bnd, int64_t key_space) {
+    int32_t* __restrict__ bnd, int64_t key_space, const uint32_t* __restrict__ counts) {
     constexpr int RPI = kWave / LPR;
     constexpr int U = kSumRows / RPI;  // load instructions per block of columns
     constexpr int CB = LPR * V;        // columns per block of columns
@@ -563,6 +586,7 @@ __global__ __launch_bounds__(kSumThreads) void k_seg_sum(
     __shared__ double pl[kSumWaves][CB];
     __shared__ uint32_t wheads[kSumWaves], wflags[kSumWaves];
     __shared__ int32_t wfirst_end[kSumWaves], wlast_seg[kSumWaves], wlast_head[kSumWaves];
+    __shared__ uint32_t wcnt[kSumWaves];
     __shared__ uint32_t s_tile, s_excl, s_ok;
     const int tid = threadIdx.x;
     const int w = tid >> 6;
@@ -570,10 +594,16 @@ __global__ __launch_bounds__(kSumThreads) void k_seg_sum(
     const int sub = lane / LPR, sl = lane % LPR;
     // The status word (an id out of range, a wait that timed out) is loaded
     // while the ticket is taken; nothing is written before it is checked.
+    // With per-tile head counts (counts: at most kSumThreads tiles) there is
+    // no ticket and no look-back: tile = block, and thread t holds the count
+    // of tile t if t comes before this tile, loaded with the keys.
     const uint32_t st0 = *status;
-    if (tid == 0) s_tile = atomicAdd(ticket, 1u);
-    __syncthreads();
-    const int64_t tile = s_tile;
+    if (counts == nullptr) {
+        if (tid == 0) s_tile = atomicAdd(ticket, 1u);
+        __syncthreads();
+    }
+    const int64_t tile = counts != nullptr ? (int64_t)blockIdx.x : (int64_t)s_tile;
+    const uint32_t cbefore = (counts != nullptr && tid < tile) ? counts[tid] : 0u;
     const int64_t i0 = tile * kSumTile + (int64_t)w * kSumRows;
     const int cnt = i0 >= n ? 0 : (int)((n - i0) < kSumRows ? (n - i0) : kSumRows);
 
@@ -592,7 +622,11 @@ __global__ __launch_bounds__(kSumThreads) void k_seg_sum(
     const bool ends = in && (i + 1 >= n || (next >> pos_bits) != id);
     const uint32_t pos = (uint32_t)(key & ((1ull << pos_bits) - 1ull));
     const uint64_t hm = ballot(head);
-    if (lane == 0) wheads[w] = (uint32_t)popc64(hm);
+    const uint32_t cw = read_lane(wave_incl_scan(cbefore), kWave - 1);
+    if (lane == 0) {
+        wheads[w] = (uint32_t)popc64(hm);
+        wcnt[w] = cw;
+    }
     __syncthreads();
     uint32_t tile_heads = 0, before = 0;
 #pragma unroll
@@ -600,16 +634,25 @@ __global__ __launch_bounds__(kSumThreads) void k_seg_sum(
         if (ww < w) before += wheads[ww];
         tile_heads += wheads[ww];
     }
-    if (w == 0) {
-        uint32_t excl = 0;
-        const bool ok = tile_exclusive_prefix(words, tile, tile_heads, &excl);
-        if (lane == 0) {
-            s_excl = excl;
-            s_ok = ok ? 1u : 0u;
+    uint32_t excl0 = 0;
+    bool ok0 = true;
+    if (counts != nullptr) {
+#pragma unroll
+        for (int ww = 0; ww < kSumWaves; ++ww) excl0 += wcnt[ww];
+    } else {
+        if (w == 0) {
+            uint32_t excl = 0;
+            const bool ok = tile_exclusive_prefix(words, tile, tile_heads, &excl);
+            if (lane == 0) {
+                s_excl = excl;
+                s_ok = ok ? 1u : 0u;
+            }
         }
+        __syncthreads();
+        excl0 = s_excl;
+        ok0 = s_ok != 0u;
     }
-    __syncthreads();
-    if (!s_ok) {
+    if (!ok0) {
         if (tid == 0) {
             atomicOr(status, kStatusTimeout);
             *d_nunique = 0;
@@ -618,7 +661,7 @@ __global__ __launch_bounds__(kSumThreads) void k_seg_sum(
     }
     const uint64_t upto = lane == 63 ? ~0ull : ((2ull << lane) - 1ull);
     const uint32_t heads_upto = (uint32_t)popc64(hm & upto);
-    const int32_t seg = (int32_t)(s_excl + before + heads_upto) - 1;
+    const int32_t seg = (int32_t)(excl0 + before + heads_upto) - 1;
     const bool starts_here = heads_upto > 0;  // a head at or before lane j in this wave
     int kind = kFlushNone;
     if (in && (ends || lane == cnt - 1))
@@ -654,7 +697,7 @@ __global__ __launch_bounds__(kSumThreads) void k_seg_sum(
         out_counts[seg] = lane - first + 1;
     }
     if (tile == ntiles - 1 && tid == 0) {
-        const uint32_t u = s_excl + tile_heads;
+        const uint32_t u = excl0 + tile_heads;
         *d_nunique = (int64_t)u;
         seg_start[u] = (int32_t)n;
         if (bnd != nullptr) {  // blocks past the last id: all U ids below them
@@ -1053,11 +1096,18 @@ static int canon_run(const char* what, const int64_t* ids, const float* vals, in
     const uintptr_t al = (uintptr_t)vals | (uintptr_t)out_vals;
     const int V = (width % 4 == 0 && (al & 15u) == 0) ? 4 : (width % 2 == 0 && (al & 7u) == 0) ? 2 : 1;
     const int lpr = width <= 16 * V ? 16 : ((width <= 32 * V || V >= 2) ? 32 : 64);
+    // Few tiles: their head counts first, summed by each tile instead of a
+    // look-back (the counts take the look-back words' place).
+    const bool counted = L.nsum <= kSumThreads;
+    if (counted) {
+        k_head_count<<<(unsigned)L.nsum, kSumTile, 0, st>>>(sorted, n, L.pos_bits, sumwords);
+        SPOPT_LAUNCHED();
+    }
     auto sum = [&](auto kernel) {
         kernel<<<(unsigned)L.nsum, kSumThreads, 0, st>>>(
             sorted, n, L.pos_bits, L.nsum, vals, width, out_keys, out_vals, out_counts, d_nunique,
             seg_start, tfirst, tlast, tcross, sumwords, tickets + kMaxPasses,
-            status, bnd, key_space);
+            status, bnd, key_space, counted ? sumwords : nullptr);
     };
     if (V == 4)
         lpr == 16 ? sum(k_seg_sum<4, 16>) : sum(k_seg_sum<4, 32>);
