@@ -157,6 +157,9 @@ __device__ __forceinline__ void csr_row_block(int64_t rb, const int64_t* __restr
     const int64_t r1 = (r0 + kRoBits < rows + 1) ? r0 + kRoBits : rows + 1;
 #pragma unroll
     for (int j = 0; j < 2 * kWordsPer; ++j) flags[j * kRoThreads + tid] = make_uint4(0u, 0u, 0u, 0u);
+    // Every flag is zeroed before any thread sets one (a thread's zeroing of
+    // its slice must not land after another thread's flag in it).
+    __syncthreads();
     int64_t ka, kb;
     if (bnd != nullptr) {
         // #keys below the block's first row and below the next block's, as

@@ -87,6 +87,27 @@ def test_matches_oracle_and_two_calls(rows, cols, n, pattern, ro_shift):
     _check(rows, cols, ids, vals, ro_shift)
 
 
+def test_many_row_blocks_repeatedly():
+    """Regression test: 50M rows make 6104 row_offsets blocks a call; every call
+    over 25 steps of Zipf lookups must give exactly the offsets of csr_from_coo
+    (a missing barrier between zeroing a block's LDS flags and setting them once
+    dropped a key from a block now and then)."""
+    import synth
+    w = synth.WORKLOADS[5].scaled(cols=4)
+    R, C, n = w.rows, w.cols, w.n_lookups
+    ws = torch.empty(L.sparse_opt_workspace_size(n, C, R), dtype=torch.uint8, device="cuda")
+    ro1 = torch.empty(R + 1, dtype=torch.int32, device="cuda")
+    ro2 = torch.empty(R + 1, dtype=torch.int32, device="cuda")
+    for s in range(25):
+        ids, grads = synth.lookups(w, s)
+        csr, _, U = L.csr_from_lookups(dev(ids), dev(grads), R, row_offsets=ro1,
+                                       want_col_indices=False, workspace=ws)
+        coo = L.CooGradient(csr.touched_rows, csr.values, dim=R, width=C, nnz=n, d_nnz=U)
+        L.csr_from_coo(coo, R, C, row_offsets=ro2, want_col_indices=False, copy_values=False)
+        torch.cuda.synchronize()
+        assert torch.equal(ro1, ro2), f"step {s}"
+
+
 def test_without_col_indices():
     rng = np.random.default_rng(5)
     ids = _ids(30000, 5000, "hot", rng)
