@@ -68,12 +68,19 @@ constexpr uint32_t kSpinLimit = 1u << 16;
 // loaded before any is used.
 constexpr int kPackBlocks = 32;
 constexpr int kPackIpt = 8;
+// Up to this many radix tiles, the first pass reads the per-tile digit counts
+// the pack kernel wrote instead of looking back; kCountBatch counts are loaded
+// per round trip.  (Later passes would need their tiles' counts added up by
+// the pass before with a global atomic per key: measured at 24 µs a pass.)
+constexpr int kMaxCountTiles = 64;
+constexpr int kCountBatch = 32;
 
 struct CanonLayout {
     int key_bits, pos_bits, passes, digit_bits;
     int64_t ntiles, nsum;
     int64_t npack;  // blocks of the pack kernel
-    size_t off_a, off_b, off_part, off_pflag, off_clear, clear_bytes, off_status, off_tickets,
+    size_t off_a, off_b, off_part, off_pflag, off_thist0, off_clear, clear_bytes, off_status,
+        off_tickets,
         off_sumwords, off_words, off_segstart, off_tcross, off_tfirst, off_tlast, off_bnd,
         bnd_entries, total;
 };
@@ -112,6 +119,9 @@ static bool canon_layout(int64_t n, int64_t width, int64_t key_space, CanonLayou
     // Digit histograms and range flag of each pack block.
     L->off_part = take(sizeof(uint32_t) * (size_t)kPackBlocks * kRadix * P);
     L->off_pflag = take(sizeof(uint32_t) * (size_t)kPackBlocks);
+    // Digit counts of each radix tile for the first pass (written whole by the
+    // pack kernel when the tiles are few).
+    L->off_thist0 = take(sizeof(uint32_t) * (size_t)kRadix * (size_t)L->ntiles);
     // Everything the kernels after the pack kernel must find zeroed sits in
     // one contiguous region, which the pack kernel zeroes.
     L->off_clear = o;
@@ -204,8 +214,12 @@ __global__ __launch_bounds__(kThreads) void k_pack(const int64_t* __restrict__ i
                                                    int digit_bits, uint64_t* __restrict__ out,
                                                    uint32_t* __restrict__ part,
                                                    uint32_t* __restrict__ pflag,
-                                                   uint4* __restrict__ zero, int64_t nzero16) {
+                                                   uint4* __restrict__ zero, int64_t nzero16,
+                                                   uint32_t* __restrict__ thist0) {
+    static_assert((int64_t)kPackIpt * kThreads == kTile, "a pack chunk is a radix tile");
+    static_assert(kThreads == kRadix, "thread d owns digit d of a chunk's counts");
     __shared__ uint32_t h[kMaxPasses * kRadix];
+    __shared__ uint32_t h0[kRadix];
     const int tid = threadIdx.x;
     const int words = passes * kRadix;
     for (int i = tid; i < words; i += kThreads) h[i] = 0;
@@ -224,6 +238,10 @@ __global__ __launch_bounds__(kThreads) void k_pack(const int64_t* __restrict__ i
             const int64_t i = base + (int64_t)j * kThreads + tid;
             id[j] = ids[i < n ? i : n - 1];
         }
+        if (thist0 != nullptr) {  // this chunk's first-digit counts (thread d: digit d)
+            h0[tid] = 0u;
+            __syncthreads();
+        }
 #pragma unroll
         for (int j = 0; j < kPackIpt; ++j) {
             const int64_t i = base + (int64_t)j * kThreads + tid;
@@ -239,7 +257,13 @@ __global__ __launch_bounds__(kThreads) void k_pack(const int64_t* __restrict__ i
                     atomicAdd(&h[p * kRadix +
                                  ((uint32_t)(packed >> (pos_bits + p * digit_bits)) & dmask)],
                               1u);
+                if (thist0 != nullptr && passes > 0)
+                    atomicAdd(&h0[(uint32_t)(packed >> pos_bits) & dmask], 1u);
             }
+        }
+        if (thist0 != nullptr) {
+            __syncthreads();
+            thist0[(base / kChunk) * kRadix + tid] = h0[tid];  // read and later zeroed by tid
         }
     }
     const bool any_bad = __syncthreads_or(bad);
@@ -260,7 +284,7 @@ __global__ __launch_bounds__(kThreads) void k_pack(const int64_t* __restrict__ i
 __global__ __launch_bounds__(kSortThreads) void k_onesweep(
     const uint64_t* __restrict__ in, uint64_t* __restrict__ out, int64_t n, int shift, int nbits,
     const uint32_t* __restrict__ part, int npack, int part_stride, const uint32_t* pflag,
-    uint32_t* lb, uint32_t* ticket, uint32_t* status) {
+    uint32_t* lb, uint32_t* ticket, uint32_t* status, const uint32_t* __restrict__ thist) {
     static_assert(kSortThreads >= kRadix && kRadix % kWave == 0,
                   "threads 0..kRadix-1 own the digits (whole waves)");
     __shared__ uint32_t cnt[kSortWaves][kRadix];
@@ -270,13 +294,15 @@ __global__ __launch_bounds__(kSortThreads) void k_onesweep(
     const int tid = threadIdx.x;
     const int w = tid >> 6;
     const int lane = lane_id();
+    // thist (first pass, few tiles): the digit counts of every tile, so tile =
+    // block and no look-back; else tiles by ticket and decoupled look-back.
     if (tid == 0) {
-        s_tile = atomicAdd(ticket, 1u);
+        if (thist == nullptr) s_tile = atomicAdd(ticket, 1u);
         s_bad = 0u;
     }
     for (int i = tid; i < kSortWaves * kRadix; i += kSortThreads) (&cnt[0][0])[i] = 0;
     __syncthreads();
-    const int64_t tile = s_tile;
+    const int64_t tile = thist != nullptr ? (int64_t)blockIdx.x : (int64_t)s_tile;
     const bool owner = tid < kRadix;  // wave-uniform
 
     const int64_t first = tile * kTile + (int64_t)w * (kIpt * kWave);
@@ -299,6 +325,13 @@ __global__ __launch_bounds__(kSortThreads) void k_onesweep(
 #pragma unroll
         for (int g = 0; g < kPackBlocks; ++g)
             hpart[g] = part[(int64_t)(g < npack ? g : 0) * part_stride + tid];
+    }
+    // Counts of digit tid in the first kCountBatch tiles before this one.
+    uint32_t tpre[kCountBatch];
+    if (owner && thist != nullptr) {
+#pragma unroll
+        for (int g = 0; g < kCountBatch; ++g)
+            tpre[g] = thist[(int64_t)(g < tile ? g : 0) * kRadix + tid];
     }
 #pragma unroll
     for (int r = 0; r < kIpt; ++r) {
@@ -330,14 +363,27 @@ __global__ __launch_bounds__(kSortThreads) void k_onesweep(
             cnt[ww][d] = run;
             run += c;
         }
-        uint32_t* mine = lb + tile * kRadix + d;
         bool ok = true;
-        if (tile == 0) {
-            st_dev(mine, kLbInc | run);
+        if (thist != nullptr) {
+#pragma unroll
+            for (int g = 0; g < kCountBatch; ++g) excl += g < tile ? tpre[g] : 0u;
+            for (int64_t g0 = kCountBatch; g0 < tile; g0 += kCountBatch) {
+                uint32_t more[kCountBatch];
+#pragma unroll
+                for (int g = 0; g < kCountBatch; ++g)
+                    more[g] = thist[(g0 + g < tile ? g0 + g : 0) * kRadix + d];
+#pragma unroll
+                for (int g = 0; g < kCountBatch; ++g) excl += g0 + g < tile ? more[g] : 0u;
+            }
         } else {
-            st_dev(mine, kLbAgg | run);
-            ok = look_back(lb + d, tile, kRadix, &excl);
-            if (ok) st_dev(mine, kLbInc | (excl + run));
+            uint32_t* mine = lb + tile * kRadix + d;
+            if (tile == 0) {
+                st_dev(mine, kLbInc | run);
+            } else {
+                st_dev(mine, kLbAgg | run);
+                ok = look_back(lb + d, tile, kRadix, &excl);
+                if (ok) st_dev(mine, kLbInc | (excl + run));
+            }
         }
         if (!ok) atomicOr(&s_bad, 1u);
 #pragma unroll
@@ -1050,10 +1096,14 @@ static int canon_run(const char* what, const int64_t* ids, const float* vals, in
 
     // Pack and count digits; the pack kernel also zeroes the status word,
     // tickets and look-back words of the kernels after it.
+    // Few radix tiles: the first pass takes per-tile digit counts from the
+    // pack kernel instead of looking back.
+    const bool counted_sort = L.ntiles <= kMaxCountTiles;
+    uint32_t* thist0 = counted_sort ? (uint32_t*)(ws + L.off_thist0) : nullptr;
     k_pack<<<(unsigned)L.npack, kThreads, 0, st>>>(ids, n, key_space, L.pos_bits, L.passes,
                                                    L.digit_bits, a, part, pflag,
                                                    (uint4*)(ws + L.off_clear),
-                                                   (int64_t)(L.clear_bytes / 16));
+                                                   (int64_t)(L.clear_bytes / 16), thist0);
     SPOPT_LAUNCHED();
     const bool validate = (flags_arg & SPOPT_VALIDATE) != 0;
     if (validate) {
@@ -1079,8 +1129,8 @@ static int canon_run(const char* what, const int64_t* ids, const float* vals, in
         uint32_t* pwords = words + (int64_t)p * L.ntiles * kRadix;
         k_onesweep<<<(unsigned)L.ntiles, kSortThreads, 0, st>>>(
             src, dst, n, shift, nbits, part + (int64_t)p * kRadix, (int)L.npack,
-            L.passes * kRadix, p == 0 ? pflag : nullptr, pwords,
-            tickets + p, status);
+            L.passes * kRadix, p == 0 ? pflag : nullptr, pwords, tickets + p, status,
+            p == 0 ? thist0 : nullptr);
         SPOPT_LAUNCHED();
         uint64_t* t = src;
         src = dst;
