@@ -70,8 +70,10 @@ constexpr int kPackBlocks = 32;
 constexpr int kPackIpt = 8;
 // Up to this many radix tiles, the first pass reads the per-tile digit counts
 // the pack kernel wrote instead of looking back; kCountBatch counts are loaded
-// per round trip.  (Later passes would need their tiles' counts added up by
-// the pass before with a global atomic per key: measured at 24 µs a pass.)
+// per round trip.  (Later passes would need their tiles' counts from the pass
+// before: added up with a global atomic per key they took 24 µs a pass;
+// counted in LDS per source tile and stored as prefixes, they cost the pass
+// that writes them about as much as they save the pass that reads them.)
 constexpr int kMaxCountTiles = 64;
 constexpr int kCountBatch = 32;
 
