@@ -57,7 +57,7 @@ BYTES_PER_ROW_ROW_LS = 24
 UPDATE_SOURCES = ("lazy_optimizer_step_amd/csrc/update.hip",
                   "lazy_optimizer_step_amd/csrc/common.hpp")
 UPDATE_TRAFFIC = {"sources_sha256": "9603ce4e10ac53fe5af479b1ef102a3a82dffe85afc6b2537fc330d65e22886b",
-                  "fetch_bytes": 2.0 * 33795.7 * 1024, "write_bytes": 1.0 * 59021.4 * 1024}
+                  "fetch_bytes": 2.0 * 33795.3 * 1024, "write_bytes": 1.0 * 59017.9 * 1024}
 
 
 def sources_sha256() -> str:
