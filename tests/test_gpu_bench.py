@@ -1,0 +1,43 @@
+"""The benchmark's one JSON line, from short runs of the default command and
+of its two-call and per-row variants: every field of the output contract is
+there, and the roofline and CPU-baseline figures are consistent with each
+other.  (The bench times the GPU, so these are GPU tests.)"""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FIELDS = ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
+          "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config", "roofline",
+          "cpu_baseline", "breakdown_us")
+
+
+@pytest.mark.parametrize("extra", [[], ["--separate-calls"], ["--last-step-per-row"]],
+                         ids=["fused", "separate_calls", "row_last_step"])
+def test_bench_json_line(extra):
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "3",
+                        "--warmup", "1", "--cpu-seconds", "0.5", *extra],
+                       capture_output=True, text=True, timeout=300, cwd=ROOT)
+    assert r.returncode == 0, r.stderr[-3000:]
+    lines = [l for l in r.stdout.splitlines() if l.strip()]
+    assert len(lines) == 1, r.stdout[-2000:]
+    d = json.loads(lines[0])
+    for k in FIELDS:
+        assert k in d, k
+    assert d["n_gpus"] == 1 and d["steps"] == 3 and d["warmup"] == 1
+    assert d["value"] > 0 and d["ms_per_step"] > 0 and d["higher_is_better"] is True
+    assert d["config"]["workload"] == "table10Mx128_zipf1.05_dormancy"
+    rf = d["roofline"]
+    assert rf["bound"] == "hbm" and rf["peak"] == 8000.0 and rf["unit"] == "GB/s"
+    assert 0 < rf["frac"] < 1 and abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-9
+    assert rf["traffic"] is None or rf["traffic"] > rf["algorithmic_bytes_per_launch"]
+    cb = d["cpu_baseline"]
+    assert cb["kind"] == "oracle" and cb["cores"] == 1 and cb["value"] > 0
+    calls = ["coo_from_lookups", "csr_from_coo"] if extra == ["--separate-calls"] \
+        else ["csr_from_lookups"]
+    assert list(d["breakdown_us"]) == calls + ["sparse_adam_step", "step"]
