@@ -1,21 +1,25 @@
 """Benchmark of the sparse / lazy Adam step on one MI355X.
 
-One step is the whole hot path over one batch of raw lookups:
-  csr_from_lookups  (radix sort, dedupe, duplicate sums; row_offsets over every
-                     table row, col_indices, touched rows)
-  sparse_adam_step  (DormancyDecay update of the touched coordinates)
-(--separate-calls: coo_from_lookups then csr_from_coo in place of the first.)
+One step is the whole hot path over one batch of raw lookups, in one call:
+  sparse_step_from_lookups  (radix sort, dedupe, duplicate sums; then one
+                             launch that completes the tile-crossing sums,
+                             writes row_offsets over every table row and
+                             col_indices, and applies the DormancyDecay update
+                             to the touched coordinates)
+(--two-calls: csr_from_lookups then sparse_adam_step on its CSR;
+--separate-calls: coo_from_lookups, csr_from_coo, sparse_adam_step.)
 on the 10M x 128 float32 table (65,536 Zipf(1.05) lookups per step, last_step
 int32 per coordinate).  Inputs for every step are generated up front and are
 resident in HBM before the timed region starts.
 
 Prints one JSON line:  value = touched coordinates updated per second over the
-whole timed region (G/s); roofline = the update kernel's algorithmic bytes per
-launch / its mean duration (HIP events around every update launch of the timed
-region, on the launch stream) against 8 TB/s, with a plain 1 GiB device copy
-measured alongside as the practical bandwidth ceiling; breakdown_us = p10 /
-median / p90 of each call and of the whole step from a second, separately
-timed pass over the same inputs; cold = the update again in a third pass that
+whole timed region (G/s); roofline = the algorithmic bytes of the launch that
+updates the table / its mean duration (HIP events that the library records
+around that launch on its stream, through its timing hook, at every step of the
+timed region) against 8 TB/s, with a plain 1 GiB device copy measured
+alongside as the practical bandwidth ceiling; breakdown_us = p10 / median / p90
+of each call, of that launch and of the whole step from a second, separately
+timed pass over the same inputs; cold = that launch again in a third pass that
 writes a 512 MB buffer before every step, so the state rows come from HBM
 rather than the 256 MB last-level cache; read_rows = the forward gather of each
 step's lookups, timed in a pass of its own; cpu_baseline = the CPU oracle on a
@@ -48,14 +52,26 @@ BYTES_PER_COORD = 36
 BYTES_PER_ROW = 16
 BYTES_PER_COORD_ROW_LS = 28
 BYTES_PER_ROW_ROW_LS = 24
+# The one-call step (sparse_step_from_lookups) updates the table in the same
+# launch that writes the CSR: col_indices (4 B per touched coordinate), each
+# distinct id read once more by the row_offsets blocks (8 B per touched row),
+# row_offsets (4 B per table row, plus one) and the per-8192-row id counts
+# they read (4 B per block).  Not counted: the combine's reads of the double
+# partial sums of tile-crossing segments (at most two 8*cols B rows per
+# 256-lookup tile, about 0.5% of the launch's bytes here).
+CSR_BYTES_PER_COORD = 4
+CSR_BYTES_PER_ROW = 8
+CSR_BYTES_PER_TABLE_ROW = 4
 
-# HBM bytes per launch of the update kernel on this workload, from two
-# rocprofv3 --pmc passes of this command (FETCH_SIZE scaled by 2.0 and
-# WRITE_SIZE by 1.0: a plain 1 GiB device copy reads 512 MiB by FETCH_SIZE and
-# writes 1 GiB by WRITE_SIZE).  Valid only for the kernel sources they were
-# taken with; reported as null once those sources change.
+# HBM bytes per launch of the one-call step's last kernel (k_step_lookups) on
+# this workload, from two rocprofv3 --pmc passes of this command (FETCH_SIZE
+# scaled by 2.0 and WRITE_SIZE by 1.0: a plain 1 GiB device copy reads 512 MiB
+# by FETCH_SIZE and writes 1 GiB by WRITE_SIZE).  Valid only for the kernel
+# sources they were taken with; reported as null once those sources change.
 UPDATE_SOURCES = ("lazy_optimizer_step_amd/csrc/update.hip",
-                  "lazy_optimizer_step_amd/csrc/common.hpp")
+                  "lazy_optimizer_step_amd/csrc/common.hpp",
+                  "lazy_optimizer_step_amd/csrc/csr_full.hpp",
+                  "lazy_optimizer_step_amd/csrc/seg_combine.hpp")
 UPDATE_TRAFFIC = {"sources_sha256": "9603ce4e10ac53fe5af479b1ef102a3a82dffe85afc6b2537fc330d65e22886b",
                   "fetch_bytes": 2.0 * 33795.3 * 1024, "write_bytes": 1.0 * 59017.9 * 1024}
 
@@ -83,9 +99,11 @@ def parse():
                     help="budget of the CPU-oracle sample (0 disables it)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling HBM counters)")
+    ap.add_argument("--two-calls", action="store_true",
+                    help="step with csr_from_lookups + sparse_adam_step instead of the one "
+                         "call sparse_step_from_lookups")
     ap.add_argument("--separate-calls", action="store_true",
-                    help="canonicalise with coo_from_lookups + csr_from_coo instead of the "
-                         "fused csr_from_lookups")
+                    help="step with coo_from_lookups + csr_from_coo + sparse_adam_step")
     ap.add_argument("--last-step-per-row", action="store_true",
                     help="keep one last_step per table row instead of one per coordinate")
     ap.add_argument("--host-state", action="store_true",
@@ -309,44 +327,59 @@ def main() -> int:
         return L.csr_from_coo(coo, R, Cc, row_offsets=row_offsets, col_indices=col_indices,
                               copy_values=False, stream=stream)
 
-    def fused(s: int):
+    def lookups_csr(s: int):
         return L.csr_from_lookups(ids_d[s], grads_d[s], R, out_keys=keys, out_vals=sums,
                                   out_counts=counts, d_nunique=nuniq[s:s + 1],
                                   row_offsets=row_offsets, col_indices=col_indices,
                                   workspace=ws, stream=stream)[0]
 
-    # The calls that turn step s's lookups into its gradient, named for the
-    # breakdown; the last one's result is the gradient.
-    if args.separate_calls:
-        calls = [("coo_from_lookups", canon), ("csr_from_coo", csr)]
-    else:
-        calls = [("csr_from_lookups", fused)]
+    def fused(s: int) -> None:
+        opt.step_lookups(ids_d[s], grads_d[s], out_keys=keys, out_vals=sums, out_counts=counts,
+                         d_nunique=nuniq[s:s + 1], row_offsets=row_offsets,
+                         col_indices=col_indices, workspace=ws, stream=stream)
 
-    def prep(s: int):
+    def adam(g) -> None:
+        opt.step(g, stream=stream)
+
+    # The calls of one step, named for the breakdown; each takes the step
+    # index, or (the step call) the gradient the previous call returned.
+    if args.separate_calls:
+        calls = [("coo_from_lookups", canon), ("csr_from_coo", csr), ("sparse_adam_step", adam)]
+    elif args.two_calls:
+        calls = [("csr_from_lookups", lookups_csr), ("sparse_adam_step", adam)]
+    else:
+        calls = [("sparse_step_from_lookups", fused)]
+
+    def step(s: int, ev=None, base: int = 0) -> None:
+        """One step; with ev, event base + c is recorded before call c and
+        base + len(calls) after the last."""
         g = None
-        for _, f in calls:
-            g = f(s)
-        return g
+        for c, (name, f) in enumerate(calls):
+            if ev is not None:
+                ev.record(base + c, stream)
+            g = f(g) if f is adam else f(s)
+        if ev is not None:
+            ev.record(base + len(calls), stream)
 
     log(f"warmup {W} steps")
     for s in range(W):
-        opt.step(prep(s), stream=stream)
+        step(s)
     torch.cuda.synchronize()
 
-    # Timed region: K whole steps.  Events bracket the region and every update
-    # launch in it.  A bounded spin kernel holds the stream while the host
-    # queues every step behind it, so the steps run back to back and the
-    # events time device work rather than the host's launch rate.
+    # Timed region: K whole steps.  Events bracket the region, and the library
+    # records a pair around every launch that updates the table (its timing
+    # hook).  A bounded spin kernel holds the stream while the host queues
+    # every step behind it, so the steps run back to back and the events time
+    # device work rather than the host's launch rate.
     ev = HipEvents(2 + 2 * K)
     cycles = calibrate_sleep(torch, stream, hold_ms=2.0 + 0.5 * K)
     log(f"timed {K} steps (queued behind a {cycles}-cycle spin)")
     torch.cuda._sleep(cycles)
     ev.record(0, stream)
     for k, s in enumerate(range(W, W + K)):
-        g = prep(s)
-        ev.record(2 + 2 * k, stream)
-        opt.step(g, stream=stream)
-        ev.record(3 + 2 * k, stream)
+        L.set_step_events(ev.ev[2 + 2 * k], ev.ev[3 + 2 * k])
+        step(s)
+    L.set_step_events()
     ev.record(1, stream)
     torch.cuda.synchronize()
     total_ms = ev.ms(0, 1)
@@ -354,38 +387,37 @@ def main() -> int:
     ev.close()
 
     # Breakdown (not part of the value): the same K inputs again, every call
-    # bracketed by events.
-    E = len(calls) + 2  # events per step: before each call, before and after the update
+    # bracketed by events, and the update launch by the hook's pair.
+    E = len(calls) + 3  # events per step: before each call, after the last, the hook's two
     bev = HipEvents(E * K)
     torch.cuda._sleep(cycles)
     for k, s in enumerate(range(W, W + K)):
-        g = None
-        for c, (_, f) in enumerate(calls):
-            bev.record(E * k + c, stream)
-            g = f(s)
-        bev.record(E * k + E - 2, stream)
-        opt.step(g, stream=stream)
-        bev.record(E * k + E - 1, stream)
+        L.set_step_events(bev.ev[E * k + E - 2], bev.ev[E * k + E - 1])
+        step(s, bev, E * k)
+    L.set_step_events()
     torch.cuda.synchronize()
     breakdown = {}
     for c, (name, _) in enumerate(calls):
         breakdown[name] = pcts(np.array([bev.ms(E * k + c, E * k + c + 1) for k in range(K)]))
-    breakdown["sparse_adam_step"] = pcts(
+    breakdown["update_launch"] = pcts(
         np.array([bev.ms(E * k + E - 2, E * k + E - 1) for k in range(K)]))
-    breakdown["step"] = pcts(np.array([bev.ms(E * k, E * k + E - 1) for k in range(K)]))
+    if not args.separate_calls and not args.two_calls:
+        # the canonicalisation kernels of the one call, before its last launch
+        breakdown["before_update_launch"] = pcts(
+            np.array([bev.ms(E * k, E * k + E - 2) for k in range(K)]))
+    breakdown["step"] = pcts(np.array([bev.ms(E * k, E * k + len(calls)) for k in range(K)]))
     bev.close()
 
     # Cold regime (not part of the value): the same K inputs, a 512 MB buffer
-    # written between steps to evict the last-level cache, update timed.
+    # written between steps to evict the last-level cache, update launch timed.
     log("cold pass (512 MB written between steps)")
     scrub = torch.empty(128 << 20, dtype=torch.float32, device="cuda")
     cev = HipEvents(2 * K)
     for k, s in enumerate(range(W, W + K)):
         scrub.fill_(float(k))
-        g = prep(s)
-        cev.record(2 * k, stream)
-        opt.step(g, stream=stream)
-        cev.record(2 * k + 1, stream)
+        L.set_step_events(cev.ev[2 * k], cev.ev[2 * k + 1])
+        step(s)
+    L.set_step_events()
     torch.cuda.synchronize()
     upd_cold = np.array([cev.ms(2 * k, 2 * k + 1) for k in range(K)])
     cev.close()
@@ -411,11 +443,21 @@ def main() -> int:
         upd_bytes = BYTES_PER_COORD_ROW_LS * U * Cc + BYTES_PER_ROW_ROW_LS * U
     else:
         upd_bytes = BYTES_PER_COORD * U * Cc + BYTES_PER_ROW * U
+    one_call = not args.separate_calls and not args.two_calls
+    if one_call:
+        # the same launch also writes the CSR's row_offsets and col_indices
+        upd_bytes = upd_bytes + (CSR_BYTES_PER_COORD * U * Cc + CSR_BYTES_PER_ROW * U
+                                 + CSR_BYTES_PER_TABLE_ROW * (R + 1) + 4 * (R // 8192 + 1))
     achieved = float((upd_bytes / (upd * 1e-3)).mean() / 1e9)
     cold_achieved = float((upd_bytes / (upd_cold * 1e-3)).mean() / 1e9)
     traffic = None
-    if not per_row and not args.host_state and sources_sha256() == UPDATE_TRAFFIC["sources_sha256"]:
+    if one_call and not per_row and not args.host_state \
+            and sources_sha256() == UPDATE_TRAFFIC["sources_sha256"]:
         traffic = UPDATE_TRAFFIC["fetch_bytes"] + UPDATE_TRAFFIC["write_bytes"]
+    op = ("AdamOp<DormancyDecay, no decay, "
+          + ("last_step per row" if per_row else "last_step per coordinate") + ">")
+    kernel = (f"k_step_lookups<{op}, 32, 2> (tile combine + update + CSR blocks)" if one_call
+              else f"k_update_rows<{op}, SrcCsrTouched, 32, 2>")
 
     result = {
         "metric": METRIC,
@@ -434,14 +476,12 @@ def main() -> int:
                    "zipf_s": w.zipf_s, "mode": w.mode, "state": "p,m,v float32 + last_step int32 per " + ("row" if per_row else "coordinate")
                    + (", in mapped pinned host memory" if args.host_state else ", in HBM"),
                    "mean_unique_rows": float(U.mean()),
-                   "calls": " + ".join([c for c, _ in calls] + ["sparse_adam_step"])},
+                   "calls": " + ".join(c for c, _ in calls)},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled)",
                      "algorithmic_bytes_per_launch": float(upd_bytes.mean()),
-                     "kernel": "k_update_rows<AdamOp<DormancyDecay, no decay, "
-                               + ("last_step per row" if per_row else "last_step per coordinate")
-                               + ">, SrcCsrTouched, 32>",
+                     "kernel": kernel,
                      "mean_us": float(upd.mean() * 1e3), "us": pcts(upd),
                      "coords_per_s_G": float((U * Cc / (upd * 1e-3)).mean() / 1e9),
                      "device_copy_GBs": copy_gbs,

@@ -35,9 +35,10 @@
  *     crosses the ABI.  sparse_opt_last_error() gives a message for the
  *     calling thread's most recent failure.
  *   - A call that returns an error has enqueued no kernel that writes an
- *     output or state array, with one documented exception: in trusted mode
+ *     output or state array, with two documented exceptions: in trusted mode
  *     coo_from_lookups cannot see device-side errors, so it marks its result
- *     empty instead (see there).
+ *     empty instead (see there); and sparse_step_from_lookups writes its
+ *     canonical outputs before the step's own checks (see there).
  *   - Layouts are row-major and contiguous; float arrays whose width is a
  *     multiple of 4 take 16-byte vector loads when their base is 16-byte
  *     aligned (torch allocations are), and a scalar path otherwise.
@@ -194,6 +195,16 @@ SPOPT_API int sparse_opt_set_step(spopt_t h, int64_t t);
 /* Message of the calling thread's last failure ("" if none). */
 SPOPT_API const char* sparse_opt_last_error(void);
 
+/* Timing of the update launch (profiling).  With two hipEvent_t handles set
+ * (created by the caller), every later sparse_adam_step, sparse_sgd_step and
+ * sparse_step_from_lookups call of the calling thread records `begin` just
+ * before the kernel that updates the table and `end` just after it, on the
+ * call's stream (a step that validates records them after its checks).  The
+ * events stay the caller's; (NULL, NULL) stops the recording.  Errors:
+ * SPOPT_EINVAL when only one is NULL; a failed record makes the step return
+ * SPOPT_EDEVICE. */
+SPOPT_API int sparse_opt_set_step_events(void* begin, void* end);
+
 /* ---- canonicalisation --------------------------------------------------- */
 
 /* ---- host-resident state ------------------------------------------------ */
@@ -317,6 +328,29 @@ SPOPT_API int sparse_adam_step(spopt_t h, const spopt_grad* g, void* stream, uin
 /* One sparse SGD step on the touched coordinates (same gradient forms and
  * error rules as sparse_adam_step).  t advances as well. */
 SPOPT_API int sparse_sgd_step(spopt_t h, const spopt_grad* g, void* stream, uint32_t flags);
+
+/* Raw lookups of full table rows -> one optimizer step, in one call: the same
+ * outputs and the same table, bit for bit, as csr_from_lookups(ids, vals, n,
+ * rows, cols, ...) on the handle's rows x cols followed by sparse_adam_step
+ * (Adam handle) or sparse_sgd_step (SGD handle) on the CSR it built, with
+ * out_keys as the touched-row list (n_touched = n, d_n_touched = d_nunique).
+ * The whole of the optirs_gpu sparse_optimizer page's step from a
+ * CooGradient: the canonical gradient ("Canonicalisation"), then the touched
+ * coordinates' update.  In trusted mode the step's work shares the CSR
+ * call's last launch: the combine of sums that cross segment tiles, the
+ * update of every touched row and the row_offsets / col_indices blocks run
+ * side by side (a tile-crossing row is updated by the block that completes
+ * its sum), when cols % 4 == 0 and row_offsets and col_indices are 16-byte
+ * aligned; otherwise, and with SPOPT_VALIDATE, it makes the two calls.
+ *   Arguments: as csr_from_lookups, with rows and cols the handle's.
+ * Errors: those of csr_from_lookups and of the step call; SPOPT_EINVAL for a
+ * NULL handle.  A step the validation rejects leaves the table and t as they
+ * were; the canonical outputs are written all the same. */
+SPOPT_API int sparse_step_from_lookups(spopt_t h, const int64_t* ids, const float* vals, int64_t n,
+                                       int64_t* out_keys, float* out_vals, int32_t* out_counts,
+                                       int64_t* d_nunique, int32_t* row_offsets,
+                                       int32_t* col_indices, void* workspace,
+                                       size_t workspace_bytes, void* stream, uint32_t flags);
 
 /* ---- forward gather ----------------------------------------------------- */
 

@@ -24,7 +24,9 @@ from ._lib import (FORMAT_COO, FORMAT_CSR, KIND_ADAM, KIND_SGD, MODE_DORMANCY, M
 
 __all__ = ["coo_from_lookups", "csr_from_coo", "csr_from_lookups", "csr_to_coo",
            "sparse_opt_workspace_size",
-           "sparse_opt_create", "sparse_adam_step", "sparse_sgd_step", "CooGradient",
+           "sparse_opt_create", "sparse_adam_step", "sparse_sgd_step", "sparse_step_from_lookups",
+           "set_step_events",
+           "CooGradient",
            "CsrGradient", "SparseAdam", "SparseSgd", "SparseOptError", "TRUSTED", "VALIDATE",
            "read_rows", "HostArray"]
 
@@ -248,14 +250,10 @@ def csr_from_coo(coo: CooGradient, rows: int, cols: int, *, row_offsets=None, co
                        n_touched=c.nnz if full else None, d_n_touched=dn if full else None)
 
 
-def csr_from_lookups(ids: torch.Tensor, vals: torch.Tensor, rows: int, *, out_keys=None,
-                     out_vals=None, out_counts=None, d_nunique=None, row_offsets=None,
-                     col_indices=None, want_col_indices=True, workspace=None, stream=None,
-                     validate: bool = False):
-    """Raw lookups of full table rows -> full-row CSR gradient in one call: the
-    result of coo_from_lookups then csr_from_coo(copy_values=False), bit for bit.
-    vals: (n, cols).  Returns (csr, counts, d_nunique): csr.touched_rows holds the
-    distinct ids and csr.values their summed rows (first U = d_nunique entries)."""
+def _lookup_outputs(ids, vals, rows, out_keys, out_vals, out_counts, d_nunique, row_offsets,
+                    col_indices, want_col_indices, workspace):
+    """Checks (and allocates what is not given of) the arrays of a call that
+    takes raw lookups of full rows to the full-row CSR."""
     n = ids.numel()
     cols = vals.shape[1] if vals.dim() == 2 else (vals.numel() // n if n else 1)
     dev = ids.device
@@ -284,10 +282,44 @@ def csr_from_lookups(ids: torch.Tensor, vals: torch.Tensor, rows: int, *, out_ke
     if col_indices is not None:
         _need(col_indices, torch.int32, "col_indices", n * cols)
     _need(workspace, torch.uint8, "workspace")
+    return n, cols, out_keys, out_vals, out_counts, d_nunique, row_offsets, col_indices, workspace
+
+
+def csr_from_lookups(ids: torch.Tensor, vals: torch.Tensor, rows: int, *, out_keys=None,
+                     out_vals=None, out_counts=None, d_nunique=None, row_offsets=None,
+                     col_indices=None, want_col_indices=True, workspace=None, stream=None,
+                     validate: bool = False):
+    """Raw lookups of full table rows -> full-row CSR gradient in one call: the
+    result of coo_from_lookups then csr_from_coo(copy_values=False), bit for bit.
+    vals: (n, cols).  Returns (csr, counts, d_nunique): csr.touched_rows holds the
+    distinct ids and csr.values their summed rows (first U = d_nunique entries)."""
+    (n, cols, out_keys, out_vals, out_counts, d_nunique, row_offsets, col_indices,
+     workspace) = _lookup_outputs(ids, vals, rows, out_keys, out_vals, out_counts, d_nunique,
+                                  row_offsets, col_indices, want_col_indices, workspace)
     check(_lib.lib().csr_from_lookups(_ptr(ids), _ptr(vals), n, rows, cols, _ptr(out_keys),
                                       _ptr(out_vals), _ptr(out_counts), _ptr(d_nunique),
                                       _ptr(row_offsets), _ptr(col_indices), _ptr(workspace),
                                       workspace.numel(), _stream(stream), _flags(validate)))
+    csr = CsrGradient(row_offsets, col_indices, out_vals, rows, cols, touched_rows=out_keys,
+                      n_touched=n, d_n_touched=d_nunique)
+    return csr, out_counts, d_nunique
+
+
+def sparse_step_from_lookups(h: "_Handle", ids: torch.Tensor, vals: torch.Tensor, rows: int, *,
+                             out_keys=None, out_vals=None, out_counts=None, d_nunique=None,
+                             row_offsets=None, col_indices=None, want_col_indices=True,
+                             workspace=None, stream=None, validate: bool = False):
+    """Raw lookups of full rows -> one step of the handle's optimizer in one call:
+    the outputs of csr_from_lookups and the table of the step on that CSR, bit for
+    bit.  rows must be the handle's.  Returns (csr, counts, d_nunique) as
+    csr_from_lookups."""
+    (n, cols, out_keys, out_vals, out_counts, d_nunique, row_offsets, col_indices,
+     workspace) = _lookup_outputs(ids, vals, rows, out_keys, out_vals, out_counts, d_nunique,
+                                  row_offsets, col_indices, want_col_indices, workspace)
+    check(h._L.sparse_step_from_lookups(h._h, _ptr(ids), _ptr(vals), n, _ptr(out_keys),
+                                        _ptr(out_vals), _ptr(out_counts), _ptr(d_nunique),
+                                        _ptr(row_offsets), _ptr(col_indices), _ptr(workspace),
+                                        workspace.numel(), _stream(stream), _flags(validate)))
     csr = CsrGradient(row_offsets, col_indices, out_vals, rows, cols, touched_rows=out_keys,
                       n_touched=n, d_n_touched=d_nunique)
     return csr, out_counts, d_nunique
@@ -360,6 +392,13 @@ def sparse_sgd_step(h: _Handle, grad, *, stream=None, validate: bool = False) ->
     check(h._L.sparse_sgd_step(h._h, C.byref(g), _stream(stream), _flags(validate)))
 
 
+def set_step_events(begin=None, end=None) -> None:
+    """Have the calling thread's step calls record the two HIP events (raw
+    hipEvent_t handles, as ints or ctypes pointers) just before and just after
+    the launch that updates the table; no arguments stop it."""
+    check(_lib.lib().sparse_opt_set_step_events(begin, end))
+
+
 def read_rows(params: torch.Tensor, indices: torch.Tensor, *, out=None, stream=None,
               validate: bool = False) -> torch.Tensor:
     """Forward gather: out[k] = params[indices[k]] (rows of a 2-D float32 table)."""
@@ -414,6 +453,11 @@ class SparseAdam:
     def step(self, grad, *, stream=None, validate=False) -> None:
         sparse_adam_step(self.handle, grad, stream=stream, validate=validate)
 
+    def step_lookups(self, ids: torch.Tensor, vals: torch.Tensor, **kw):
+        """One step from raw lookups of full rows (ids (n,), vals (n, cols));
+        keywords and result as sparse_step_from_lookups."""
+        return sparse_step_from_lookups(self.handle, ids, vals, self.rows, **kw)
+
     def read_rows(self, indices: torch.Tensor, *, out=None, stream=None, validate=False):
         """The current rows of the table for a batch of lookups (forward pass)."""
         return read_rows(self.params, indices, out=out, stream=stream, validate=validate)
@@ -457,3 +501,7 @@ class SparseSgd:
 
     def step(self, grad, *, stream=None, validate=False) -> None:
         sparse_sgd_step(self.handle, grad, stream=stream, validate=validate)
+
+    def step_lookups(self, ids: torch.Tensor, vals: torch.Tensor, **kw):
+        """One step from raw lookups of full rows; as SparseAdam.step_lookups."""
+        return sparse_step_from_lookups(self.handle, ids, vals, self.rows, **kw)

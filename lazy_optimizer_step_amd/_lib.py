@@ -104,6 +104,11 @@ def lib() -> C.CDLL:
         L.sparse_opt_host_device_pointer.restype = C.c_int
         L.sparse_opt_host_device_pointer.argtypes = [P, C.POINTER(P)]
         L.sparse_sgd_step.restype = C.c_int
+        L.sparse_step_from_lookups.argtypes = [P, P, P, I64, P, P, P, P, P, P, P, C.c_size_t, P,
+                                               U32]
+        L.sparse_step_from_lookups.restype = C.c_int
+        L.sparse_opt_set_step_events.argtypes = [P, P]
+        L.sparse_opt_set_step_events.restype = C.c_int
         _lib = L
     return _lib
 
@@ -116,5 +121,5 @@ def check(rc: int) -> None:
 EXPORTED = ("sparse_opt_create", "sparse_opt_destroy", "sparse_opt_get_step", "sparse_opt_set_step",
             "sparse_opt_last_error", "sparse_opt_workspace_size", "coo_from_lookups",
             "csr_from_coo", "csr_from_lookups", "csr_to_coo", "sparse_adam_step",
-            "sparse_sgd_step", "read_rows",
+            "sparse_sgd_step", "sparse_step_from_lookups", "sparse_opt_set_step_events", "read_rows",
             "sparse_opt_host_alloc", "sparse_opt_host_free", "sparse_opt_host_device_pointer")

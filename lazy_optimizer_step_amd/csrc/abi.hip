@@ -297,18 +297,29 @@ static int validate_grad(const spopt_optimizer* h, const spopt_grad* g, const in
     });
 }
 
-extern "C" int sparse_adam_step(spopt_t h, const spopt_grad* g, void* stream, uint32_t flags) {
-    hipStream_t s = (hipStream_t)stream;
-    if (h == nullptr) return fail(SPOPT_EINVAL, "sparse_adam_step: NULL handle");
-    if (h->kind != SPOPT_KIND_ADAM) return fail(SPOPT_EINVAL, "sparse_adam_step: not an Adam handle");
-    int rc = check_grad_shape(h, g, "sparse_adam_step");
-    if (rc) return rc;
-    const int64_t t = h->t + 1;
-    if (t >= INT32_MAX) return fail(SPOPT_EINVAL, "sparse_adam_step: t would reach 2^31");
-    if (flags & SPOPT_VALIDATE) {
-        rc = validate_grad(h, g, h->ls, (int32_t)t, s, "sparse_adam_step");
-        if (rc) return rc;
-    }
+// Events a caller asked to have recorded, on the call's stream, just before
+// and just after the launch that updates the table (per host thread).
+static thread_local hipEvent_t t_ev_begin = nullptr;
+static thread_local hipEvent_t t_ev_end = nullptr;
+
+extern "C" int sparse_opt_set_step_events(void* begin, void* end) {
+    if ((begin == nullptr) != (end == nullptr))
+        return fail(SPOPT_EINVAL, "sparse_opt_set_step_events: give both events or neither");
+    t_ev_begin = (hipEvent_t)begin;
+    t_ev_end = (hipEvent_t)end;
+    return SPOPT_OK;
+}
+
+static int step_event(hipEvent_t e, hipStream_t s, const char* what) {
+    if (e == nullptr) return SPOPT_OK;
+    const hipError_t err = hipEventRecord(e, s);
+    if (err != hipSuccess)
+        return fail(SPOPT_EDEVICE, "%s: hipEventRecord: %s", what, hipGetErrorString(err));
+    return SPOPT_OK;
+}
+
+// Per-step scalars of Adam at step t, in double on the host.
+static AdamScalars adam_scalars(const spopt_optimizer* h, int64_t t) {
     const spopt_adam_config& c = h->adam;
     AdamScalars a;
     a.lr = c.lr;
@@ -326,11 +337,34 @@ extern "C" int sparse_adam_step(spopt_t h, const spopt_grad* g, void* stream, ui
     a.t = (int32_t)t;
     a.wd = c.weight_decay;
     a.lr_wd = c.lr * c.weight_decay;
-    const int wd_kind = c.weight_decay == 0.0 ? kWdNone
-                        : c.weight_decay_mode == SPOPT_WD_L2 ? kWdL2 : kWdDecoupled;
+    return a;
+}
+
+static int adam_wd_kind(const spopt_adam_config& c) {
+    return c.weight_decay == 0.0 ? kWdNone
+           : c.weight_decay_mode == SPOPT_WD_L2 ? kWdL2 : kWdDecoupled;
+}
+
+extern "C" int sparse_adam_step(spopt_t h, const spopt_grad* g, void* stream, uint32_t flags) {
+    hipStream_t s = (hipStream_t)stream;
+    if (h == nullptr) return fail(SPOPT_EINVAL, "sparse_adam_step: NULL handle");
+    if (h->kind != SPOPT_KIND_ADAM) return fail(SPOPT_EINVAL, "sparse_adam_step: not an Adam handle");
+    int rc = check_grad_shape(h, g, "sparse_adam_step");
+    if (rc) return rc;
+    const int64_t t = h->t + 1;
+    if (t >= INT32_MAX) return fail(SPOPT_EINVAL, "sparse_adam_step: t would reach 2^31");
+    if (flags & SPOPT_VALIDATE) {
+        rc = validate_grad(h, g, h->ls, (int32_t)t, s, "sparse_adam_step");
+        if (rc) return rc;
+    }
+    const spopt_adam_config& c = h->adam;
+    const AdamScalars a = adam_scalars(h, t);
+    const int wd_kind = adam_wd_kind(c);
+    if ((rc = step_event(t_ev_begin, s, "sparse_adam_step"))) return rc;
     rc = launch_adam(h->p, h->m, h->v, h->ls, c.last_step_per_row != 0, a, c.mode, wd_kind, g,
                      h->rows, h->cols, s);
     if (rc) return rc;
+    if ((rc = step_event(t_ev_end, s, "sparse_adam_step"))) return rc;
     h->t = t;
     return SPOPT_OK;
 }
@@ -348,8 +382,60 @@ extern "C" int sparse_sgd_step(spopt_t h, const spopt_grad* g, void* stream, uin
         if (rc) return rc;
     }
     const spopt_sgd_config& c = h->sgd;
+    if ((rc = step_event(t_ev_begin, s, "sparse_sgd_step"))) return rc;
     rc = launch_sgd(h->p, h->m, c.lr, c.momentum, c.weight_decay, g, h->rows, h->cols, s);
     if (rc) return rc;
+    if ((rc = step_event(t_ev_end, s, "sparse_sgd_step"))) return rc;
+    h->t = t;
+    return SPOPT_OK;
+}
+
+extern "C" int sparse_step_from_lookups(spopt_t h, const int64_t* ids, const float* vals,
+                                        int64_t n, int64_t* out_keys, float* out_vals,
+                                        int32_t* out_counts, int64_t* d_nunique,
+                                        int32_t* row_offsets, int32_t* col_indices,
+                                        void* workspace, size_t workspace_bytes, void* stream,
+                                        uint32_t flags) {
+    hipStream_t s = (hipStream_t)stream;
+    if (h == nullptr) return fail(SPOPT_EINVAL, "sparse_step_from_lookups: NULL handle");
+    if (h->kind != SPOPT_KIND_ADAM && h->kind != SPOPT_KIND_SGD)
+        return fail(SPOPT_EINVAL, "sparse_step_from_lookups: unknown handle kind");
+    const int64_t t = h->t + 1;
+    if (t >= INT32_MAX) return fail(SPOPT_EINVAL, "sparse_step_from_lookups: t would reach 2^31");
+    FusedCsr f;
+    bool deferred = false;
+    int rc = csr_lookups_run(ids, vals, n, h->rows, h->cols, out_keys, out_vals, out_counts,
+                             d_nunique, row_offsets, col_indices, workspace, workspace_bytes, s,
+                             flags, &f, &deferred);
+    if (rc) return rc;
+    if (!deferred) {
+        // Validated, or a layout the fused launch does not take: the step
+        // call on the CSR just built.
+        spopt_grad g;
+        memset(&g, 0, sizeof(g));
+        g.format = SPOPT_FORMAT_CSR;
+        g.csr.rows = h->rows;
+        g.csr.cols = h->cols;
+        g.csr.row_offsets = row_offsets;
+        g.csr.col_indices = col_indices;
+        g.csr.values = out_vals;
+        g.csr.touched_rows = out_keys;
+        g.csr.n_touched = n;
+        g.csr.d_n_touched = d_nunique;
+        return h->kind == SPOPT_KIND_ADAM ? sparse_adam_step(h, &g, stream, flags)
+                                          : sparse_sgd_step(h, &g, stream, flags);
+    }
+    if ((rc = step_event(t_ev_begin, s, "sparse_step_from_lookups"))) return rc;
+    if (h->kind == SPOPT_KIND_ADAM) {
+        const spopt_adam_config& c = h->adam;
+        rc = launch_adam_fused(h->p, h->m, h->v, h->ls, c.last_step_per_row != 0,
+                               adam_scalars(h, t), c.mode, adam_wd_kind(c), f, s);
+    } else {
+        const spopt_sgd_config& c = h->sgd;
+        rc = launch_sgd_fused(h->p, h->m, c.lr, c.momentum, c.weight_decay, f, s);
+    }
+    if (rc) return rc;
+    if ((rc = step_event(t_ev_end, s, "sparse_step_from_lookups"))) return rc;
     h->t = t;
     return SPOPT_OK;
 }

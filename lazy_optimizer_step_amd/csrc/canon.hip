@@ -27,6 +27,7 @@
 
 #include "common.hpp"
 #include "csr_full.hpp"
+#include "seg_combine.hpp"
 
 namespace spopt {
 
@@ -38,13 +39,7 @@ constexpr int kTile = kSortThreads * kIpt;      // lookups per radix-pass tile
 constexpr int kRadixBits = 8;                   // at most 256 buckets per radix pass
 constexpr int kRadix = 1 << kRadixBits;
 constexpr int kMaxPasses = 8;
-constexpr int kSumWaves = 16;                   // waves per segment-and-sum block
-constexpr int kSumThreads = kSumWaves * kWave;
-constexpr int kSumRows = 16;                    // sorted lookups per wave (lanes 0..15)
-constexpr int kSumTile = kSumWaves * kSumRows;  // sorted lookups per such block
-constexpr int kTilePartials = 8;                // partials one wave adds alone in the combine
 constexpr int kFixWaves2 = 16;                  // waves of the combining block
-constexpr int kFixRuns = 16;                    // runs of a segment with more partials
 // Per-block key counts for csr_from_lookups are kept for tables of fewer rows.
 constexpr int64_t kBndMaxRows = ((int64_t)1 << 31) - 1;
 
@@ -507,21 +502,6 @@ __device__ __forceinline__ void load_row(float (&r)[V], const float* row, int64_
 }
 
 template <int V>
-__device__ __forceinline__ void store_row(float* dst, const double (&r)[V], int64_t col,
-                                          int64_t width) {
-    if (col < width) {
-        if constexpr (V == 4) {
-            *reinterpret_cast<float4*>(dst) =
-                make_float4((float)r[0], (float)r[1], (float)r[2], (float)r[3]);
-        } else if constexpr (V == 2) {
-            *reinterpret_cast<float2*>(dst) = make_float2((float)r[0], (float)r[1]);
-        } else {
-            dst[0] = (float)r[0];
-        }
-    }
-}
-
-template <int V>
 __device__ __forceinline__ void store_row_f(float* dst, const float (&r)[V], int64_t col,
                                             int64_t width) {
     if (col < width) {
@@ -532,18 +512,6 @@ __device__ __forceinline__ void store_row_f(float* dst, const float (&r)[V], int
         } else {
             dst[0] = r[0];
         }
-    }
-}
-
-// Partial sums of segments that cross a chunk boundary stay in double.
-template <int V>
-__device__ __forceinline__ void load_part(double (&r)[V], const double* src, int64_t col,
-                                          int64_t width) {
-#pragma unroll
-    for (int v = 0; v < V; ++v) {
-        const bool in = col + v < width;
-        const double x = src[in ? v : -col];  // past the row: its first column
-        r[v] = in ? x : 0.0;
     }
 }
 
@@ -897,87 +865,6 @@ __global__ __launch_bounds__(kSumThreads) void k_seg_sum(
     }
 }
 
-// Adds partials q in [lo, hi) of a segment whose start tile is `tile` (q = 0:
-// tlast[tile], q > 0: tfirst[tile + q]) in increasing q, D loads in flight
-// (past hi, partial lo is reloaded and unused).
-template <int V, int D>
-__device__ __forceinline__ void add_partials(double (&acc)[V], const double* tfirst,
-                                             const double* tlast, int64_t tile, int64_t lo,
-                                             int64_t hi, int64_t width, int64_t col) {
-    for (int64_t q0 = lo; q0 < hi; q0 += D) {
-        double row[D][V];
-#pragma unroll
-        for (int u = 0; u < D; ++u) {
-            const int64_t q = q0 + u < hi ? q0 + u : lo;
-            const double* src = (q == 0) ? tlast + tile * width : tfirst + (tile + q) * width;
-            load_part<V>(row[u], src + col, col, width);
-        }
-#pragma unroll
-        for (int u = 0; u < D; ++u)
-            if (q0 + u < hi) {
-#pragma unroll
-                for (int v = 0; v < V; ++v) acc[v] += row[u][v];
-            }
-    }
-}
-
-// Segments that cross tiles, one block per tile that starts one (tcross):
-// m partials (tlast of the start tile, tfirst of each following tile up to
-// the one where it ends).  The order of the additions depends on m only, so
-// the result is the same run to run and whatever the block's shape: up to
-// kTilePartials partials are added in tile order by wave 0; beyond, [0, m) is
-// cut into kFixRuns equal runs, each added in tile order (run r by wave
-// r mod W), and wave 0 adds the run sums in run order.  The block also writes
-// the segment's count.  part: LDS, kFixRuns rows.
-template <int V, int W>
-__device__ __forceinline__ void tile_fixup_body(
-    int64_t tile, const int32_t* __restrict__ tcross, const int32_t* __restrict__ seg_start,
-    const double* __restrict__ tfirst, const double* __restrict__ tlast, int64_t width,
-    float* __restrict__ out_vals, int32_t* __restrict__ out_counts, const uint32_t* status,
-    double (*part)[kWave * V]) {
-    const uint32_t st0 = *status;  // loaded together with the crossing segment
-    const int32_t seg = tcross[tile];
-    if (st0 != 0u || seg < 0) return;
-    const int w = (int)(threadIdx.x >> 6);
-    const int lane = lane_id();
-    const int64_t s0 = seg_start[seg], s1 = seg_start[seg + 1];
-    if (threadIdx.x == 0) out_counts[seg] = (int32_t)(s1 - s0);
-    const int64_t m = (s1 - 1) / kSumTile - tile + 1;
-    for (int64_t c0 = 0; c0 < width; c0 += (int64_t)kWave * V) {
-        const int64_t col = c0 + (int64_t)lane * V;
-        if (m <= kTilePartials) {
-            if (w == 0) {
-                double tot[V];
-#pragma unroll
-                for (int v = 0; v < V; ++v) tot[v] = 0.0;
-                add_partials<V, (V == 4 ? 4 : 8)>(tot, tfirst, tlast, tile, 0, m, width, col);
-                store_row<V>(out_vals + (int64_t)seg * width + col, tot, col, width);
-            }
-            continue;
-        }
-        for (int r = w; r < kFixRuns; r += W) {
-            const int64_t lo = m * r / kFixRuns, hi = m * (r + 1) / kFixRuns;
-            double acc[V];
-#pragma unroll
-            for (int v = 0; v < V; ++v) acc[v] = 0.0;
-            add_partials<V, (V == 4 ? 4 : 8)>(acc, tfirst, tlast, tile, lo, hi, width, col);
-#pragma unroll
-            for (int v = 0; v < V; ++v) part[r][lane * V + v] = acc[v];
-        }
-        __syncthreads();
-        if (w == 0) {
-            double tot[V];
-#pragma unroll
-            for (int v = 0; v < V; ++v) tot[v] = part[0][lane * V + v];
-            for (int r = 1; r < kFixRuns; ++r)
-#pragma unroll
-                for (int v = 0; v < V; ++v) tot[v] += part[r][lane * V + v];
-            store_row<V>(out_vals + (int64_t)seg * width + col, tot, col, width);
-        }
-        __syncthreads();
-    }
-}
-
 template <int V>
 __global__ __launch_bounds__(kFixWaves2 * kWave) void k_tile_fixup(
     const int32_t* __restrict__ tcross, const int32_t* __restrict__ seg_start,
@@ -1198,12 +1085,14 @@ extern "C" int coo_from_lookups(const int64_t* ids, const float* vals, int64_t n
                      nullptr, true);
 }
 
-extern "C" int csr_from_lookups(const int64_t* ids, const float* vals, int64_t n, int64_t rows,
-                                int64_t cols, int64_t* out_keys, float* out_vals,
-                                int32_t* out_counts, int64_t* d_nunique, int32_t* row_offsets,
-                                int32_t* col_indices, void* workspace, size_t workspace_bytes,
-                                void* stream, uint32_t flags) {
-    hipStream_t st = (hipStream_t)stream;
+namespace spopt {
+
+int csr_lookups_run(const int64_t* ids, const float* vals, int64_t n, int64_t rows, int64_t cols,
+                    int64_t* out_keys, float* out_vals, int32_t* out_counts, int64_t* d_nunique,
+                    int32_t* row_offsets, int32_t* col_indices, void* workspace,
+                    size_t workspace_bytes, hipStream_t st, uint32_t flags, FusedCsr* defer,
+                    bool* deferred) {
+    if (deferred) *deferred = false;
     if (row_offsets == nullptr || rows < 1 || cols < 1)
         return fail(SPOPT_EINVAL, "csr_from_lookups: NULL row_offsets or bad size");
     if (n * cols >= ((int64_t)1 << 31))
@@ -1222,30 +1111,47 @@ extern "C" int csr_from_lookups(const int64_t* ids, const float* vals, int64_t n
         if (rc) return rc;
         spopt_coo coo{rows, cols, n, d_nunique, out_keys, out_vals};
         return csr_from_coo(&coo, rows, cols, row_offsets, col_indices, out_vals, nullptr,
-                            nullptr, stream, 0u);
+                            nullptr, (void*)st, 0u);
     }
     char* ws = (char*)workspace;
     int32_t* bnd = (n > 0 && L.bnd_entries > 0) ? (int32_t*)(ws + L.off_bnd) : nullptr;
     int rc = canon_run("csr_from_lookups", ids, vals, n, cols, rows, out_keys, out_vals,
                        out_counts, d_nunique, workspace, workspace_bytes, st, flags, bnd, false);
     if (rc) return rc;
-    const int64_t nfix = n > 0 ? L.nsum : 0;
-    const int64_t nblk_ro = rows / kRoBits + 1;
-    int64_t nblk_ci = 0;
+    FusedCsr f;
+    f.nfix = n > 0 ? L.nsum : 0;
+    f.nblk_ro = rows / kRoBits + 1;
+    f.nblk_ci = 0;
     if (col_indices != nullptr) {
-        nblk_ci = ceil_div(n * cols / 4, kRoThreads);
-        if (nblk_ci > 1024) nblk_ci = 1024;
-        if (nblk_ci < 1) nblk_ci = 1;
+        f.nblk_ci = ceil_div(n * cols / 4, kRoThreads);
+        if (f.nblk_ci > 1024) f.nblk_ci = 1024;
+        if (f.nblk_ci < 1) f.nblk_ci = 1;
     }
-    const int32_t* tcross = n > 0 ? (const int32_t*)(ws + L.off_tcross) : nullptr;
-    const int32_t* seg_start = n > 0 ? (const int32_t*)(ws + L.off_segstart) : nullptr;
-    const double* tfirst = n > 0 ? (const double*)(ws + L.off_tfirst) : nullptr;
-    const double* tlast = n > 0 ? (const double*)(ws + L.off_tlast) : nullptr;
-    const uint32_t* status = n > 0 ? (const uint32_t*)(ws + L.off_status) : nullptr;
+    f.tcross = n > 0 ? (const int32_t*)(ws + L.off_tcross) : nullptr;
+    f.seg_start = n > 0 ? (const int32_t*)(ws + L.off_segstart) : nullptr;
+    f.tfirst = n > 0 ? (const double*)(ws + L.off_tfirst) : nullptr;
+    f.tlast = n > 0 ? (const double*)(ws + L.off_tlast) : nullptr;
+    f.status = n > 0 ? (const uint32_t*)(ws + L.off_status) : nullptr;
+    f.keys = out_keys;
+    f.vals = out_vals;
+    f.counts = out_counts;
+    f.d_n = d_nunique;
+    f.n = n;
+    f.rows = rows;
+    f.cols = cols;
+    f.row_offsets = row_offsets;
+    f.col_indices = col_indices;
+    f.bnd = bnd;
+    if (defer != nullptr && deferred != nullptr && (flags & SPOPT_VALIDATE) == 0u &&
+        aligned16(row_offsets)) {
+        *defer = f;
+        *deferred = true;
+        return SPOPT_OK;
+    }
     auto go = [&](auto kernel) {
-        kernel<<<(unsigned)(nfix + nblk_ci + nblk_ro), kRoThreads, 0, st>>>(
-            tcross, seg_start, tfirst, tlast, cols, out_vals, out_counts, status, nfix, out_keys,
-            d_nunique, n, rows, row_offsets, nblk_ci, col_indices, bnd);
+        kernel<<<(unsigned)(f.nfix + f.nblk_ci + f.nblk_ro), kRoThreads, 0, st>>>(
+            f.tcross, f.seg_start, f.tfirst, f.tlast, cols, out_vals, out_counts, f.status,
+            f.nfix, out_keys, d_nunique, n, rows, row_offsets, f.nblk_ci, col_indices, bnd);
     };
     if (aligned16(row_offsets))
         go(k_fix_csr<true>);
@@ -1253,4 +1159,16 @@ extern "C" int csr_from_lookups(const int64_t* ids, const float* vals, int64_t n
         go(k_fix_csr<false>);
     SPOPT_LAUNCHED();
     return SPOPT_OK;
+}
+
+}  // namespace spopt
+
+extern "C" int csr_from_lookups(const int64_t* ids, const float* vals, int64_t n, int64_t rows,
+                                int64_t cols, int64_t* out_keys, float* out_vals,
+                                int32_t* out_counts, int64_t* d_nunique, int32_t* row_offsets,
+                                int32_t* col_indices, void* workspace, size_t workspace_bytes,
+                                void* stream, uint32_t flags) {
+    return csr_lookups_run(ids, vals, n, rows, cols, out_keys, out_vals, out_counts, d_nunique,
+                           row_offsets, col_indices, workspace, workspace_bytes,
+                           (hipStream_t)stream, flags, nullptr, nullptr);
 }

@@ -154,6 +154,47 @@ int launch_adam(float* p, float* m, float* v, int32_t* ls, bool ls_per_row, cons
 int launch_sgd(float* p, float* b, double lr, double mu, double wd, const spopt_grad* gr,
                int64_t rows, int64_t cols, hipStream_t s);
 
+// What is left of csr_from_lookups after its segment kernel, when a step from
+// raw lookups finishes it in the update's own launch: the combine of the
+// segments that cross segment tiles (nfix blocks, one per tile), the
+// col_indices blocks (nblk_ci, none without col_indices) and the row_offsets
+// blocks (nblk_ro).  keys/vals/counts are the canonical outputs (n lookups at
+// most; the distinct count on the device at d_n); tcross .. status point into
+// the call's workspace; bnd (or NULL) holds the id counts below each 8192-row
+// block.  row_offsets is 16-byte aligned and cols a multiple of 4.
+struct FusedCsr {
+    const int32_t* tcross;
+    const int32_t* seg_start;
+    const double* tfirst;
+    const double* tlast;
+    const uint32_t* status;
+    int64_t nfix;
+    const int64_t* keys;
+    float* vals;
+    int32_t* counts;
+    const int64_t* d_n;
+    int64_t n, rows, cols;
+    int32_t* row_offsets;
+    int32_t* col_indices;
+    const int32_t* bnd;
+    int64_t nblk_ci, nblk_ro;
+};
+
+// csr_from_lookups with `defer` != NULL: when the call can hand its last
+// launch over (trusted, cols % 4 == 0, row_offsets and col_indices 16-byte
+// aligned) it fills *defer and returns with *deferred = true; otherwise it
+// completes the CSR itself (*deferred = false).
+int csr_lookups_run(const int64_t* ids, const float* vals, int64_t n, int64_t rows, int64_t cols,
+                    int64_t* out_keys, float* out_vals, int32_t* out_counts, int64_t* d_nunique,
+                    int32_t* row_offsets, int32_t* col_indices, void* workspace,
+                    size_t workspace_bytes, hipStream_t s, uint32_t flags, FusedCsr* defer,
+                    bool* deferred);
+int launch_adam_fused(float* p, float* m, float* v, int32_t* ls, bool ls_per_row,
+                      const AdamScalars& a, int mode, int wd_kind, const FusedCsr& f,
+                      hipStream_t s);
+int launch_sgd_fused(float* p, float* b, double lr, double mu, double wd, const FusedCsr& f,
+                     hipStream_t s);
+
 // A validated call: serialised with every other validated call of the
 // process, it clears the device's status block, lets `launch` enqueue its
 // checks into it, and reads it back (one synchronisation of `s`).

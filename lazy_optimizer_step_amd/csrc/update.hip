@@ -27,6 +27,8 @@
 // (CSR) or the keys of a full-row COO; without a list the CSR kernel scans
 // row_offsets 64 rows per wave.
 #include "common.hpp"
+#include "csr_full.hpp"
+#include "seg_combine.hpp"
 
 namespace spopt {
 
@@ -226,6 +228,23 @@ struct SrcBlockCoo {
     __device__ __forceinline__ int64_t col(int64_t, int64_t j) const { return j; }
 };
 
+// The segments of the lookup canonicalisation, still in the workspace: row
+// keys[k], values at k*cols.  A segment that crosses a segment tile is left
+// out (len 0): its sum is not complete until the combine, whose block updates
+// that row itself.
+struct SrcSegs {
+    const int64_t* __restrict__ keys;
+    const int32_t* __restrict__ seg_start;
+    int64_t cols;
+    __device__ __forceinline__ void get(int64_t k, int64_t& row, int64_t& st, int64_t& len) const {
+        row = keys[k];
+        st = k * cols;
+        const int32_t a = seg_start[k], b = seg_start[k + 1];
+        len = (a / kSumTile == (b - 1) / kSumTile) ? cols : 0;
+    }
+    __device__ __forceinline__ int64_t col(int64_t, int64_t j) const { return j; }
+};
+
 // Touched rows of a CSR gradient.
 struct SrcCsrTouched {
     const int64_t* __restrict__ touched;
@@ -248,25 +267,61 @@ struct SrcCsrTouched {
     }
 };
 
-// Each wave takes a batch of RPW*ITERS consecutive touched rows.  Lanes
-// 0..RPW*ITERS-1 first fetch one row each (id, start of its values, length),
-// so the dependent index loads of the whole batch cost one round trip; then
-// every sub-group issues the 16-byte loads of all ITERS of its full rows
-// before it computes and stores any of them.  Partial rows (and rows whose
-// values are not 16-byte aligned) take a scalar loop, one lane per entry.
+// One touched row (id `row`, values g[st, st + len)) by the LPR lanes sl of a
+// group: 16-byte vectors when the row is full and aligned, else one lane per
+// entry.  With one last_step per row, every lane reads it before any lane of
+// the row writes it (the loads of the first pass below, or row_last), and it
+// is written once the row is done.
+template <class Op, class Src>
+__device__ __forceinline__ void update_row(const Op& op, const Src& src, int64_t row, int64_t st,
+                                           int64_t len, int64_t cols, const float* __restrict__ g,
+                                           bool vec_ok, int sl, int lpr) {
+    const int64_t base = row * cols;
+    const int32_t rl = op.row_last(row);
+    if (vec_ok && len == cols && (st & 3) == 0) {
+        const int64_t nvec = cols >> 2;
+        for (int64_t c4 = sl; c4 < nvec; c4 += lpr) {
+            typename Op::Vec r;
+            typename Op::Aux x;
+            op.load(base + 4 * c4, row, r);
+            if constexpr (Op::kLsRow) r.ls = make_int4(rl, rl, rl, rl);
+            const float4 gv = *reinterpret_cast<const float4*>(g + st + 4 * c4);
+            op.prep(r, x);
+            op.compute(r, x, gv);
+            op.store(base + 4 * c4, row, r);
+        }
+    } else {
+        const int64_t n = len < cols ? len : cols;
+        for (int64_t j = sl; j < n; j += lpr) {
+            const int64_t c = src.col(st, j);
+            if ((uint64_t)c < (uint64_t)cols) op.scalar(base + c, rl, g[st + j]);
+        }
+        op.row_done(row);
+    }
+}
+
+// The touched rows of block `bid` of `nblk` (the waves of all nblk blocks
+// stride over them together).  Each wave takes a batch of RPW*ITERS
+// consecutive touched rows.  Lanes 0..RPW*ITERS-1 first fetch one row each
+// (id, start of its values, length), so the dependent index loads of the
+// whole batch cost one round trip; then every sub-group issues the 16-byte
+// loads of all ITERS of its full rows before it computes and stores any of
+// them.  Partial rows (and rows whose values are not 16-byte aligned) take a
+// scalar loop, one lane per entry.
 template <class Op, class Src, int LPR, int ITERS>
-__global__ __launch_bounds__(256) void k_update_rows(Op op, Src src, const int64_t* d_count,
-                                                     int64_t count_host, int64_t rows,
-                                                     int64_t cols, const float* __restrict__ g,
-                                                     int vec_ok) {
+__device__ __forceinline__ void update_rows_body(const Op& op, const Src& src,
+                                                 const int64_t* d_count, int64_t count_host,
+                                                 int64_t rows, int64_t cols,
+                                                 const float* __restrict__ g, int vec_ok,
+                                                 int64_t bid, int64_t nblk) {
     const int64_t count = d_count ? (*d_count < count_host ? *d_count : count_host) : count_host;
     constexpr int RPW = kWave / LPR;
     constexpr int BATCH = RPW * ITERS;
     static_assert(BATCH <= kWave, "one lane per row of the batch");
     const int lane = lane_id();
     const int sub = lane / LPR, sl = lane % LPR;
-    const int64_t gw = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
-    const int64_t nw = ((int64_t)gridDim.x * blockDim.x) >> 6;
+    const int64_t gw = (bid * blockDim.x + threadIdx.x) >> 6;
+    const int64_t nw = (nblk * blockDim.x) >> 6;
     const int64_t nvec = cols >> 2;
     for (int64_t k0 = gw * BATCH; k0 < count; k0 += nw * BATCH) {
         int64_t prow = -1, pst = 0, plen = 0;
@@ -323,35 +378,65 @@ __global__ __launch_bounds__(256) void k_update_rows(Op op, Src src, const int64
             }
         } else {
 #pragma unroll
-            for (int it = 0; it < ITERS; ++it) {
-                if (len[it] <= 0) continue;
-                const int64_t base = row[it] * cols;
-                // One last_step per row: every lane reads it before any lane
-                // of the row writes it (the loads of the first pass below, or
-                // row_last), and it is written once the row is done.
-                const int32_t rl = op.row_last(row[it]);
-                if (vec_ok && len[it] == cols && (st[it] & 3) == 0) {
-                    for (int64_t c4 = sl; c4 < nvec; c4 += LPR) {
-                        typename Op::Vec r;
-                        typename Op::Aux x;
-                        op.load(base + 4 * c4, row[it], r);
-                        if constexpr (Op::kLsRow) r.ls = make_int4(rl, rl, rl, rl);
-                        const float4 gv = *reinterpret_cast<const float4*>(g + st[it] + 4 * c4);
-                        op.prep(r, x);
-                        op.compute(r, x, gv);
-                        op.store(base + 4 * c4, row[it], r);
-                    }
-                } else {
-                    const int64_t n = len[it] < cols ? len[it] : cols;
-                    for (int64_t j = sl; j < n; j += LPR) {
-                        const int64_t c = src.col(st[it], j);
-                        if ((uint64_t)c < (uint64_t)cols) op.scalar(base + c, rl, g[st[it] + j]);
-                    }
-                    op.row_done(row[it]);
-                }
-            }
+            for (int it = 0; it < ITERS; ++it)
+                if (len[it] > 0)
+                    update_row(op, src, row[it], st[it], len[it], cols, g, vec_ok != 0, sl, LPR);
         }
     }
+}
+
+template <class Op, class Src, int LPR, int ITERS>
+__global__ __launch_bounds__(256) void k_update_rows(Op op, Src src, const int64_t* d_count,
+                                                     int64_t count_host, int64_t rows,
+                                                     int64_t cols, const float* __restrict__ g,
+                                                     int vec_ok) {
+    update_rows_body<Op, Src, LPR, ITERS>(op, src, d_count, count_host, rows, cols, g, vec_ok,
+                                          blockIdx.x, gridDim.x);
+}
+
+// The step from raw lookups after the segment kernel, in one launch of
+// 256-thread blocks, none of which waits on another:
+//   [0, nfix)            the combine of the segment that crosses out of
+//                        segment tile b, if any, then the update of its row
+//                        from the combined sums (read back after a barrier);
+//   [nfix, nfix + nupd)  the update of every segment that lies within one
+//                        tile, as k_update_rows;
+//   then the col_indices and row_offsets blocks of the CSR.
+// Each coordinate's arithmetic and each sum's order of additions are those
+// of the canonicalisation and step calls, so the results are the same bit for
+// bit.
+template <class Op, int LPR, int ITERS>
+__global__ __launch_bounds__(256) void k_step_lookups(Op op, FusedCsr f, int64_t nupd,
+                                                      int vec_ok) {
+    __shared__ double part[kFixRuns][kWave];
+    int64_t b = blockIdx.x;
+    if (b < f.nfix) {
+        const int32_t seg = tile_fixup_body<1, 256 / kWave>(b, f.tcross, f.seg_start, f.tfirst,
+                                                            f.tlast, f.cols, f.vals, f.counts,
+                                                            f.status, part);
+        if (seg < 0) return;
+        __syncthreads();
+        if (threadIdx.x < kWave) {
+            const int64_t row = f.keys[seg];
+            if ((uint64_t)row < (uint64_t)f.rows)
+                update_row(op, SrcSegs{f.keys, f.seg_start, f.cols}, row, (int64_t)seg * f.cols,
+                           f.cols, f.cols, f.vals, vec_ok != 0, lane_id(), kWave);
+        }
+        return;
+    }
+    b -= f.nfix;
+    if (b < nupd) {
+        update_rows_body<Op, SrcSegs, LPR, ITERS>(op, SrcSegs{f.keys, f.seg_start, f.cols}, f.d_n,
+                                                  f.n, f.rows, f.cols, f.vals, vec_ok, b, nupd);
+        return;
+    }
+    b -= nupd;
+    const int64_t nnz = *f.d_n < f.n ? *f.d_n : f.n;
+    if (b < f.nblk_ci) {
+        csr_col_block(b, f.nblk_ci, nnz, f.cols, f.col_indices);
+        return;
+    }
+    csr_row_block<true>(b - f.nblk_ci, f.keys, f.n, nnz, f.rows, f.cols, f.row_offsets, f.bnd);
 }
 
 // CSR without a touched-row list: one wave per 64 rows of row_offsets.
@@ -417,6 +502,11 @@ static int lanes_per_row(int64_t cols) {
     return 64;
 }
 
+// Blocks of a row-update launch: about what the chip holds at once (256 CUs,
+// 3-4 of these blocks each); the waves stride over the rows beyond.  More
+// blocks only queue empty ones ahead of whatever the launch does next.
+constexpr int64_t kUpdateBlocks = 1024;
+
 static unsigned grid_cap(int64_t blocks, int64_t cap = 4096) {
     if (blocks < 1) blocks = 1;
     return (unsigned)(blocks < cap ? blocks : cap);
@@ -431,18 +521,25 @@ struct RowBatch<AdamOp<MODE, WD, LSROW>> {
     static constexpr int kIters = 2;  // Adam holds more state per row in registers
 };
 
+// Touched rows one 256-thread block takes per round (4 lanes per row: one
+// row per sub-group at a time).
+template <class Op>
+static int64_t update_rows_per_block(int lpr) {
+    return 4 * (kWave / lpr) * (lpr == 4 ? 1 : RowBatch<Op>::kIters);
+}
+
 template <class Op, class Src>
 static int launch_rows(const Op& op, const Src& src, const int64_t* d_count, int64_t count,
                        int64_t rows, int64_t cols, const float* g, bool vec_ok, hipStream_t s) {
     constexpr int kIters = RowBatch<Op>::kIters;
     const int lpr = lanes_per_row(cols);
-    const int64_t rows_per_block = 4 * (kWave / lpr) * kIters;
-    const unsigned grid = grid_cap(ceil_div(count, rows_per_block));
+    const unsigned grid =
+        grid_cap(ceil_div(count, update_rows_per_block<Op>(lpr)), kUpdateBlocks);
     const int v = vec_ok ? 1 : 0;
     switch (lpr) {
         case 4:
-            k_update_rows<Op, Src, 4, 1><<<grid_cap(ceil_div(count, 64)), 256, 0, s>>>(
-                op, src, d_count, count, rows, cols, g, v);
+            k_update_rows<Op, Src, 4, 1><<<grid, 256, 0, s>>>(op, src, d_count, count, rows, cols,
+                                                              g, v);
             break;
         case 16:
             k_update_rows<Op, Src, 16, kIters><<<grid, 256, 0, s>>>(op, src, d_count, count, rows,
@@ -493,43 +590,89 @@ static int launch_update(const Op& op, bool state_aligned, const spopt_grad* gr,
     return SPOPT_OK;
 }
 
-template <int MODE, bool LSROW>
-static int launch_adam_mode(float* p, float* m, float* v, int32_t* ls, const AdamScalars& a,
-                            int wd_kind, bool al, const spopt_grad* gr, int64_t rows, int64_t cols,
-                            hipStream_t s) {
-    if (wd_kind == kWdL2)
-        return launch_update(AdamOp<MODE, kWdL2, LSROW>{p, m, v, ls, a}, al, gr, rows, cols, s);
-    if (wd_kind == kWdDecoupled)
-        return launch_update(AdamOp<MODE, kWdDecoupled, LSROW>{p, m, v, ls, a}, al, gr, rows,
-                             cols, s);
-    return launch_update(AdamOp<MODE, kWdNone, LSROW>{p, m, v, ls, a}, al, gr, rows, cols, s);
+template <class Op>
+static int launch_fused(const Op& op, bool state_aligned, const FusedCsr& f, hipStream_t s) {
+    constexpr int kIters = RowBatch<Op>::kIters;
+    const int lpr = lanes_per_row(f.cols);
+    const int v = state_aligned && aligned16(f.vals) ? 1 : 0;
+    const int64_t nupd =
+        f.n > 0 ? grid_cap(ceil_div(f.n, update_rows_per_block<Op>(lpr)), kUpdateBlocks) : 0;
+    const unsigned grid = (unsigned)(f.nfix + nupd + f.nblk_ci + f.nblk_ro);
+    switch (lpr) {
+        case 4:
+            k_step_lookups<Op, 4, 1><<<grid, 256, 0, s>>>(op, f, nupd, v);
+            break;
+        case 16:
+            k_step_lookups<Op, 16, kIters><<<grid, 256, 0, s>>>(op, f, nupd, v);
+            break;
+        case 32:
+            k_step_lookups<Op, 32, kIters><<<grid, 256, 0, s>>>(op, f, nupd, v);
+            break;
+        default:
+            k_step_lookups<Op, 64, kIters><<<grid, 256, 0, s>>>(op, f, nupd, v);
+            break;
+    }
+    SPOPT_LAUNCHED();
+    return SPOPT_OK;
+}
+
+// Calls go(op, aligned) with the Adam op of the mode, weight decay and
+// last_step layout asked for.
+template <int MODE, bool LSROW, class Go>
+static int with_adam_mode(float* p, float* m, float* v, int32_t* ls, const AdamScalars& a,
+                          int wd_kind, bool al, Go&& go) {
+    if (wd_kind == kWdL2) return go(AdamOp<MODE, kWdL2, LSROW>{p, m, v, ls, a}, al);
+    if (wd_kind == kWdDecoupled) return go(AdamOp<MODE, kWdDecoupled, LSROW>{p, m, v, ls, a}, al);
+    return go(AdamOp<MODE, kWdNone, LSROW>{p, m, v, ls, a}, al);
+}
+
+template <class Go>
+static int with_adam_op(float* p, float* m, float* v, int32_t* ls, bool ls_per_row,
+                        const AdamScalars& a, int mode, int wd_kind, Go&& go) {
+    // With one last_step per row, only p, m and v are moved 16 bytes at a time.
+    const bool al = aligned16(p) && aligned16(m) && aligned16(v) && (ls_per_row || aligned16(ls));
+    if (ls_per_row) {
+        if (mode == SPOPT_MODE_DORMANCY)
+            return with_adam_mode<SPOPT_MODE_DORMANCY, true>(p, m, v, ls, a, wd_kind, al, go);
+        return with_adam_mode<SPOPT_MODE_LAZY, true>(p, m, v, ls, a, wd_kind, al, go);
+    }
+    if (mode == SPOPT_MODE_DORMANCY)
+        return with_adam_mode<SPOPT_MODE_DORMANCY, false>(p, m, v, ls, a, wd_kind, al, go);
+    return with_adam_mode<SPOPT_MODE_LAZY, false>(p, m, v, ls, a, wd_kind, al, go);
+}
+
+template <class Go>
+static int with_sgd_op(float* p, float* b, double lr, double mu, double wd, Go&& go) {
+    if (mu != 0.0 && b != nullptr) return go(SgdOp<true>{p, b, lr, mu, wd}, aligned16(p) && aligned16(b));
+    return go(SgdOp<false>{p, nullptr, lr, 0.0, wd}, aligned16(p));
 }
 
 int launch_adam(float* p, float* m, float* v, int32_t* ls, bool ls_per_row, const AdamScalars& a,
                 int mode, int wd_kind, const spopt_grad* gr, int64_t rows, int64_t cols,
                 hipStream_t s) {
-    // With one last_step per row, only p, m and v are moved 16 bytes at a time.
-    const bool al = aligned16(p) && aligned16(m) && aligned16(v) && (ls_per_row || aligned16(ls));
-    if (ls_per_row) {
-        if (mode == SPOPT_MODE_DORMANCY)
-            return launch_adam_mode<SPOPT_MODE_DORMANCY, true>(p, m, v, ls, a, wd_kind, al, gr,
-                                                               rows, cols, s);
-        return launch_adam_mode<SPOPT_MODE_LAZY, true>(p, m, v, ls, a, wd_kind, al, gr, rows, cols,
-                                                       s);
-    }
-    if (mode == SPOPT_MODE_DORMANCY)
-        return launch_adam_mode<SPOPT_MODE_DORMANCY, false>(p, m, v, ls, a, wd_kind, al, gr, rows,
-                                                            cols, s);
-    return launch_adam_mode<SPOPT_MODE_LAZY, false>(p, m, v, ls, a, wd_kind, al, gr, rows, cols, s);
+    return with_adam_op(p, m, v, ls, ls_per_row, a, mode, wd_kind, [&](const auto& op, bool al) {
+        return launch_update(op, al, gr, rows, cols, s);
+    });
+}
+
+int launch_adam_fused(float* p, float* m, float* v, int32_t* ls, bool ls_per_row,
+                      const AdamScalars& a, int mode, int wd_kind, const FusedCsr& f,
+                      hipStream_t s) {
+    return with_adam_op(p, m, v, ls, ls_per_row, a, mode, wd_kind,
+                        [&](const auto& op, bool al) { return launch_fused(op, al, f, s); });
 }
 
 int launch_sgd(float* p, float* b, double lr, double mu, double wd, const spopt_grad* gr,
                int64_t rows, int64_t cols, hipStream_t s) {
-    if (mu != 0.0 && b != nullptr) {
-        const bool al = aligned16(p) && aligned16(b);
-        return launch_update(SgdOp<true>{p, b, lr, mu, wd}, al, gr, rows, cols, s);
-    }
-    return launch_update(SgdOp<false>{p, nullptr, lr, 0.0, wd}, aligned16(p), gr, rows, cols, s);
+    return with_sgd_op(p, b, lr, mu, wd, [&](const auto& op, bool al) {
+        return launch_update(op, al, gr, rows, cols, s);
+    });
+}
+
+int launch_sgd_fused(float* p, float* b, double lr, double mu, double wd, const FusedCsr& f,
+                     hipStream_t s) {
+    return with_sgd_op(p, b, lr, mu, wd,
+                       [&](const auto& op, bool al) { return launch_fused(op, al, f, s); });
 }
 
 }  // namespace spopt

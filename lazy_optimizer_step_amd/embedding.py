@@ -5,16 +5,17 @@ loop uses them (read_rows for the forward pass, then step with the lookup
 indices and the gradient rows): ``forward(ids)`` gathers the current rows with
 ``read_rows``; autograd hands the backward the per-lookup gradient rows, in
 lookup order, which is the value layout ``csr_from_lookups`` sorts and sums
-directly (no re-layout); ``step()`` canonicalises them and assembles the CSR
-gradient over every table row in that one call, then applies the optimizer to
-the touched rows only.  Every step of the path runs in the library's kernels; this module only
-keeps the buffers and the order of the calls.
+directly (no re-layout); ``step()`` canonicalises them, assembles the CSR
+gradient over every table row and applies the optimizer to the touched rows
+only, all in one call (``sparse_step_from_lookups``).  Every step of the path
+runs in the library's kernels; this module only keeps the buffers and the order
+of the calls.
 """
 from __future__ import annotations
 
 import torch
 
-from . import SparseAdam, SparseSgd, csr_from_lookups, read_rows, sparse_opt_workspace_size
+from . import SparseAdam, SparseSgd, read_rows, sparse_opt_workspace_size
 
 
 class _Lookup(torch.autograd.Function):
@@ -100,9 +101,8 @@ class SparseEmbedding(torch.nn.Module):
         self._pending.clear()
         n = ids.numel()
         b = self._buffers_for(n)
-        csr, _, _ = csr_from_lookups(ids, grads, self.num_rows, out_keys=b["keys"],
-                                     out_vals=b["sums"], out_counts=b["counts"],
-                                     d_nunique=b["U"], row_offsets=b["row_offsets"],
-                                     want_col_indices=False, workspace=b["ws"], stream=stream)
-        self.opt.step(csr, stream=stream)
+        self.opt.step_lookups(ids, grads, out_keys=b["keys"], out_vals=b["sums"],
+                              out_counts=b["counts"], d_nunique=b["U"],
+                              row_offsets=b["row_offsets"], want_col_indices=False,
+                              workspace=b["ws"], stream=stream)
         return n

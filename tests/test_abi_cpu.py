@@ -115,6 +115,18 @@ def test_csr_from_lookups_host_errors():
     assert f(*args(ws=16)) == _lib.EWORKSPACE
 
 
+def test_step_from_lookups_host_errors():
+    """The step from raw lookups checks its handle before any device work; the
+    timing hook takes two events or none."""
+    f = _lib.lib().sparse_step_from_lookups
+    assert f(None, FAKE, FAKE, 10, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 20, None,
+             0) == _lib.EINVAL
+    ev = _lib.lib().sparse_opt_set_step_events
+    assert ev(FAKE, None) == _lib.EINVAL
+    assert ev(None, FAKE) == _lib.EINVAL
+    assert ev(None, None) == _lib.OK
+
+
 def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True)

@@ -1,7 +1,8 @@
-"""The benchmark's one JSON line, from short runs of the default command and
-of its two-call and per-row variants: every field of the output contract is
-there, and the roofline and CPU-baseline figures are consistent with each
-other.  (The bench times the GPU, so these are GPU tests.)"""
+"""The benchmark's one JSON line, from short runs of the default command (the
+one-call step) and of its two-call, three-call and per-row variants: every
+field of the output contract is there, and the roofline and CPU-baseline
+figures are consistent with each other.  (The bench times the GPU, so these are
+GPU tests.)"""
 import json
 import os
 import subprocess
@@ -17,8 +18,9 @@ FIELDS = ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
           "cpu_baseline", "breakdown_us")
 
 
-@pytest.mark.parametrize("extra", [[], ["--separate-calls"], ["--last-step-per-row"]],
-                         ids=["fused", "separate_calls", "row_last_step"])
+@pytest.mark.parametrize("extra", [[], ["--two-calls"], ["--separate-calls"],
+                                   ["--last-step-per-row"]],
+                         ids=["one_call", "two_calls", "separate_calls", "row_last_step"])
 def test_bench_json_line(extra):
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "3",
                         "--warmup", "1", "--cpu-seconds", "0.5", *extra],
@@ -38,6 +40,15 @@ def test_bench_json_line(extra):
     assert rf["traffic"] is None or rf["traffic"] > rf["algorithmic_bytes_per_launch"]
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["cores"] == 1 and cb["value"] > 0
-    calls = ["coo_from_lookups", "csr_from_coo"] if extra == ["--separate-calls"] \
-        else ["csr_from_lookups"]
-    assert list(d["breakdown_us"]) == calls + ["sparse_adam_step", "step"]
+    if extra == ["--separate-calls"]:
+        calls = ["coo_from_lookups", "csr_from_coo", "sparse_adam_step"]
+    elif extra == ["--two-calls"]:
+        calls = ["csr_from_lookups", "sparse_adam_step"]
+    else:
+        calls = ["sparse_step_from_lookups"]
+    assert d["config"]["calls"] == " + ".join(calls)
+    extra_keys = ["before_update_launch"] if len(calls) == 1 else []
+    assert list(d["breakdown_us"]) == calls + ["update_launch"] + extra_keys + ["step"]
+    # the update launch lies inside the step
+    assert d["breakdown_us"]["update_launch"]["p50"] < d["breakdown_us"]["step"]["p50"]
+    assert ("k_step_lookups" in rf["kernel"]) == (len(calls) == 1)

@@ -42,11 +42,13 @@ def _free_gpu():
 
 
 class LookupPath:
-    """The benchmark's per-step calls with preallocated outputs: the fused
-    csr_from_lookups, or (fused=False) coo_from_lookups then csr_from_coo."""
+    """The benchmark's per-step calls with preallocated outputs: the one call
+    sparse_step_from_lookups (mode "one_call", the benchmark's default),
+    csr_from_lookups then the step ("two_calls"), or coo_from_lookups,
+    csr_from_coo, then the step ("separate")."""
 
-    def __init__(self, opt, rows, cols, n, fused=True):
-        self.opt, self.rows, self.cols, self.n, self.fused = opt, rows, cols, n, fused
+    def __init__(self, opt, rows, cols, n, mode="one_call"):
+        self.opt, self.rows, self.cols, self.n, self.mode = opt, rows, cols, n, mode
         self.keys = torch.empty(n, dtype=torch.int64, device="cuda")
         self.sums = torch.empty((n, cols), dtype=torch.float32, device="cuda")
         self.counts = torch.empty(n, dtype=torch.int32, device="cuda")
@@ -57,11 +59,14 @@ class LookupPath:
         self.col_indices = torch.empty(n * cols, dtype=torch.int32, device="cuda")
 
     def step(self, ids, grads):
-        if self.fused:
-            csr, _, _ = L.csr_from_lookups(dev(ids), dev(grads), self.rows, out_keys=self.keys,
-                                           out_vals=self.sums, out_counts=self.counts,
-                                           d_nunique=self.U, row_offsets=self.row_offsets,
-                                           col_indices=self.col_indices, workspace=self.ws)
+        out = dict(out_keys=self.keys, out_vals=self.sums, out_counts=self.counts,
+                   d_nunique=self.U, row_offsets=self.row_offsets,
+                   col_indices=self.col_indices, workspace=self.ws)
+        if self.mode == "one_call":
+            self.opt.step_lookups(dev(ids), dev(grads), **out)
+            return
+        if self.mode == "two_calls":
+            csr, _, _ = L.csr_from_lookups(dev(ids), dev(grads), self.rows, **out)
         else:
             L.coo_from_lookups(dev(ids), dev(grads), self.rows, out_keys=self.keys,
                                out_vals=self.sums, out_counts=self.counts, d_nunique=self.U,
@@ -81,7 +86,7 @@ def test_table_1M_x_64_lazy_full_compare():
                       mode="lazy")
     gpu = L.SparseAdam(dev(p0), lr=h["lr"], beta1=h["beta1"], beta2=h["beta2"], eps=h["eps"],
                        mode="lazy")
-    path = LookupPath(gpu, w.rows, w.cols, w.n_lookups, fused=False)
+    path = LookupPath(gpu, w.rows, w.cols, w.n_lookups, mode="separate")
     for s, (ids, grads) in enumerate(synth.lookups_many(w, range(w.steps))):
         keys, sums, counts = oracle.coo_from_lookups(ids, grads, w.rows)
         ro, ci, cv = oracle.csr_from_coo(keys, sums, w.rows, w.cols, w.rows, w.cols)
@@ -148,7 +153,7 @@ def test_table_2M_x_256_partial_rows_full_compare(opt):
         assert_state_close(host(gpu.v), ora.v, "2Mx256 adam v")
 
 
-def _sampled_lookup_run(cfg):
+def _sampled_lookup_run(cfg, mode="one_call"):
     w = synth.WORKLOADS[cfg]
     h = w.hyper
     R, C = w.rows, w.cols
@@ -157,7 +162,7 @@ def _sampled_lookup_run(cfg):
     log(f"cfg{cfg}: initial table in {time.time() - t0:.1f} s")
     gpu = L.SparseAdam(torch.from_numpy(p0).to("cuda"), lr=h["lr"], beta1=h["beta1"],
                        beta2=h["beta2"], eps=h["eps"], mode=w.mode)
-    path = LookupPath(gpu, R, C, w.n_lookups)
+    path = LookupPath(gpu, R, C, w.n_lookups, mode)
     t0 = time.time()
     batches = synth.lookups_many(w, range(w.steps))
     log(f"cfg{cfg}: {w.steps} steps of lookups in {time.time() - t0:.1f} s")
@@ -175,7 +180,9 @@ def _sampled_lookup_run(cfg):
         if s in check_ro:
             ro, _, _ = oracle.csr_from_coo(ok, np.zeros((ok.size, C), np.float32), R, C, R, C)
             assert np.array_equal(host(path.row_offsets), ro), f"step {s}: row_offsets"
-    log(f"cfg{cfg}: GPU path done, keys/counts/row_offsets bit-exact")
+            assert np.array_equal(host(path.col_indices)[:u * C],
+                                  np.tile(np.arange(C, dtype=np.int32), u)), f"step {s}: cols"
+    log(f"cfg{cfg}: GPU path done, keys/counts/row_offsets/col_indices bit-exact")
 
     rng = np.random.default_rng(cfg)
     touched_rows = np.nonzero(touch_count)[0]
@@ -205,8 +212,9 @@ def _sampled_lookup_run(cfg):
     log(f"cfg{cfg}: {sample.size} sampled rows within tolerance, untouched rows intact")
 
 
-def test_table_10M_x_128_dormancy_sampled():
-    _sampled_lookup_run(3)
+@pytest.mark.parametrize("mode", ["one_call", "two_calls"])
+def test_table_10M_x_128_dormancy_sampled(mode):
+    _sampled_lookup_run(3, mode)
 
 
 def test_table_50M_x_128_dormancy_sampled():
