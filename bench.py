@@ -72,8 +72,8 @@ UPDATE_SOURCES = ("lazy_optimizer_step_amd/csrc/update.hip",
                   "lazy_optimizer_step_amd/csrc/common.hpp",
                   "lazy_optimizer_step_amd/csrc/csr_full.hpp",
                   "lazy_optimizer_step_amd/csrc/seg_combine.hpp")
-UPDATE_TRAFFIC = {"sources_sha256": "9603ce4e10ac53fe5af479b1ef102a3a82dffe85afc6b2537fc330d65e22886b",
-                  "fetch_bytes": 2.0 * 33795.3 * 1024, "write_bytes": 1.0 * 59017.9 * 1024}
+UPDATE_TRAFFIC = {"sources_sha256": "f98720680465b97482ad72e93f406e7c5ebe69416b164b86cf10cae23d46678d",
+                  "fetch_bytes": 2.0 * 33444.7 * 1024, "write_bytes": 1.0 * 104288.0 * 1024}
 
 
 def sources_sha256() -> str:
