@@ -404,9 +404,9 @@ extern "C" int sparse_step_from_lookups(spopt_t h, const int64_t* ids, const flo
     if (t >= INT32_MAX) return fail(SPOPT_EINVAL, "sparse_step_from_lookups: t would reach 2^31");
     FusedCsr f;
     bool deferred = false;
-    int rc = csr_lookups_run(ids, vals, n, h->rows, h->cols, out_keys, out_vals, out_counts,
-                             d_nunique, row_offsets, col_indices, workspace, workspace_bytes, s,
-                             flags, &f, &deferred);
+    int rc = csr_lookups_run("sparse_step_from_lookups", ids, vals, n, h->rows, h->cols, out_keys,
+                             out_vals, out_counts, d_nunique, row_offsets, col_indices, workspace,
+                             workspace_bytes, s, flags, &f, &deferred);
     if (rc) return rc;
     if (!deferred) {
         // Validated, or a layout the fused launch does not take: the step

@@ -21,6 +21,8 @@
 // csr_from_lookups runs 1 and 2 (the segment kernel also recording how many
 // ids lie below each 8192-row block), then one launch that does 3 and builds
 // the CSR's row_offsets and col_indices (csr_full.hpp) from those counts.
+// sparse_step_from_lookups runs 1 and 2 the same way and leaves 3 and the CSR
+// blocks to the launch that updates the table (update.hip).
 #include <stdarg.h>
 #include <stdio.h>
 
@@ -1087,27 +1089,26 @@ extern "C" int coo_from_lookups(const int64_t* ids, const float* vals, int64_t n
 
 namespace spopt {
 
-int csr_lookups_run(const int64_t* ids, const float* vals, int64_t n, int64_t rows, int64_t cols,
-                    int64_t* out_keys, float* out_vals, int32_t* out_counts, int64_t* d_nunique,
-                    int32_t* row_offsets, int32_t* col_indices, void* workspace,
-                    size_t workspace_bytes, hipStream_t st, uint32_t flags, FusedCsr* defer,
-                    bool* deferred) {
+int csr_lookups_run(const char* what, const int64_t* ids, const float* vals, int64_t n,
+                    int64_t rows, int64_t cols, int64_t* out_keys, float* out_vals,
+                    int32_t* out_counts, int64_t* d_nunique, int32_t* row_offsets,
+                    int32_t* col_indices, void* workspace, size_t workspace_bytes, hipStream_t st,
+                    uint32_t flags, FusedCsr* defer, bool* deferred) {
     if (deferred) *deferred = false;
     if (row_offsets == nullptr || rows < 1 || cols < 1)
-        return fail(SPOPT_EINVAL, "csr_from_lookups: NULL row_offsets or bad size");
+        return fail(SPOPT_EINVAL, "%s: NULL row_offsets or bad size", what);
     if (n * cols >= ((int64_t)1 << 31))
-        return fail(SPOPT_EOVERFLOW, "csr_from_lookups: %lld entries do not fit int32 offsets",
+        return fail(SPOPT_EOVERFLOW, "%s: %lld entries do not fit int32 offsets", what,
                     (long long)(n * cols));
     CanonLayout L;
     if (!canon_layout(n, cols, rows, &L))
-        return fail(SPOPT_EINVAL, "csr_from_lookups: bad n=%lld cols=%lld rows=%lld",
-                    (long long)n, (long long)cols, (long long)rows);
+        return fail(SPOPT_EINVAL, "%s: bad n=%lld cols=%lld rows=%lld", what, (long long)n,
+                    (long long)cols, (long long)rows);
     const bool fused = (cols & 3) == 0 && (col_indices == nullptr || aligned16(col_indices));
     if (!fused) {
         // Columns not in 16-byte groups: the two calls one after the other.
-        int rc = canon_run("csr_from_lookups", ids, vals, n, cols, rows, out_keys, out_vals,
-                           out_counts, d_nunique, workspace, workspace_bytes, st, flags, nullptr,
-                           true);
+        int rc = canon_run(what, ids, vals, n, cols, rows, out_keys, out_vals, out_counts,
+                           d_nunique, workspace, workspace_bytes, st, flags, nullptr, true);
         if (rc) return rc;
         spopt_coo coo{rows, cols, n, d_nunique, out_keys, out_vals};
         return csr_from_coo(&coo, rows, cols, row_offsets, col_indices, out_vals, nullptr,
@@ -1115,8 +1116,8 @@ int csr_lookups_run(const int64_t* ids, const float* vals, int64_t n, int64_t ro
     }
     char* ws = (char*)workspace;
     int32_t* bnd = (n > 0 && L.bnd_entries > 0) ? (int32_t*)(ws + L.off_bnd) : nullptr;
-    int rc = canon_run("csr_from_lookups", ids, vals, n, cols, rows, out_keys, out_vals,
-                       out_counts, d_nunique, workspace, workspace_bytes, st, flags, bnd, false);
+    int rc = canon_run(what, ids, vals, n, cols, rows, out_keys, out_vals, out_counts, d_nunique,
+                       workspace, workspace_bytes, st, flags, bnd, false);
     if (rc) return rc;
     FusedCsr f;
     f.nfix = n > 0 ? L.nsum : 0;
@@ -1168,7 +1169,7 @@ extern "C" int csr_from_lookups(const int64_t* ids, const float* vals, int64_t n
                                 int32_t* out_counts, int64_t* d_nunique, int32_t* row_offsets,
                                 int32_t* col_indices, void* workspace, size_t workspace_bytes,
                                 void* stream, uint32_t flags) {
-    return csr_lookups_run(ids, vals, n, rows, cols, out_keys, out_vals, out_counts, d_nunique,
-                           row_offsets, col_indices, workspace, workspace_bytes,
-                           (hipStream_t)stream, flags, nullptr, nullptr);
+    return csr_lookups_run("csr_from_lookups", ids, vals, n, rows, cols, out_keys, out_vals,
+                           out_counts, d_nunique, row_offsets, col_indices, workspace,
+                           workspace_bytes, (hipStream_t)stream, flags, nullptr, nullptr);
 }

@@ -183,12 +183,13 @@ struct FusedCsr {
 // csr_from_lookups with `defer` != NULL: when the call can hand its last
 // launch over (trusted, cols % 4 == 0, row_offsets and col_indices 16-byte
 // aligned) it fills *defer and returns with *deferred = true; otherwise it
-// completes the CSR itself (*deferred = false).
-int csr_lookups_run(const int64_t* ids, const float* vals, int64_t n, int64_t rows, int64_t cols,
-                    int64_t* out_keys, float* out_vals, int32_t* out_counts, int64_t* d_nunique,
-                    int32_t* row_offsets, int32_t* col_indices, void* workspace,
-                    size_t workspace_bytes, hipStream_t s, uint32_t flags, FusedCsr* defer,
-                    bool* deferred);
+// completes the CSR itself (*deferred = false).  `what` names the entry
+// point in errors.
+int csr_lookups_run(const char* what, const int64_t* ids, const float* vals, int64_t n,
+                    int64_t rows, int64_t cols, int64_t* out_keys, float* out_vals,
+                    int32_t* out_counts, int64_t* d_nunique, int32_t* row_offsets,
+                    int32_t* col_indices, void* workspace, size_t workspace_bytes, hipStream_t s,
+                    uint32_t flags, FusedCsr* defer, bool* deferred);
 int launch_adam_fused(float* p, float* m, float* v, int32_t* ls, bool ls_per_row,
                       const AdamScalars& a, int mode, int wd_kind, const FusedCsr& f,
                       hipStream_t s);

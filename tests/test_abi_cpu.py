@@ -118,10 +118,28 @@ def test_csr_from_lookups_host_errors():
 def test_step_from_lookups_host_errors():
     """The step from raw lookups checks its handle before any device work; the
     timing hook takes two events or none."""
-    f = _lib.lib().sparse_step_from_lookups
+    L_ = _lib.lib()
+    f = L_.sparse_step_from_lookups
     assert f(None, FAKE, FAKE, 10, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 20, None,
              0) == _lib.EINVAL
-    ev = _lib.lib().sparse_opt_set_step_events
+    h = C.c_void_p()
+    cfg = _lib.SgdConfig(0.1, 0.0, 0.0)
+    assert L_.sparse_opt_create(C.byref(h), _lib.KIND_SGD, C.byref(cfg), 100, 4, FAKE, None, None,
+                                None) == 0
+    try:
+        args = lambda n=10, ro=FAKE, ws=1 << 20: (h, FAKE, FAKE, n, FAKE, FAKE, FAKE, FAKE, ro,
+                                                  None, FAKE, ws, None, 0)
+        assert f(*args(ro=None)) == _lib.EINVAL
+        assert b"sparse_step_from_lookups" in L_.sparse_opt_last_error()
+        assert f(*args(n=1 << 30)) == _lib.EOVERFLOW        # n * cols >= 2^31
+        assert f(*args(ws=16)) == _lib.EWORKSPACE
+        assert b"sparse_step_from_lookups" in L_.sparse_opt_last_error()
+        assert L_.sparse_opt_get_step(h) == 0               # no step taken
+        assert L_.sparse_opt_set_step(h, (1 << 31) - 2) == 0
+        assert f(*args()) == _lib.EINVAL                    # t would reach 2^31
+    finally:
+        L_.sparse_opt_destroy(h)
+    ev = L_.sparse_opt_set_step_events
     assert ev(FAKE, None) == _lib.EINVAL
     assert ev(None, FAKE) == _lib.EINVAL
     assert ev(None, None) == _lib.OK
