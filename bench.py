@@ -72,8 +72,8 @@ UPDATE_SOURCES = ("lazy_optimizer_step_amd/csrc/update.hip",
                   "lazy_optimizer_step_amd/csrc/common.hpp",
                   "lazy_optimizer_step_amd/csrc/csr_full.hpp",
                   "lazy_optimizer_step_amd/csrc/seg_combine.hpp")
-UPDATE_TRAFFIC = {"sources_sha256": "f98720680465b97482ad72e93f406e7c5ebe69416b164b86cf10cae23d46678d",
-                  "fetch_bytes": 2.0 * 33444.7 * 1024, "write_bytes": 1.0 * 104288.0 * 1024}
+UPDATE_TRAFFIC = {"sources_sha256": "6ff370ebe5388ba0b43ac1480dce399b102499299e6e4e320bb25826f00f1e2c",
+                  "fetch_bytes": 2.0 * 33443.1 * 1024, "write_bytes": 1.0 * 104286.1 * 1024}
 
 
 def sources_sha256() -> str:
