@@ -252,20 +252,31 @@ def cpu_baseline(w, host_p0, batches, budget_s: float, per_row: bool = False):
               mode=w.mode, m=m, v=v, last_step=ls)
     coords = 0
     steps = 0
+    t_canon = 0.0
     t0 = time.perf_counter()
     for ids, grads in batches:
+        tc = time.perf_counter()
         keys, sums, _ = oracle.coo_from_lookups(ids, grads, w.rows)
         ro, ci, cv = oracle.csr_from_coo(keys, sums, w.rows, w.cols, w.rows, w.cols)
+        t_canon += time.perf_counter() - tc
         opt.step_csr(ro, ci, cv)
         coords += keys.size * w.cols
         steps += 1
         if steps >= 2 and time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": coords / dt / 1e9, "unit": "G touched coords/s", "cores": 1,
             "kind": "oracle",
             "sample": f"first {steps} steps of the same workload (whole step: canonicalise, CSR, "
-                      f"update; {coords} touched coords in {dt:.2f} s, one thread)"}
+                      f"update; {coords} touched coords in {dt:.2f} s, one thread)",
+            "canonicalise_s": t_canon, "update_s": dt - t_canon,
+            "host": {"cpu": model, "nproc": os.cpu_count()}}
 
 
 def main() -> int:
@@ -456,6 +467,10 @@ def main() -> int:
     if one_call and not per_row and not args.host_state \
             and sources_sha256() == UPDATE_TRAFFIC["sources_sha256"]:
         traffic = UPDATE_TRAFFIC["fetch_bytes"] + UPDATE_TRAFFIC["write_bytes"]
+    # measured DRAM bytes / time beside algorithmic bytes / time, each regime
+    # (the counters read the same bytes per launch, within 0.1%, in both)
+    traffic_gbs = None if traffic is None else traffic / (upd.mean() * 1e-3) / 1e9
+    traffic_gbs_cold = None if traffic is None else traffic / (upd_cold.mean() * 1e-3) / 1e9
     op = ("AdamOp<DormancyDecay, no decay, "
           + ("last_step per row" if per_row else "last_step per coordinate") + ">")
     kernel = (f"k_step_lookups<{op}, 32, 2> (tile combine + update + CSR blocks)" if one_call
@@ -481,6 +496,7 @@ def main() -> int:
                    "calls": " + ".join(c for c, _ in calls)},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "traffic_GBs": traffic_gbs,
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled)",
                      "algorithmic_bytes_per_launch": float(upd_bytes.mean()),
                      "kernel": kernel,
@@ -489,6 +505,7 @@ def main() -> int:
                      "device_copy_GBs": copy_gbs,
                      "frac_of_device_copy": achieved / copy_gbs,
                      "cold": {"achieved": cold_achieved, "frac": cold_achieved / HBM_PEAK_GBS,
+                              "traffic_GBs": traffic_gbs_cold,
                               "mean_us": float(upd_cold.mean() * 1e3), "us": pcts(upd_cold)}},
         "breakdown_us": breakdown,
         "read_rows": {"us": pcts(rr), "lookups": n,

@@ -38,8 +38,13 @@ def test_bench_json_line(extra):
     assert rf["bound"] == "hbm" and rf["peak"] == 8000.0 and rf["unit"] == "GB/s"
     assert 0 < rf["frac"] < 1 and abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-9
     assert rf["traffic"] is None or rf["traffic"] > rf["algorithmic_bytes_per_launch"]
+    if rf["traffic"] is not None:   # DRAM bytes / time beside algorithmic bytes / time
+        assert abs(rf["traffic_GBs"] / rf["achieved"]
+                   - rf["traffic"] / rf["algorithmic_bytes_per_launch"]) < 1e-6
+        assert rf["cold"]["traffic_GBs"] < rf["traffic_GBs"] * 1.5
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["cores"] == 1 and cb["value"] > 0
+    assert cb["canonicalise_s"] > 0 and cb["update_s"] > 0 and cb["host"]["nproc"] >= 1
     if extra == ["--separate-calls"]:
         calls = ["coo_from_lookups", "csr_from_coo", "sparse_adam_step"]
     elif extra == ["--two-calls"]:
