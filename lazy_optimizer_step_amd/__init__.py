@@ -305,22 +305,27 @@ def csr_from_lookups(ids: torch.Tensor, vals: torch.Tensor, rows: int, *, out_ke
     return csr, out_counts, d_nunique
 
 
-def sparse_step_from_lookups(h: "_Handle", ids: torch.Tensor, vals: torch.Tensor, rows: int, *,
+def sparse_step_from_lookups(h: "_Handle", ids: torch.Tensor, vals: torch.Tensor, *,
                              out_keys=None, out_vals=None, out_counts=None, d_nunique=None,
                              row_offsets=None, col_indices=None, want_col_indices=True,
                              workspace=None, stream=None, validate: bool = False):
     """Raw lookups of full rows -> one step of the handle's optimizer in one call:
     the outputs of csr_from_lookups and the table of the step on that CSR, bit for
-    bit.  rows must be the handle's.  Returns (csr, counts, d_nunique) as
-    csr_from_lookups."""
+    bit.  vals: (n, cols) with the handle's cols.  Returns (csr, counts,
+    d_nunique) as csr_from_lookups."""
+    n = ids.numel()
+    if vals.numel() != n * h.cols or (vals.dim() == 2 and vals.shape[1] != h.cols):
+        raise ValueError(f"vals: shape {tuple(vals.shape)}, the handle's table takes "
+                         f"({n}, {h.cols})")
+    vals = vals if vals.dim() == 2 else vals.view(n, h.cols)
     (n, cols, out_keys, out_vals, out_counts, d_nunique, row_offsets, col_indices,
-     workspace) = _lookup_outputs(ids, vals, rows, out_keys, out_vals, out_counts, d_nunique,
+     workspace) = _lookup_outputs(ids, vals, h.rows, out_keys, out_vals, out_counts, d_nunique,
                                   row_offsets, col_indices, want_col_indices, workspace)
     check(h._L.sparse_step_from_lookups(h._h, _ptr(ids), _ptr(vals), n, _ptr(out_keys),
                                         _ptr(out_vals), _ptr(out_counts), _ptr(d_nunique),
                                         _ptr(row_offsets), _ptr(col_indices), _ptr(workspace),
                                         workspace.numel(), _stream(stream), _flags(validate)))
-    csr = CsrGradient(row_offsets, col_indices, out_vals, rows, cols, touched_rows=out_keys,
+    csr = CsrGradient(row_offsets, col_indices, out_vals, h.rows, cols, touched_rows=out_keys,
                       n_touched=n, d_n_touched=d_nunique)
     return csr, out_counts, d_nunique
 
@@ -350,6 +355,7 @@ def csr_to_coo(csr: CsrGradient, *, out_indices=None, out_values=None, nnz: int 
 
 class _Handle:
     def __init__(self, kind, cfg, rows, cols, p, m, v, ls):
+        self.rows, self.cols = rows, cols
         self._h = C.c_void_p()
         check(_lib.lib().sparse_opt_create(C.byref(self._h), kind, C.byref(cfg), rows, cols,
                                            _ptr(p), _ptr(m), _ptr(v), _ptr(ls)))
@@ -456,7 +462,7 @@ class SparseAdam:
     def step_lookups(self, ids: torch.Tensor, vals: torch.Tensor, **kw):
         """One step from raw lookups of full rows (ids (n,), vals (n, cols));
         keywords and result as sparse_step_from_lookups."""
-        return sparse_step_from_lookups(self.handle, ids, vals, self.rows, **kw)
+        return sparse_step_from_lookups(self.handle, ids, vals, **kw)
 
     def read_rows(self, indices: torch.Tensor, *, out=None, stream=None, validate=False):
         """The current rows of the table for a batch of lookups (forward pass)."""
@@ -504,4 +510,4 @@ class SparseSgd:
 
     def step_lookups(self, ids: torch.Tensor, vals: torch.Tensor, **kw):
         """One step from raw lookups of full rows; as SparseAdam.step_lookups."""
-        return sparse_step_from_lookups(self.handle, ids, vals, self.rows, **kw)
+        return sparse_step_from_lookups(self.handle, ids, vals, **kw)

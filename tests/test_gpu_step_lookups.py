@@ -38,8 +38,9 @@ def _state(o):
 
 def _outputs(csr, counts, U, cols):
     u = int(host(U)[0])
-    out = [u, host(csr.touched_rows)[:u].tobytes(), host(csr.values).reshape(-1)[:u * cols].tobytes(),
-           host(counts)[:u].tobytes(), host(csr.row_offsets).tobytes()]
+    out = [u, host(csr.touched_rows)[:u].tobytes(),
+           host(csr.values).reshape(-1)[:u * cols].tobytes(), host(counts)[:u].tobytes(),
+           host(csr.row_offsets).tobytes()]
     if csr.col_indices is not None:
         out.append(host(csr.col_indices)[:u * cols].tobytes())
     return out
@@ -204,3 +205,21 @@ def test_against_oracle(kind, cfg):
         assert np.array_equal(host(a.last_step), o.ls)
     else:
         assert_state_close(host(a.momentum_buf), o.b, "momentum")
+
+
+def test_binding_checks_shapes_against_the_handle():
+    """The binding sizes and checks every array from the handle's rows and cols,
+    so vals of another width are refused before the library is called."""
+    a, _, _ = _make("adam", 1000, 8, 10, dict(mode="dormancy"))
+    ids = torch.zeros(16, dtype=torch.int64, device="cuda")
+    with pytest.raises(ValueError):
+        a.step_lookups(ids, torch.zeros((16, 4), dtype=torch.float32, device="cuda"))
+    with pytest.raises(ValueError):
+        a.step_lookups(ids, torch.zeros(16 * 8 + 1, dtype=torch.float32, device="cuda"))
+    with pytest.raises(ValueError):   # row_offsets for fewer rows than the table's
+        a.step_lookups(ids, torch.zeros((16, 8), dtype=torch.float32, device="cuda"),
+                       row_offsets=torch.empty(500, dtype=torch.int32, device="cuda"))
+    assert a.t == 0
+    a.step_lookups(ids, torch.ones(16 * 8, dtype=torch.float32, device="cuda"))  # flat is fine
+    torch.cuda.synchronize()
+    assert a.t == 1 and host(a.last_step)[0].tolist() == [1] * 8
