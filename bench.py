@@ -14,9 +14,10 @@ resident in HBM before the timed region starts.
 
 Prints one JSON line:  value = touched coordinates updated per second over the
 whole timed region (G/s); roofline = the algorithmic bytes of the launch that
-updates the table / its mean duration (HIP events that the library records
-around that launch on its stream, through its timing hook, at every step of the
-timed region) against 8 TB/s, with a plain 1 GiB device copy measured
+updates the table / its mean duration (HIP events that the library attaches to
+that launch's dispatch through its timing hook, so they take the kernel's own
+start and end times on its stream, at every step of the timed region) against
+8 TB/s, with a plain 1 GiB device copy measured
 alongside as the practical bandwidth ceiling; breakdown_us = p10 / median / p90
 of each call, of that launch and of the whole step from a second, separately
 timed pass over the same inputs; cold = that launch again in a third pass that
@@ -72,8 +73,8 @@ UPDATE_SOURCES = ("lazy_optimizer_step_amd/csrc/update.hip",
                   "lazy_optimizer_step_amd/csrc/common.hpp",
                   "lazy_optimizer_step_amd/csrc/csr_full.hpp",
                   "lazy_optimizer_step_amd/csrc/seg_combine.hpp")
-UPDATE_TRAFFIC = {"sources_sha256": "6ff370ebe5388ba0b43ac1480dce399b102499299e6e4e320bb25826f00f1e2c",
-                  "fetch_bytes": 2.0 * 33443.1 * 1024, "write_bytes": 1.0 * 104286.1 * 1024}
+UPDATE_TRAFFIC = {"sources_sha256": "f5d6ca28368bc3892abf6b5eb6356dad4a20bbbf736d0fbbd023ec06bb5630cc",
+                  "fetch_bytes": 2.0 * 33446.6 * 1024, "write_bytes": 1.0 * 104288.7 * 1024}
 
 
 def sources_sha256() -> str:
@@ -378,8 +379,8 @@ def main() -> int:
     torch.cuda.synchronize()
 
     # Timed region: K whole steps.  Events bracket the region, and the library
-    # records a pair around every launch that updates the table (its timing
-    # hook).  A bounded spin kernel holds the stream while the host queues
+    # attaches a pair to the dispatch of every launch that updates the table
+    # (its timing hook).  A bounded spin kernel holds the stream while the host queues
     # every step behind it, so the steps run back to back and the events time
     # device work rather than the host's launch rate.
     ev = HipEvents(2 + 2 * K)

@@ -196,13 +196,13 @@ SPOPT_API int sparse_opt_set_step(spopt_t h, int64_t t);
 SPOPT_API const char* sparse_opt_last_error(void);
 
 /* Timing of the update launch (profiling).  With two hipEvent_t handles set
- * (created by the caller), every later sparse_adam_step, sparse_sgd_step and
- * sparse_step_from_lookups call of the calling thread records `begin` just
- * before the kernel that updates the table and `end` just after it, on the
- * call's stream (a step that validates records them after its checks).  The
- * events stay the caller's; (NULL, NULL) stops the recording.  Errors:
- * SPOPT_EINVAL when only one is NULL; a failed record makes the step return
- * SPOPT_EDEVICE. */
+ * (created by the caller, timing enabled), every later sparse_adam_step,
+ * sparse_sgd_step and sparse_step_from_lookups call of the calling thread
+ * attaches them to the dispatch of the kernel that updates the table
+ * (hipExtLaunchKernel), so `begin` takes that kernel's start time and `end`
+ * its end time, with no stream packets of their own.  The events stay the
+ * caller's; (NULL, NULL) stops it.  Errors: SPOPT_EINVAL when only one is
+ * NULL; a failed launch makes the step return SPOPT_EDEVICE as usual. */
 SPOPT_API int sparse_opt_set_step_events(void* begin, void* end);
 
 /* ---- canonicalisation --------------------------------------------------- */

@@ -297,24 +297,20 @@ static int validate_grad(const spopt_optimizer* h, const spopt_grad* g, const in
     });
 }
 
-// Events a caller asked to have recorded, on the call's stream, just before
-// and just after the launch that updates the table (per host thread).
+// Timing events a caller asked for, per host thread; the update launchers
+// attach them to the dispatch of the kernel that updates the table.
 static thread_local hipEvent_t t_ev_begin = nullptr;
 static thread_local hipEvent_t t_ev_end = nullptr;
+
+namespace spopt {
+StepEvents step_events() { return StepEvents{t_ev_begin, t_ev_end}; }
+}  // namespace spopt
 
 extern "C" int sparse_opt_set_step_events(void* begin, void* end) {
     if ((begin == nullptr) != (end == nullptr))
         return fail(SPOPT_EINVAL, "sparse_opt_set_step_events: give both events or neither");
     t_ev_begin = (hipEvent_t)begin;
     t_ev_end = (hipEvent_t)end;
-    return SPOPT_OK;
-}
-
-static int step_event(hipEvent_t e, hipStream_t s, const char* what) {
-    if (e == nullptr) return SPOPT_OK;
-    const hipError_t err = hipEventRecord(e, s);
-    if (err != hipSuccess)
-        return fail(SPOPT_EDEVICE, "%s: hipEventRecord: %s", what, hipGetErrorString(err));
     return SPOPT_OK;
 }
 
@@ -360,11 +356,9 @@ extern "C" int sparse_adam_step(spopt_t h, const spopt_grad* g, void* stream, ui
     const spopt_adam_config& c = h->adam;
     const AdamScalars a = adam_scalars(h, t);
     const int wd_kind = adam_wd_kind(c);
-    if ((rc = step_event(t_ev_begin, s, "sparse_adam_step"))) return rc;
     rc = launch_adam(h->p, h->m, h->v, h->ls, c.last_step_per_row != 0, a, c.mode, wd_kind, g,
                      h->rows, h->cols, s);
     if (rc) return rc;
-    if ((rc = step_event(t_ev_end, s, "sparse_adam_step"))) return rc;
     h->t = t;
     return SPOPT_OK;
 }
@@ -382,10 +376,8 @@ extern "C" int sparse_sgd_step(spopt_t h, const spopt_grad* g, void* stream, uin
         if (rc) return rc;
     }
     const spopt_sgd_config& c = h->sgd;
-    if ((rc = step_event(t_ev_begin, s, "sparse_sgd_step"))) return rc;
     rc = launch_sgd(h->p, h->m, c.lr, c.momentum, c.weight_decay, g, h->rows, h->cols, s);
     if (rc) return rc;
-    if ((rc = step_event(t_ev_end, s, "sparse_sgd_step"))) return rc;
     h->t = t;
     return SPOPT_OK;
 }
@@ -425,7 +417,6 @@ extern "C" int sparse_step_from_lookups(spopt_t h, const int64_t* ids, const flo
         return h->kind == SPOPT_KIND_ADAM ? sparse_adam_step(h, &g, stream, flags)
                                           : sparse_sgd_step(h, &g, stream, flags);
     }
-    if ((rc = step_event(t_ev_begin, s, "sparse_step_from_lookups"))) return rc;
     if (h->kind == SPOPT_KIND_ADAM) {
         const spopt_adam_config& c = h->adam;
         rc = launch_adam_fused(h->p, h->m, h->v, h->ls, c.last_step_per_row != 0,
@@ -435,7 +426,6 @@ extern "C" int sparse_step_from_lookups(spopt_t h, const int64_t* ids, const flo
         rc = launch_sgd_fused(h->p, h->m, c.lr, c.momentum, c.weight_decay, f, s);
     }
     if (rc) return rc;
-    if ((rc = step_event(t_ev_end, s, "sparse_step_from_lookups"))) return rc;
     h->t = t;
     return SPOPT_OK;
 }

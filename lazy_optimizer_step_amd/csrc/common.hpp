@@ -148,6 +148,14 @@ struct AdamScalars {
     const double* pow2;  // device [kPowTable]: beta2^k
     int32_t t;
 };
+// The calling thread's timing events (sparse_opt_set_step_events), both NULL
+// when none are set: attached to the dispatch of every kernel that updates a
+// table, they take its start and end times.
+struct StepEvents {
+    hipEvent_t begin, end;
+};
+StepEvents step_events();
+
 int launch_adam(float* p, float* m, float* v, int32_t* ls, bool ls_per_row, const AdamScalars& a,
                 int mode, int wd_kind, const spopt_grad* gr, int64_t rows, int64_t cols,
                 hipStream_t s);

@@ -26,6 +26,8 @@
 // a partial row uses one lane per entry.  Rows come from a touched-row list
 // (CSR) or the keys of a full-row COO; without a list the CSR kernel scans
 // row_offsets 64 rows per wave.
+#include <hip/hip_ext.h>
+
 #include "common.hpp"
 #include "csr_full.hpp"
 #include "seg_combine.hpp"
@@ -521,6 +523,19 @@ struct RowBatch<AdamOp<MODE, WD, LSROW>> {
     static constexpr int kIters = 2;  // Adam holds more state per row in registers
 };
 
+// A kernel that updates a table, on 256-thread blocks.  With the calling
+// thread's timing events set, they ride on the dispatch itself
+// (hipExtLaunchKernel), so they take the kernel's start and end times without
+// stream packets of their own.
+template <class K, class... A>
+static void launch_update_kernel(K kernel, unsigned grid, hipStream_t s, A... args) {
+    const StepEvents ev = step_events();
+    if (ev.begin != nullptr)
+        hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(256), 0, s, ev.begin, ev.end, 0u, args...);
+    else
+        kernel<<<grid, 256, 0, s>>>(args...);
+}
+
 // Touched rows one 256-thread block takes per round (4 lanes per row: one
 // row per sub-group at a time).
 template <class Op>
@@ -538,20 +553,20 @@ static int launch_rows(const Op& op, const Src& src, const int64_t* d_count, int
     const int v = vec_ok ? 1 : 0;
     switch (lpr) {
         case 4:
-            k_update_rows<Op, Src, 4, 1><<<grid, 256, 0, s>>>(op, src, d_count, count, rows, cols,
-                                                              g, v);
+            launch_update_kernel(k_update_rows<Op, Src, 4, 1>, grid, s, op, src, d_count, count,
+                                 rows, cols, g, v);
             break;
         case 16:
-            k_update_rows<Op, Src, 16, kIters><<<grid, 256, 0, s>>>(op, src, d_count, count, rows,
-                                                                    cols, g, v);
+            launch_update_kernel(k_update_rows<Op, Src, 16, kIters>, grid, s, op, src, d_count,
+                                 count, rows, cols, g, v);
             break;
         case 32:
-            k_update_rows<Op, Src, 32, kIters><<<grid, 256, 0, s>>>(op, src, d_count, count, rows,
-                                                                    cols, g, v);
+            launch_update_kernel(k_update_rows<Op, Src, 32, kIters>, grid, s, op, src, d_count,
+                                 count, rows, cols, g, v);
             break;
         default:
-            k_update_rows<Op, Src, 64, kIters><<<grid, 256, 0, s>>>(op, src, d_count, count, rows,
-                                                                    cols, g, v);
+            launch_update_kernel(k_update_rows<Op, Src, 64, kIters>, grid, s, op, src, d_count,
+                                 count, rows, cols, g, v);
             break;
     }
     SPOPT_LAUNCHED();
@@ -567,8 +582,8 @@ static int launch_update(const Op& op, bool state_aligned, const spopt_grad* gr,
         if (c.nnz == 0) return SPOPT_OK;
         if (c.width == 1) {
             const unsigned grid = grid_cap(ceil_div(c.nnz, 256));
-            k_update_coo_scalar<Op><<<grid, 256, 0, s>>>(op, c.indices, c.d_nnz, c.nnz,
-                                                         rows * cols, c.values);
+            launch_update_kernel(k_update_coo_scalar<Op>, grid, s, op, c.indices, c.d_nnz, c.nnz,
+                                 rows * cols, c.values);
             SPOPT_LAUNCHED();
             return SPOPT_OK;
         }
@@ -584,8 +599,8 @@ static int launch_update(const Op& op, bool state_aligned, const spopt_grad* gr,
                            c.d_n_touched, c.n_touched, rows, cols, c.values, vec_ok, s);
     }
     const unsigned grid = grid_cap(ceil_div(ceil_div(rows, kWave), 4));
-    k_update_csr_scan<Op><<<grid, 256, 0, s>>>(op, c.row_offsets, c.col_indices, rows, cols,
-                                               c.values);
+    launch_update_kernel(k_update_csr_scan<Op>, grid, s, op, c.row_offsets, c.col_indices, rows,
+                         cols, c.values);
     SPOPT_LAUNCHED();
     return SPOPT_OK;
 }
@@ -600,16 +615,16 @@ static int launch_fused(const Op& op, bool state_aligned, const FusedCsr& f, hip
     const unsigned grid = (unsigned)(f.nfix + nupd + f.nblk_ci + f.nblk_ro);
     switch (lpr) {
         case 4:
-            k_step_lookups<Op, 4, 1><<<grid, 256, 0, s>>>(op, f, nupd, v);
+            launch_update_kernel(k_step_lookups<Op, 4, 1>, grid, s, op, f, nupd, v);
             break;
         case 16:
-            k_step_lookups<Op, 16, kIters><<<grid, 256, 0, s>>>(op, f, nupd, v);
+            launch_update_kernel(k_step_lookups<Op, 16, kIters>, grid, s, op, f, nupd, v);
             break;
         case 32:
-            k_step_lookups<Op, 32, kIters><<<grid, 256, 0, s>>>(op, f, nupd, v);
+            launch_update_kernel(k_step_lookups<Op, 32, kIters>, grid, s, op, f, nupd, v);
             break;
         default:
-            k_step_lookups<Op, 64, kIters><<<grid, 256, 0, s>>>(op, f, nupd, v);
+            launch_update_kernel(k_step_lookups<Op, 64, kIters>, grid, s, op, f, nupd, v);
             break;
     }
     SPOPT_LAUNCHED();
