@@ -60,6 +60,8 @@ BYTES_PER_ROW_ROW_LS = 24
 # they read (4 B per block).  Not counted: the combine's reads of the double
 # partial sums of tile-crossing segments (at most two 8*cols B rows per
 # 256-lookup tile, about 0.5% of the launch's bytes here).
+# --scrambled: a prime multiplier, coprime to the 10M rows.
+SCRAMBLE = 999983
 CSR_BYTES_PER_COORD = 4
 CSR_BYTES_PER_ROW = 8
 CSR_BYTES_PER_TABLE_ROW = 4
@@ -107,6 +109,9 @@ def parse():
                     help="step with coo_from_lookups + csr_from_coo + sparse_adam_step")
     ap.add_argument("--last-step-per-row", action="store_true",
                     help="keep one last_step per table row instead of one per coordinate")
+    ap.add_argument("--scrambled", action="store_true",
+                    help="the same Zipf frequencies with the hot rows spread over the table "
+                         "(rank k -> row (k-1)*999983 mod rows) instead of at the lowest ids")
     ap.add_argument("--host-state", action="store_true",
                     help="keep the table and its state in mapped pinned host memory")
     return ap.parse_args()
@@ -300,6 +305,8 @@ def main() -> int:
 
     torch.cuda.set_device(0)
     w = synth.WORKLOADS[3]
+    if args.scrambled:
+        w = w.scaled(name=w.name + "_scrambled", scramble=SCRAMBLE)
     R, Cc, n = w.rows, w.cols, w.n_lookups
     K, W = args.steps, args.warmup
     h = w.hyper

@@ -15,7 +15,8 @@ Every stream is keyed by ``SeedSequence([SEED, cfg, stream, index])``:
 
 "N(0, x)" in a workload description means a normal with standard deviation x.
 Bounded Zipf(s) over R rows gives rank k in 1..R probability k^-s / H(R, s) and
-maps it to row id k-1, so row 0 is the hottest row.
+maps it to row id k-1, so row 0 is the hottest row; a workload with scramble = A
+(coprime to R) maps rank k to row (k-1)*A mod R instead.
 """
 from __future__ import annotations
 
@@ -68,6 +69,7 @@ class Workload:
     grad_std: float = 0.01
     n_lookups: int = 0        # "lookups": lookups per step
     zipf_s: float = 0.0       # "lookups": Zipf exponent
+    scramble: int = 0         # "lookups": 0, or A coprime to rows: rank k -> row (k-1)*A mod rows
     n_indices: int = 0        # "coo1d": unique indices per step
     n_rows_touched: int = 0   # "csr": rows per step
     col_min: int = 0          # "csr": columns per touched row, inclusive range
@@ -176,6 +178,9 @@ def lookups(w: Workload, step: int, n: int | None = None):
     """Raw lookups of one step: (ids int64[n], grads float32[n, cols])."""
     n = w.n_lookups if n is None else n
     ids = zipf_rows(rng(w.cfg, STREAM_IDS, step), w.rows, w.zipf_s, n)
+    if w.scramble:
+        # the same frequencies, the hot rows spread over the table
+        ids = (ids * np.int64(w.scramble)) % np.int64(w.rows)
     grads = np.empty((n, w.cols), dtype=np.float32)
     rng(w.cfg, STREAM_VALS, step).standard_normal(out=grads.reshape(-1), dtype=np.float32)
     if w.grad_std != 1.0:

@@ -223,3 +223,34 @@ def test_binding_checks_shapes_against_the_handle():
     a.step_lookups(ids, torch.ones(16 * 8, dtype=torch.float32, device="cuda"))  # flat is fine
     torch.cuda.synchronize()
     assert a.t == 1 and host(a.last_step)[0].tolist() == [1] * 8
+
+
+def test_scrambled_zipf_lookups_match_two_calls_and_oracle():
+    """Zipf lookups with the hot rows spread over the table (the scrambled
+    placement), three steps: bit for bit against the two calls, and the touched
+    rows within tolerance of the oracle."""
+    import synth
+    w = synth.WORKLOADS[3].scaled(rows=2_000_000, n_lookups=30000, scramble=999983)
+    h = w.hyper
+    a, b, p0 = _make("adam", w.rows, w.cols, 11, dict(mode="dormancy"))
+    touched = []
+    for s in range(3):
+        ids, grads = synth.lookups(w, s)
+        touched.append(ids)
+        got = a.step_lookups(dev(ids), dev(grads))
+        csr, counts, U = L.csr_from_lookups(dev(ids), dev(grads), w.rows)
+        b.step(csr)
+        torch.cuda.synchronize()
+        assert _outputs(*got, w.cols) == _outputs(csr, counts, U, w.cols), f"outputs, step {s + 1}"
+        assert _state(a) == _state(b), f"table, step {s + 1}"
+    rows = np.unique(np.concatenate(touched))
+    o = oracle.Adam(p0[rows].copy(), lr=h["lr"], beta1=h["beta1"], beta2=h["beta2"],
+                    eps=h["eps"], mode="dormancy")
+    for s in range(3):
+        ids, grads = synth.lookups(w, s)
+        ok, ov, _ = oracle.coo_from_lookups(ids, grads, w.rows)
+        o.step_coo(np.searchsorted(rows, ok), ov, width=w.cols)
+    idx = torch.from_numpy(rows).cuda()
+    assert_state_close(host(a.params.index_select(0, idx)), o.p, "params")
+    assert_state_close(host(a.m.index_select(0, idx)), o.m, "m")
+    assert np.array_equal(host(a.last_step.index_select(0, idx)), o.ls)
