@@ -39,8 +39,11 @@ def test_bench_json_line(extra):
     assert 0 < rf["frac"] < 1 and abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-9
     assert rf["traffic"] is None or rf["traffic"] > rf["algorithmic_bytes_per_launch"]
     if rf["traffic"] is not None:   # DRAM bytes / time beside algorithmic bytes / time
+        # traffic over the mean launch time (achieved is a mean of per-step rates)
+        expect = rf["traffic"] / (rf["mean_us"] * 1e-6) / 1e9
+        assert abs(rf["traffic_GBs"] - expect) < 1e-6 * expect
         assert abs(rf["traffic_GBs"] / rf["achieved"]
-                   - rf["traffic"] / rf["algorithmic_bytes_per_launch"]) < 1e-6
+                   / (rf["traffic"] / rf["algorithmic_bytes_per_launch"]) - 1) < 0.05
         assert rf["cold"]["traffic_GBs"] < rf["traffic_GBs"] * 1.5
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["cores"] == 1 and cb["value"] > 0
