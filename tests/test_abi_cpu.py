@@ -149,3 +149,45 @@ def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_header_is_plain_c_and_callable_from_c(tmp_path):
+    """include/sparse_opt.h compiles as C99 and C++11 with warnings as errors, and
+    a C program linked against the library gets the workspace size and the
+    argument errors that need no device."""
+    import shutil
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    inc = os.path.join(ROOT, "include")
+    hdr = os.path.join(inc, "sparse_opt.h")
+    for cmd in ([gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-fsyntax-only",
+                 "-x", "c", hdr],
+                ["g++", "-std=c++11", "-Wall", "-Werror", "-fsyntax-only", "-x", "c++", hdr]):
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
+    src = tmp_path / "use.c"
+    src.write_text(r'''
+#include <stdio.h>
+#include "sparse_opt.h"
+int main(void) {
+    size_t a = 0, b = 0;
+    if (sparse_opt_workspace_size(65536, 128, 10000000, &a) != SPOPT_OK) return 1;
+    if (sparse_opt_workspace_size(1024, 128, 10000000, &b) != SPOPT_OK) return 2;
+    if (!(a > b && b > 0)) return 3;
+    if (sparse_opt_workspace_size(-1, 128, 10, &a) != SPOPT_EINVAL) return 4;
+    if (csr_from_lookups(0, 0, 10, 0, 4, 0, 0, 0, 0, 0, 0, 0, 0, 0, SPOPT_TRUSTED) != SPOPT_EINVAL)
+        return 5;
+    printf("%s\n", sparse_opt_last_error());
+    return 0;
+}
+''')
+    libdir = os.path.dirname(_lib.LIB_PATH)
+    exe = tmp_path / "use"
+    r = subprocess.run([gcc, "-std=c99", "-Wall", "-Werror", str(src), "-I", inc, "-L", libdir,
+                        "-lsparseopt", f"-Wl,-rpath,{libdir}", "-Wl,-rpath,/opt/rocm/lib",
+                        "-o", str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, (r.returncode, r.stdout, r.stderr)
+    assert "csr_from_lookups" in r.stdout
