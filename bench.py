@@ -498,14 +498,17 @@ def main() -> int:
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "rows": R, "cols": Cc, "lookups_per_step": n,
-                   "zipf_s": w.zipf_s, "mode": w.mode, "state": "p,m,v float32 + last_step int32 per " + ("row" if per_row else "coordinate")
-                   + (", in mapped pinned host memory" if args.host_state else ", in HBM"),
+                   "zipf_s": w.zipf_s, "mode": w.mode,
+                   "state": "p,m,v float32 + last_step int32 per "
+                            + ("row" if per_row else "coordinate")
+                            + (", in mapped pinned host memory" if args.host_state else ", in HBM"),
                    "mean_unique_rows": float(U.mean()),
                    "calls": " + ".join(c for c, _ in calls)},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "traffic_GBs": traffic_gbs,
-                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled)",
+                     "traffic_unit":
+                         "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled)",
                      "algorithmic_bytes_per_launch": float(upd_bytes.mean()),
                      "kernel": kernel,
                      "mean_us": float(upd.mean() * 1e3), "us": pcts(upd),
