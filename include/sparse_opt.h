@@ -345,7 +345,9 @@ SPOPT_API int sparse_sgd_step(spopt_t h, const spopt_grad* g, void* stream, uint
  *   Arguments: as csr_from_lookups, with rows and cols the handle's.
  * Errors: those of csr_from_lookups and of the step call; SPOPT_EINVAL for a
  * NULL handle.  A step the validation rejects leaves the table and t as they
- * were; the canonical outputs are written all the same. */
+ * were; the canonical outputs are written all the same.  In trusted mode an
+ * out-of-range id gives U = 0, as csr_from_lookups: no row is updated and t
+ * still advances. */
 SPOPT_API int sparse_step_from_lookups(spopt_t h, const int64_t* ids, const float* vals, int64_t n,
                                        int64_t* out_keys, float* out_vals, int32_t* out_counts,
                                        int64_t* d_nunique, int32_t* row_offsets,
