@@ -254,3 +254,27 @@ def test_scrambled_zipf_lookups_match_two_calls_and_oracle():
     assert_state_close(host(a.params.index_select(0, idx)), o.p, "params")
     assert_state_close(host(a.m.index_select(0, idx)), o.m, "m")
     assert np.array_equal(host(a.last_step.index_select(0, idx)), o.ls)
+
+
+def test_random_configurations_match_two_calls():
+    """A seeded sweep over widths (every lanes-per-row shape, rows wider than one
+    vector per lane, widths not in groups of 4), table sizes, lookup counts, id
+    patterns and optimizer forms: two steps each, bit for bit against the two
+    calls."""
+    rng = np.random.default_rng(2026)
+    widths = [1, 3, 4, 8, 12, 16, 20, 32, 64, 100, 128, 256, 300, 302, 512]
+    cfgs = ADAM_CFGS + [dict(lr=0.05), dict(lr=0.05, momentum=0.9, weight_decay=0.01)]
+    for case in range(24):
+        cols = int(widths[case % len(widths)])
+        rows = int(rng.integers(1, 200_000))
+        n = int(rng.integers(0, 20_000))
+        pattern = ["uniform", "hot", "last_rows", "first_rows"][int(rng.integers(0, 4))]
+        if pattern in ("last_rows", "first_rows") and rows < 50:
+            pattern = "uniform"
+        cfg = cfgs[int(rng.integers(0, len(cfgs)))]
+        kind = "sgd" if "momentum" in cfg or "mode" not in cfg else "adam"
+        try:
+            _run_pair(kind, cfg, rows, cols, n, pattern, steps=2, seed=case)
+        except AssertionError as e:
+            raise AssertionError(f"case {case}: rows {rows} cols {cols} n {n} {pattern} "
+                                 f"{kind} {cfg}: {e}") from None
