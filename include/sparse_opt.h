@@ -39,6 +39,11 @@
  *     coo_from_lookups cannot see device-side errors, so it marks its result
  *     empty instead (see there); and sparse_step_from_lookups writes its
  *     canonical outputs before the step's own checks (see there).
+ *   - Trusted calls allocate nothing and never synchronise, so they can be
+ *     captured into a HIP graph; but a step's scalars (t, 1 - beta^t, ...) are
+ *     kernel arguments formed on the host at the call, so a captured step
+ *     replays the t it was captured with (and the handle's t advances only at
+ *     the capture): capture the canonicalisation alone, or one graph per step.
  *   - Layouts are row-major and contiguous; float arrays whose width is a
  *     multiple of 4 take 16-byte vector loads when their base is 16-byte
  *     aligned (torch allocations are), and a scalar path otherwise.
