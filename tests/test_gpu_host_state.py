@@ -5,7 +5,7 @@ touched rows cross the host link.
 Page: DiskSparseAdam README, "Key Features" (w, m, v and step counters out of
 core; only the rows a batch touches are loaded and written back).  Checked
 against the oracle and bit for bit against the same steps on device-resident
-state.
+state, and through the one-call step from raw lookups.
 """
 import ctypes as C
 
@@ -28,6 +28,7 @@ def test_host_resident_adam_whole_path(per_row):
     p0 = synth.init_params(w)
     kw = dict(lr=1e-2, mode="dormancy", last_step_per_row=per_row)
     hst = L.SparseAdam.host_resident(p0, **kw)
+    one = L.SparseAdam.host_resident(p0, **kw)      # stepped through the one call
     devr = L.SparseAdam(dev(p0), **kw)
     ora = (oracle.AdamRows if per_row else oracle.Adam)(p0.copy(), lr=1e-2, mode="dormancy")
     for s in range(w.steps):
@@ -40,6 +41,7 @@ def test_host_resident_adam_whole_path(per_row):
         csr = L.csr_from_coo(coo, w.rows, w.cols, copy_values=False)
         hst.step(csr)
         devr.step(csr)
+        one.step_lookups(dev(ids), dev(grads))
     torch.cuda.synchronize()
     hp, hm, hv, hl = (a.numpy() for a in (hst.params, hst.m, hst.v, hst.last_step))
     assert np.array_equal(hl, ora.ls)
@@ -48,6 +50,8 @@ def test_host_resident_adam_whole_path(per_row):
     assert_state_close(hv, ora.v, "host v")
     for a, b in ((hp, devr.params), (hm, devr.m), (hv, devr.v), (hl, devr.last_step)):
         assert a.tobytes() == host(b).tobytes()
+    for a, b in ((hp, one.params), (hm, one.m), (hv, one.v), (hl, one.last_step)):
+        assert a.tobytes() == b.numpy().tobytes()
     untouched = ora.ls.reshape(w.rows, -1)[:, 0] == 0
     assert hp[untouched].tobytes() == p0[untouched].tobytes()
     # forward gather straight from the host-resident table
