@@ -97,6 +97,8 @@ def test_sgd_matches_two_calls(cfg, pattern):
     (24577, 8, 9000, "hot", 3),         # row_offsets not 16-byte aligned: the two calls inside
     (2_000_000, 4, 500, "last_rows", 0),
     (5, 8, 7000, "uniform", 0),         # a handful of rows, long segments
+    (1, 8, 5000, "uniform", 0),         # one row: 0 key bits, no radix pass, one segment
+    (2, 16, 3000, "uniform", 0),        # two rows: one 1-bit pass
 ])
 def test_shapes_match_two_calls(rows, cols, n, pattern, ro_shift):
     _run_pair("adam", dict(mode="dormancy"), rows, cols, n, pattern, ro_shift=ro_shift)
