@@ -229,13 +229,25 @@ __global__ __launch_bounds__(kThreads) void k_pack(const int64_t* __restrict__ i
     const uint32_t dmask = (1u << digit_bits) - 1u;
     bool bad = false;
     constexpr int64_t kChunk = (int64_t)kPackIpt * kThreads;
-    for (int64_t base = (int64_t)blockIdx.x * kChunk; base < n;
-         base += (int64_t)gridDim.x * kChunk) {
+    const int64_t stride = (int64_t)gridDim.x * kChunk;
+    // The next chunk's ids are requested before this chunk is counted, so a
+    // block with several chunks waits for one load round trip, not one each.
+    int64_t nxt[kPackIpt];
+#pragma unroll
+    for (int j = 0; j < kPackIpt; ++j) {
+        const int64_t i = (int64_t)blockIdx.x * kChunk + (int64_t)j * kThreads + tid;
+        nxt[j] = ids[i < n ? i : n - 1];
+    }
+    for (int64_t base = (int64_t)blockIdx.x * kChunk; base < n; base += stride) {
         int64_t id[kPackIpt];
 #pragma unroll
-        for (int j = 0; j < kPackIpt; ++j) {
-            const int64_t i = base + (int64_t)j * kThreads + tid;
-            id[j] = ids[i < n ? i : n - 1];
+        for (int j = 0; j < kPackIpt; ++j) id[j] = nxt[j];
+        if (base + stride < n) {  // the same for every thread of the block
+#pragma unroll
+            for (int j = 0; j < kPackIpt; ++j) {
+                const int64_t i = base + stride + (int64_t)j * kThreads + tid;
+                nxt[j] = ids[i < n ? i : n - 1];
+            }
         }
         if (thist0 != nullptr) {  // this chunk's first-digit counts (thread d: digit d)
             h0[tid] = 0u;
