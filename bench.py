@@ -75,8 +75,8 @@ UPDATE_SOURCES = ("lazy_optimizer_step_amd/csrc/update.hip",
                   "lazy_optimizer_step_amd/csrc/common.hpp",
                   "lazy_optimizer_step_amd/csrc/csr_full.hpp",
                   "lazy_optimizer_step_amd/csrc/seg_combine.hpp")
-UPDATE_TRAFFIC = {"sources_sha256": "f5d6ca28368bc3892abf6b5eb6356dad4a20bbbf736d0fbbd023ec06bb5630cc",
-                  "fetch_bytes": 2.0 * 33446.6 * 1024, "write_bytes": 1.0 * 104288.7 * 1024}
+UPDATE_TRAFFIC = {"sources_sha256": "ec49f6071ccd114523f0160d63a848d6ddae0ae8c5bfe4f2323dfdcae4314128",
+                  "fetch_bytes": 2.0 * 33446.1 * 1024, "write_bytes": 1.0 * 104296.8 * 1024}
 
 
 def sources_sha256() -> str:

@@ -25,7 +25,9 @@
 // present) is moved with 16-byte loads and stores of p, m, v, last_step and g;
 // a partial row uses one lane per entry.  Rows come from a touched-row list
 // (CSR) or the keys of a full-row COO; without a list the CSR kernel scans
-// row_offsets 64 rows per wave.
+// row_offsets 64 rows per wave.  The step from raw lookups takes its rows from
+// the canonicalisation's segments and shares one launch with the tile combine
+// and the CSR blocks (k_step_lookups).
 #include <hip/hip_ext.h>
 
 #include "common.hpp"
