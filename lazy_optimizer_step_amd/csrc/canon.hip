@@ -7,7 +7,7 @@
 // indices):
 //   1. pack each lookup as (id << pos_bits) | position and radix-sort the
 //      packed words on the id bits only (LSD, stable, so equal ids keep
-//      lookup order, digits of at most 8 bits): one kernel counts the digits
+//      lookup order, digits of at most 9 bits): one kernel counts the digits
 //      of every pass, then each pass is one kernel whose tiles find their
 //      offsets by decoupled look-back;
 //   2. one kernel per tile of 256 sorted lookups: segment heads (id differs
@@ -38,7 +38,7 @@ constexpr int kIpt = 2;                         // items per thread (radix passe
 constexpr int kSortThreads = 1024;              // threads of a radix-pass block
 constexpr int kSortWaves = kSortThreads / kWave;
 constexpr int kTile = kSortThreads * kIpt;      // lookups per radix-pass tile
-constexpr int kRadixBits = 8;                   // at most 256 buckets per radix pass
+constexpr int kRadixBits = 9;                   // at most 512 buckets per radix pass
 constexpr int kRadix = 1 << kRadixBits;
 constexpr int kMaxPasses = 8;
 constexpr int kFixWaves2 = 16;                  // waves of the combining block
@@ -95,10 +95,13 @@ static bool canon_layout(int64_t n, int64_t width, int64_t key_space, CanonLayou
     L->key_bits = bits_for((uint64_t)key_space);
     L->pos_bits = bits_for((uint64_t)(n > 0 ? n : 1));
     if (L->key_bits + L->pos_bits > 64) return false;
-    // As few passes as digits of at most 8 bits allow, digits as even as
-    // possible.  (Wider digits would need fewer passes, but the look-back
-    // words are device-coherent atomics, which do not coalesce: 1024 or 4096
-    // buckets per tile cost far more per pass than the passes they save.)
+    // As few passes as digits of at most 9 bits allow, digits as even as
+    // possible (24-bit keys: three passes of 8; 26-bit keys: three of 9, not
+    // four of 7).  The 512 buckets of a 9-bit digit are owned by half of a
+    // pass block's 1024 threads.  (Wider digits would need fewer passes still,
+    // but then every thread owns several digits, and the look-back words are
+    // device-coherent atomics, which do not coalesce: 1024 or 4096 buckets
+    // per tile cost more per pass than the passes they save.)
     L->passes = (L->key_bits + kRadixBits - 1) / kRadixBits;
     L->digit_bits = L->passes ? (L->key_bits + L->passes - 1) / L->passes : 0;
     L->ntiles = ceil_div(n, kTile);
@@ -216,7 +219,7 @@ __global__ __launch_bounds__(kThreads) void k_pack(const int64_t* __restrict__ i
                                                    uint4* __restrict__ zero, int64_t nzero16,
                                                    uint32_t* __restrict__ thist0) {
     static_assert((int64_t)kPackIpt * kThreads == kTile, "a pack chunk is a radix tile");
-    static_assert(kThreads == kRadix, "thread d owns digit d of a chunk's counts");
+    static_assert(kRadix % kThreads == 0, "threads own whole digits of a chunk's counts");
     __shared__ uint32_t h[kMaxPasses * kRadix];
     __shared__ uint32_t h0[kRadix];
     const int tid = threadIdx.x;
@@ -249,8 +252,8 @@ __global__ __launch_bounds__(kThreads) void k_pack(const int64_t* __restrict__ i
                 nxt[j] = ids[i < n ? i : n - 1];
             }
         }
-        if (thist0 != nullptr) {  // this chunk's first-digit counts (thread d: digit d)
-            h0[tid] = 0u;
+        if (thist0 != nullptr) {  // this chunk's first-digit counts (thread t: digits t + k*256)
+            for (int d = tid; d < kRadix; d += kThreads) h0[d] = 0u;
             __syncthreads();
         }
 #pragma unroll
@@ -274,7 +277,8 @@ __global__ __launch_bounds__(kThreads) void k_pack(const int64_t* __restrict__ i
         }
         if (thist0 != nullptr) {
             __syncthreads();
-            thist0[(base / kChunk) * kRadix + tid] = h0[tid];  // read and later zeroed by tid
+            for (int d = tid; d < kRadix; d += kThreads)  // read and later zeroed by tid
+                thist0[(base / kChunk) * kRadix + d] = h0[d];
         }
     }
     const bool any_bad = __syncthreads_or(bad);
@@ -283,12 +287,12 @@ __global__ __launch_bounds__(kThreads) void k_pack(const int64_t* __restrict__ i
     if (tid == 0) pflag[blockIdx.x] = any_bad ? kStatusRange : 0u;
 }
 
-// One stable radix pass (digits of nbits <= 8 bits) in a single kernel.  A
+// One stable radix pass (digits of nbits <= 9 bits) in a single kernel.  A
 // block takes the next tile ticket, ranks its kTile items (wave w owns items
-// [w*256, (w+1)*256) in four rounds of 64: lanes holding the same digit are
+// [w*128, (w+1)*128) in two rounds of 64: lanes holding the same digit are
 // matched with one ballot per digit bit, a lane's rank is the number of lower
 // lanes with its digit plus the wave's running count of that digit), and
-// thread d < kRadix publishes the tile's count of digit d and sums the counts
+// thread d < 2^nbits publishes the tile's count of digit d and sums the counts
 // of the tiles before it by decoupled look-back.  Its items then go to
 // digit base (scan of the pass histogram) + prefix of the tiles before +
 // prefix of the waves before + rank.
@@ -314,7 +318,9 @@ __global__ __launch_bounds__(kSortThreads) void k_onesweep(
     for (int i = tid; i < kSortWaves * kRadix; i += kSortThreads) (&cnt[0][0])[i] = 0;
     __syncthreads();
     const int64_t tile = thist != nullptr ? (int64_t)blockIdx.x : (int64_t)s_tile;
-    const bool owner = tid < kRadix;  // wave-uniform
+    // Threads below the pass's digit count own the digits (at least a whole
+    // wave, so ownership is wave-uniform; digits past 2^nbits count nothing).
+    const bool owner = tid < ((1 << nbits) > kWave ? (1 << nbits) : kWave);
 
     const int64_t first = tile * kTile + (int64_t)w * (kIpt * kWave);
     const uint64_t lt = lanemask_lt();
@@ -401,7 +407,7 @@ __global__ __launch_bounds__(kSortThreads) void k_onesweep(
         for (int g = 0; g < kPackBlocks; ++g) hd += g < npack ? hpart[g] : 0u;
     }
     uint32_t total;
-    const uint32_t gbase = block_excl_scan(hd, wt, &total);  // all threads; zeros past kRadix
+    const uint32_t gbase = block_excl_scan(hd, wt, &total);  // all threads; zeros past the owners
     if (owner) base[d] = gbase + excl;
     __syncthreads();
     if (s_bad) {
