@@ -76,6 +76,7 @@ constexpr int kCountBatch = 32;
 
 struct CanonLayout {
     int key_bits, pos_bits, passes, digit_bits;
+    int radix;  // row width of the digit counts: 2^digit_bits, at least one wave
     int64_t ntiles, nsum;
     int64_t npack;  // blocks of the pack kernel
     size_t off_a, off_b, off_part, off_pflag, off_thist0, off_clear, clear_bytes, off_status,
@@ -104,6 +105,9 @@ static bool canon_layout(int64_t n, int64_t width, int64_t key_space, CanonLayou
     // per tile cost more per pass than the passes they save.)
     L->passes = (L->key_bits + kRadixBits - 1) / kRadixBits;
     L->digit_bits = L->passes ? (L->key_bits + L->passes - 1) / L->passes : 0;
+    // A pass's digits are owned by whole waves, so a row of counts or
+    // look-back words is at least 64 wide (digits past 2^digit_bits count 0).
+    L->radix = (1 << L->digit_bits) > kWave ? (1 << L->digit_bits) : kWave;
     L->ntiles = ceil_div(n, kTile);
     L->nsum = ceil_div(n, kSumTile);
     L->npack = ceil_div(n, (int64_t)kPackIpt * kThreads);
@@ -119,18 +123,18 @@ static bool canon_layout(int64_t n, int64_t width, int64_t key_space, CanonLayou
     L->off_a = take(sizeof(uint64_t) * (size_t)n);
     L->off_b = take(sizeof(uint64_t) * (size_t)n);
     // Digit histograms and range flag of each pack block.
-    L->off_part = take(sizeof(uint32_t) * (size_t)kPackBlocks * kRadix * P);
+    L->off_part = take(sizeof(uint32_t) * (size_t)kPackBlocks * (size_t)L->radix * P);
     L->off_pflag = take(sizeof(uint32_t) * (size_t)kPackBlocks);
     // Digit counts of each radix tile for the first pass (written whole by the
     // pack kernel when the tiles are few).
-    L->off_thist0 = take(sizeof(uint32_t) * (size_t)kRadix * (size_t)L->ntiles);
+    L->off_thist0 = take(sizeof(uint32_t) * (size_t)L->radix * (size_t)L->ntiles);
     // Everything the kernels after the pack kernel must find zeroed sits in
     // one contiguous region, which the pack kernel zeroes.
     L->off_clear = o;
     L->off_status = take(sizeof(uint32_t) * 4);
     // tickets: one per radix pass and the segment-and-sum kernel's.
     L->off_tickets = take(sizeof(uint32_t) * (kMaxPasses + 1));
-    L->off_words = take(sizeof(uint32_t) * (size_t)kRadix * (size_t)L->ntiles * P);
+    L->off_words = take(sizeof(uint32_t) * (size_t)L->radix * (size_t)L->ntiles * P);
     L->off_sumwords = take(sizeof(uint32_t) * (size_t)L->nsum);
     L->clear_bytes = o - L->off_clear;
     L->off_segstart = take(sizeof(int32_t) * ((size_t)n + 1));
@@ -213,7 +217,8 @@ __global__ void k_status_clear(uint32_t* st, int nwords) {
 // words): those kernels start after this one has ended.
 __global__ __launch_bounds__(kThreads) void k_pack(const int64_t* __restrict__ ids, int64_t n,
                                                    int64_t key_space, int pos_bits, int passes,
-                                                   int digit_bits, uint64_t* __restrict__ out,
+                                                   int digit_bits, int radix,
+                                                   uint64_t* __restrict__ out,
                                                    uint32_t* __restrict__ part,
                                                    uint32_t* __restrict__ pflag,
                                                    uint4* __restrict__ zero, int64_t nzero16,
@@ -223,7 +228,7 @@ __global__ __launch_bounds__(kThreads) void k_pack(const int64_t* __restrict__ i
     __shared__ uint32_t h[kMaxPasses * kRadix];
     __shared__ uint32_t h0[kRadix];
     const int tid = threadIdx.x;
-    const int words = passes * kRadix;
+    const int words = passes * radix;  // radix: row width of the counts, <= kRadix
     for (int i = tid; i < words; i += kThreads) h[i] = 0;
     for (int64_t i = (int64_t)blockIdx.x * kThreads + tid; i < nzero16;
          i += (int64_t)gridDim.x * kThreads)
@@ -233,27 +238,15 @@ __global__ __launch_bounds__(kThreads) void k_pack(const int64_t* __restrict__ i
     bool bad = false;
     constexpr int64_t kChunk = (int64_t)kPackIpt * kThreads;
     const int64_t stride = (int64_t)gridDim.x * kChunk;
-    // The next chunk's ids are requested before this chunk is counted, so a
-    // block with several chunks waits for one load round trip, not one each.
-    int64_t nxt[kPackIpt];
-#pragma unroll
-    for (int j = 0; j < kPackIpt; ++j) {
-        const int64_t i = (int64_t)blockIdx.x * kChunk + (int64_t)j * kThreads + tid;
-        nxt[j] = ids[i < n ? i : n - 1];
-    }
     for (int64_t base = (int64_t)blockIdx.x * kChunk; base < n; base += stride) {
         int64_t id[kPackIpt];
 #pragma unroll
-        for (int j = 0; j < kPackIpt; ++j) id[j] = nxt[j];
-        if (base + stride < n) {  // the same for every thread of the block
-#pragma unroll
-            for (int j = 0; j < kPackIpt; ++j) {
-                const int64_t i = base + stride + (int64_t)j * kThreads + tid;
-                nxt[j] = ids[i < n ? i : n - 1];
-            }
+        for (int j = 0; j < kPackIpt; ++j) {
+            const int64_t i = base + (int64_t)j * kThreads + tid;
+            id[j] = ids[i < n ? i : n - 1];
         }
         if (thist0 != nullptr) {  // this chunk's first-digit counts (thread t: digits t + k*256)
-            for (int d = tid; d < kRadix; d += kThreads) h0[d] = 0u;
+            for (int d = tid; d < radix; d += kThreads) h0[d] = 0u;
             __syncthreads();
         }
 #pragma unroll
@@ -268,7 +261,7 @@ __global__ __launch_bounds__(kThreads) void k_pack(const int64_t* __restrict__ i
                 const uint64_t packed = ((uint64_t)x << pos_bits) | (uint64_t)i;
                 out[i] = packed;
                 for (int p = 0; p < passes; ++p)
-                    atomicAdd(&h[p * kRadix +
+                    atomicAdd(&h[p * radix +
                                  ((uint32_t)(packed >> (pos_bits + p * digit_bits)) & dmask)],
                               1u);
                 if (thist0 != nullptr && passes > 0)
@@ -277,8 +270,8 @@ __global__ __launch_bounds__(kThreads) void k_pack(const int64_t* __restrict__ i
         }
         if (thist0 != nullptr) {
             __syncthreads();
-            for (int d = tid; d < kRadix; d += kThreads)  // read and later zeroed by tid
-                thist0[(base / kChunk) * kRadix + d] = h0[d];
+            for (int d = tid; d < radix; d += kThreads)  // read and later zeroed by tid
+                thist0[(base / kChunk) * radix + d] = h0[d];
         }
     }
     const bool any_bad = __syncthreads_or(bad);
@@ -298,7 +291,7 @@ __global__ __launch_bounds__(kThreads) void k_pack(const int64_t* __restrict__ i
 // prefix of the waves before + rank.
 __global__ __launch_bounds__(kSortThreads) void k_onesweep(
     const uint64_t* __restrict__ in, uint64_t* __restrict__ out, int64_t n, int shift, int nbits,
-    const uint32_t* __restrict__ part, int npack, int part_stride, const uint32_t* pflag,
+    int radix, const uint32_t* __restrict__ part, int npack, int part_stride, const uint32_t* pflag,
     uint32_t* lb, uint32_t* ticket, uint32_t* status, const uint32_t* __restrict__ thist) {
     static_assert(kSortThreads >= kRadix && kRadix % kWave == 0,
                   "threads 0..kRadix-1 own the digits (whole waves)");
@@ -348,7 +341,7 @@ __global__ __launch_bounds__(kSortThreads) void k_onesweep(
     if (owner && thist != nullptr) {
 #pragma unroll
         for (int g = 0; g < kCountBatch; ++g)
-            tpre[g] = thist[(int64_t)(g < tile ? g : 0) * kRadix + tid];
+            tpre[g] = thist[(int64_t)(g < tile ? g : 0) * radix + tid];
     }
 #pragma unroll
     for (int r = 0; r < kIpt; ++r) {
@@ -388,17 +381,17 @@ __global__ __launch_bounds__(kSortThreads) void k_onesweep(
                 uint32_t more[kCountBatch];
 #pragma unroll
                 for (int g = 0; g < kCountBatch; ++g)
-                    more[g] = thist[(g0 + g < tile ? g0 + g : 0) * kRadix + d];
+                    more[g] = thist[(g0 + g < tile ? g0 + g : 0) * radix + d];
 #pragma unroll
                 for (int g = 0; g < kCountBatch; ++g) excl += g0 + g < tile ? more[g] : 0u;
             }
         } else {
-            uint32_t* mine = lb + tile * kRadix + d;
+            uint32_t* mine = lb + tile * radix + d;
             if (tile == 0) {
                 st_dev(mine, kLbInc | run);
             } else {
                 st_dev(mine, kLbAgg | run);
-                ok = look_back(lb + d, tile, kRadix, &excl);
+                ok = look_back(lb + d, tile, radix, &excl);
                 if (ok) st_dev(mine, kLbInc | (excl + run));
             }
         }
@@ -1010,7 +1003,7 @@ static int canon_run(const char* what, const int64_t* ids, const float* vals, in
     const bool counted_sort = L.ntiles <= kMaxCountTiles;
     uint32_t* thist0 = counted_sort ? (uint32_t*)(ws + L.off_thist0) : nullptr;
     k_pack<<<(unsigned)L.npack, kThreads, 0, st>>>(ids, n, key_space, L.pos_bits, L.passes,
-                                                   L.digit_bits, a, part, pflag,
+                                                   L.digit_bits, L.radix, a, part, pflag,
                                                    (uint4*)(ws + L.off_clear),
                                                    (int64_t)(L.clear_bytes / 16), thist0);
     SPOPT_LAUNCHED();
@@ -1035,10 +1028,10 @@ static int canon_run(const char* what, const int64_t* ids, const float* vals, in
         const int rem = L.key_bits - p * L.digit_bits;
         const int nbits = rem < L.digit_bits ? rem : L.digit_bits;
         const int shift = L.pos_bits + p * L.digit_bits;
-        uint32_t* pwords = words + (int64_t)p * L.ntiles * kRadix;
+        uint32_t* pwords = words + (int64_t)p * L.ntiles * L.radix;
         k_onesweep<<<(unsigned)L.ntiles, kSortThreads, 0, st>>>(
-            src, dst, n, shift, nbits, part + (int64_t)p * kRadix, (int)L.npack,
-            L.passes * kRadix, p == 0 ? pflag : nullptr, pwords, tickets + p, status,
+            src, dst, n, shift, nbits, L.radix, part + (int64_t)p * L.radix, (int)L.npack,
+            L.passes * L.radix, p == 0 ? pflag : nullptr, pwords, tickets + p, status,
             p == 0 ? thist0 : nullptr);
         SPOPT_LAUNCHED();
         uint64_t* t = src;
