@@ -280,3 +280,35 @@ def test_random_configurations_match_two_calls():
         except AssertionError as e:
             raise AssertionError(f"case {case}: rows {rows} cols {cols} n {n} {pattern} "
                                  f"{kind} {cfg}: {e}") from None
+
+
+def test_one_call_resume_and_repeat_are_bit_identical():
+    """Ten one-call steps: a run stopped after five, its state copied into a new
+    handle whose step counter is set to 5, then resumed, ends bit for bit where
+    the uninterrupted run does; and a second uninterrupted run repeats it."""
+    import synth
+    w = synth.WORKLOADS[3].scaled(rows=200_000, n_lookups=20000)
+    p0 = synth.init_params(w)
+    batches = [synth.lookups(w, s) for s in range(10)]
+    runs = []
+    for _ in range(2):
+        a = L.SparseAdam(dev(p0), mode="dormancy")
+        for ids, g in batches:
+            a.step_lookups(dev(ids), dev(g))
+        torch.cuda.synchronize()
+        runs.append([host(x).tobytes() for x in (a.params, a.m, a.v, a.last_step)])
+    assert runs[0] == runs[1]
+    b = L.SparseAdam(dev(p0), mode="dormancy")
+    for ids, g in batches[:5]:
+        b.step_lookups(dev(ids), dev(g))
+    torch.cuda.synchronize()
+    c = L.SparseAdam(b.params.clone(), mode="dormancy")
+    c.m.copy_(b.m)
+    c.v.copy_(b.v)
+    c.last_step.copy_(b.last_step)
+    c.handle.set_step(b.t)
+    for ids, g in batches[5:]:
+        c.step_lookups(dev(ids), dev(g))
+    torch.cuda.synchronize()
+    assert c.t == 10
+    assert [host(x).tobytes() for x in (c.params, c.m, c.v, c.last_step)] == runs[0]
