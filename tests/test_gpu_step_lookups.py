@@ -312,3 +312,33 @@ def test_one_call_resume_and_repeat_are_bit_identical():
     torch.cuda.synchronize()
     assert c.t == 10
     assert [host(x).tobytes() for x in (c.params, c.m, c.v, c.last_step)] == runs[0]
+
+
+def test_two_tables_on_two_streams():
+    """Two tables stepped through the one call on two streams at once (each with
+    its own buffers and workspace, the calls interleaved on the host): each ends
+    bit for bit where the same steps on the default stream end."""
+    import synth
+    w1 = synth.WORKLOADS[3].scaled(rows=300_000, n_lookups=30000)
+    w2 = synth.WORKLOADS[2].scaled(rows=100_000, n_lookups=8192)
+    runs = {}
+    for mode in ("sequential", "concurrent"):
+        tabs = [L.SparseAdam(dev(synth.init_params(w)), mode=m)
+                for w, m in ((w1, "dormancy"), (w2, "lazy"))]
+        streams = [torch.cuda.Stream(), torch.cuda.Stream()] if mode == "concurrent" else [None, None]
+        torch.cuda.synchronize()
+        for s in range(6):
+            for k, (w, t) in enumerate(zip((w1, w2), tabs)):
+                ids, g = synth.lookups(w, s)
+                di, dg = dev(ids), dev(g)
+                if streams[k] is not None:
+                    streams[k].wait_stream(torch.cuda.current_stream())   # inputs copied
+                    with torch.cuda.stream(streams[k]):
+                        t.step_lookups(di, dg, stream=streams[k])
+                        di.record_stream(streams[k])
+                        dg.record_stream(streams[k])
+                else:
+                    t.step_lookups(di, dg)
+        torch.cuda.synchronize()
+        runs[mode] = [[host(x).tobytes() for x in (t.params, t.m, t.v, t.last_step)] for t in tabs]
+    assert runs["sequential"] == runs["concurrent"]
