@@ -66,12 +66,15 @@ class _SgdCfg(C.Structure):
 
 
 _lib = None
+# A test that plants mistakes in a copy of oracle.c (tests/test_oracle_mutations.py)
+# points this at the copy's library, in a child process of its own.
+_LIB_ENV = "SPOPT_ORACLE_LIB"
 
 
 def lib():
     global _lib
     if _lib is None:
-        L = C.CDLL(build())
+        L = C.CDLL(os.environ.get(_LIB_ENV) or build())
         P = C.c_void_p
         I64 = C.c_int64
         L.orc_coo_from_lookups.argtypes = [P, P, I64, I64, I64, P, P, P, P, C.c_int]
