@@ -26,6 +26,15 @@ rather than the 256 MB last-level cache; read_rows = the forward gather of each
 step's lookups, timed in a pass of its own; cpu_baseline = the CPU oracle on a
 bounded sample of the same workload.
 
+--workload picks another workload of the same family: table1Mx64 (1M x 64
+rows, 8,192 Zipf(1.1) lookups a step, Lazy), table50Mx128 (50M x 128 rows,
+262,144 Zipf(1.2) lookups, DormancyDecay), or partial2Mx256-sgd /
+partial2Mx256-adam (2M x 256 rows, 16,384 rows a step with 16-64 of their
+columns each: csr_from_coo of the step's flat COO, then sparse_sgd_step
+(lr 0.05, momentum 0.9, coupled weight decay 1e-4) or the DormancyDecay
+sparse_adam_step on that CSR).  Each prints its own JSON line of the same
+form; the value is touched coordinates (nonzeros for partial rows) per second.
+
 Events are created through the HIP runtime with hipEventDisableSystemFence:
 they only take timestamps, and skipping the system-scope release (an L2
 writeback and invalidate per record) keeps them from slowing the work they
@@ -75,8 +84,13 @@ UPDATE_SOURCES = ("lazy_optimizer_step_amd/csrc/update.hip",
                   "lazy_optimizer_step_amd/csrc/common.hpp",
                   "lazy_optimizer_step_amd/csrc/csr_full.hpp",
                   "lazy_optimizer_step_amd/csrc/seg_combine.hpp")
-UPDATE_TRAFFIC = {"sources_sha256": "ec49f6071ccd114523f0160d63a848d6ddae0ae8c5bfe4f2323dfdcae4314128",
-                  "fetch_bytes": 2.0 * 33446.1 * 1024, "write_bytes": 1.0 * 104296.8 * 1024}
+# Keyed by (workload, step form); the default line's entry is the one-call step
+# on the 10M x 128 workload.
+TRAFFIC = {
+    ("table10Mx128_zipf1.05_dormancy", "one_call"): {
+        "sources_sha256": "ec49f6071ccd114523f0160d63a848d6ddae0ae8c5bfe4f2323dfdcae4314128",
+        "fetch_bytes": 2.0 * 33446.1 * 1024, "write_bytes": 1.0 * 104296.8 * 1024},
+}
 
 
 def sources_sha256() -> str:
@@ -114,7 +128,16 @@ def parse():
                          "(rank k -> row (k-1)*999983 mod rows) instead of at the lowest ids")
     ap.add_argument("--host-state", action="store_true",
                     help="keep the table and its state in mapped pinned host memory")
+    ap.add_argument("--workload", default="table10Mx128", choices=sorted(WORKLOAD_CHOICES),
+                    help="table10Mx128 (default), table1Mx64, table50Mx128, partial2Mx256-sgd "
+                         "or partial2Mx256-adam")
     return ap.parse_args()
+
+
+# --workload: (synth workload number, optimizer of the partial-row workload)
+WORKLOAD_CHOICES = {"table1Mx64": (2, None), "table10Mx128": (3, None),
+                    "table50Mx128": (5, None), "partial2Mx256-sgd": (4, "sgd"),
+                    "partial2Mx256-adam": (4, "adam")}
 
 
 class HipEvents:
@@ -271,40 +294,158 @@ def cpu_baseline(w, host_p0, batches, budget_s: float, per_row: bool = False):
         if steps >= 2 and time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
-    model = ""
-    try:
-        with open("/proc/cpuinfo") as f:
-            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
-    except OSError:
-        pass
     return {"value": coords / dt / 1e9, "unit": "G touched coords/s", "cores": 1,
             "kind": "oracle",
             "sample": f"first {steps} steps of the same workload (whole step: canonicalise, CSR, "
                       f"update; {coords} touched coords in {dt:.2f} s, one thread)",
             "canonicalise_s": t_canon, "update_s": dt - t_canon,
-            "host": {"cpu": model, "nproc": os.cpu_count()}}
+            "host": {"cpu": cpu_model(), "nproc": os.cpu_count()}}
 
 
-def main() -> int:
-    args = parse()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: the sparse step is built and timed on a single "
-              "MI355X; run it with --gpus 1", file=sys.stderr, flush=True)
-        return 2
+def kernel_label(op: str, lpr: int, iters: int, one_call: bool, src: str) -> str:
+    if one_call:
+        return f"k_step_lookups<{op}, {lpr}, {iters}> (tile combine + update + CSR blocks)"
+    return f"k_update_rows<{op}, {src}, {lpr}, {iters}>"
 
+
+def lanes_per_row(cols: int) -> int:
+    """Lanes the update kernels give one full row (16-byte vectors, as the library)."""
+    nvec = (cols + 3) // 4
+    return 4 if nvec <= 4 else 16 if nvec <= 16 else 32 if nvec <= 32 else 64
+
+
+def timed_passes(torch, stream, K, W, step, L, ev_count_per_step=None):
+    """The timed pass (value) and the update launch's per-step durations: K steps
+    queued behind a bounded spin, events around the region and the library's
+    pair on each update launch."""
+    ev = HipEvents(2 + 2 * K)
+    cycles = calibrate_sleep(torch, stream, hold_ms=2.0 + 0.5 * K)
+    log(f"timed {K} steps (queued behind a {cycles}-cycle spin)")
+    torch.cuda._sleep(cycles)
+    ev.record(0, stream)
+    for k, s in enumerate(range(W, W + K)):
+        L.set_step_events(ev.ev[2 + 2 * k], ev.ev[3 + 2 * k])
+        step(s)
+    L.set_step_events()
+    ev.record(1, stream)
+    torch.cuda.synchronize()
+    import numpy as np
+
+    total_ms = ev.ms(0, 1)
+    upd = np.array([ev.ms(2 + 2 * k, 3 + 2 * k) for k in range(K)])
+    ev.close()
+    return total_ms, upd, cycles
+
+
+def breakdown_pass(torch, stream, K, W, calls, step, L, cycles, one_call):
+    """The same K inputs again, every call bracketed by events and the update
+    launch by the hook's pair (not part of the value)."""
+    import numpy as np
+
+    E = len(calls) + 3  # events per step: before each call, after the last, the hook's two
+    bev = HipEvents(E * K)
+    torch.cuda._sleep(cycles)
+    for k, s in enumerate(range(W, W + K)):
+        L.set_step_events(bev.ev[E * k + E - 2], bev.ev[E * k + E - 1])
+        step(s, bev, E * k)
+    L.set_step_events()
+    torch.cuda.synchronize()
+    breakdown = {}
+    for c, (name, _) in enumerate(calls):
+        breakdown[name] = pcts(np.array([bev.ms(E * k + c, E * k + c + 1) for k in range(K)]))
+    breakdown["update_launch"] = pcts(
+        np.array([bev.ms(E * k + E - 2, E * k + E - 1) for k in range(K)]))
+    if one_call:
+        # the canonicalisation kernels of the one call, before its last launch
+        breakdown["before_update_launch"] = pcts(
+            np.array([bev.ms(E * k, E * k + E - 2) for k in range(K)]))
+    breakdown["step"] = pcts(np.array([bev.ms(E * k, E * k + len(calls)) for k in range(K)]))
+    bev.close()
+    return breakdown
+
+
+def cold_passes(torch, K, W, step, L):
+    """The update launch with the last-level cache evicted before every step, two
+    ways: a 512 MB buffer written (its dirty lines are written back while the
+    step runs, as after a training step's other work) and the same buffer only
+    read (clean lines, so the launch's own traffic alone).  Not part of the value."""
+    import numpy as np
+
+    scrub = torch.empty(128 << 20, dtype=torch.float32, device="cuda")
+    sink = torch.empty(1, dtype=torch.float32, device="cuda")
+    out = {}
+    for kind in ("written", "read"):
+        log(f"cold pass (512 MB {kind} between steps)")
+        cev = HipEvents(2 * K)
+        for k, s in enumerate(range(W, W + K)):
+            if kind == "written":
+                scrub.fill_(float(k))
+            else:
+                torch.sum(scrub, dim=0, keepdim=True, out=sink)
+            L.set_step_events(cev.ev[2 * k], cev.ev[2 * k + 1])
+            step(s)
+        L.set_step_events()
+        torch.cuda.synchronize()
+        out[kind] = np.array([cev.ms(2 * k, 2 * k + 1) for k in range(K)])
+        cev.close()
+    del scrub
+    return out["written"], out["read"]
+
+
+def roofline_block(upd, upd_cold, upd_clean, upd_bytes, coords, copy_gbs, traffic, kernel):
+    achieved = float((upd_bytes / (upd * 1e-3)).mean() / 1e9)
+
+    def regime(x):
+        a = float((upd_bytes / (x * 1e-3)).mean() / 1e9)
+        return {"achieved": a, "frac": a / HBM_PEAK_GBS,
+                "traffic_GBs": None if traffic is None else traffic / (x.mean() * 1e-3) / 1e9,
+                "mean_us": float(x.mean() * 1e3), "us": pcts(x)}
+
+    return {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+            "traffic_GBs": None if traffic is None else traffic / (upd.mean() * 1e-3) / 1e9,
+            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled)",
+            "algorithmic_bytes_per_launch": float(upd_bytes.mean()),
+            "kernel": kernel,
+            "mean_us": float(upd.mean() * 1e3), "us": pcts(upd),
+            "coords_per_s_G": float((coords / (upd * 1e-3)).mean() / 1e9),
+            "device_copy_GBs": copy_gbs,
+            "frac_of_device_copy": achieved / copy_gbs,
+            "cold": regime(upd_cold), "cold_clean": regime(upd_clean)}
+
+
+def traffic_for(name: str, form: str):
+    t = TRAFFIC.get((name, form))
+    if t is None or sources_sha256() != t["sources_sha256"]:
+        return None
+    return t["fetch_bytes"] + t["write_bytes"]
+
+
+def result_head(w, K, W, total_ms, coords_total, metric):
+    return {
+        "metric": metric,
+        "value": coords_total / (total_ms * 1e-3) / 1e9,
+        "unit": "G touched coords/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": total_ms / K,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+    }
+
+
+def run_lookups(args, cfg: int) -> dict:
     import numpy as np
     import torch
-
-    if args.copy_probe:
-        copy_probe(args.warmup + args.steps)
-        return 0
 
     import lazy_optimizer_step_amd as L
     import synth
 
-    torch.cuda.set_device(0)
-    w = synth.WORKLOADS[3]
+    w = synth.WORKLOADS[cfg]
     if args.scrambled:
         w = w.scaled(name=w.name + "_scrambled", scramble=SCRAMBLE)
     R, Cc, n = w.rows, w.cols, w.n_lookups
@@ -368,6 +509,7 @@ def main() -> int:
         calls = [("csr_from_lookups", lookups_csr), ("sparse_adam_step", adam)]
     else:
         calls = [("sparse_step_from_lookups", fused)]
+    one_call = len(calls) == 1
 
     def step(s: int, ev=None, base: int = 0) -> None:
         """One step; with ev, event base + c is recorded before call c and
@@ -385,62 +527,9 @@ def main() -> int:
         step(s)
     torch.cuda.synchronize()
 
-    # Timed region: K whole steps.  Events bracket the region, and the library
-    # attaches a pair to the dispatch of every launch that updates the table
-    # (its timing hook).  A bounded spin kernel holds the stream while the host queues
-    # every step behind it, so the steps run back to back and the events time
-    # device work rather than the host's launch rate.
-    ev = HipEvents(2 + 2 * K)
-    cycles = calibrate_sleep(torch, stream, hold_ms=2.0 + 0.5 * K)
-    log(f"timed {K} steps (queued behind a {cycles}-cycle spin)")
-    torch.cuda._sleep(cycles)
-    ev.record(0, stream)
-    for k, s in enumerate(range(W, W + K)):
-        L.set_step_events(ev.ev[2 + 2 * k], ev.ev[3 + 2 * k])
-        step(s)
-    L.set_step_events()
-    ev.record(1, stream)
-    torch.cuda.synchronize()
-    total_ms = ev.ms(0, 1)
-    upd = np.array([ev.ms(2 + 2 * k, 3 + 2 * k) for k in range(K)])
-    ev.close()
-
-    # Breakdown (not part of the value): the same K inputs again, every call
-    # bracketed by events, and the update launch by the hook's pair.
-    E = len(calls) + 3  # events per step: before each call, after the last, the hook's two
-    bev = HipEvents(E * K)
-    torch.cuda._sleep(cycles)
-    for k, s in enumerate(range(W, W + K)):
-        L.set_step_events(bev.ev[E * k + E - 2], bev.ev[E * k + E - 1])
-        step(s, bev, E * k)
-    L.set_step_events()
-    torch.cuda.synchronize()
-    breakdown = {}
-    for c, (name, _) in enumerate(calls):
-        breakdown[name] = pcts(np.array([bev.ms(E * k + c, E * k + c + 1) for k in range(K)]))
-    breakdown["update_launch"] = pcts(
-        np.array([bev.ms(E * k + E - 2, E * k + E - 1) for k in range(K)]))
-    if not args.separate_calls and not args.two_calls:
-        # the canonicalisation kernels of the one call, before its last launch
-        breakdown["before_update_launch"] = pcts(
-            np.array([bev.ms(E * k, E * k + E - 2) for k in range(K)]))
-    breakdown["step"] = pcts(np.array([bev.ms(E * k, E * k + len(calls)) for k in range(K)]))
-    bev.close()
-
-    # Cold regime (not part of the value): the same K inputs, a 512 MB buffer
-    # written between steps to evict the last-level cache, update launch timed.
-    log("cold pass (512 MB written between steps)")
-    scrub = torch.empty(128 << 20, dtype=torch.float32, device="cuda")
-    cev = HipEvents(2 * K)
-    for k, s in enumerate(range(W, W + K)):
-        scrub.fill_(float(k))
-        L.set_step_events(cev.ev[2 * k], cev.ev[2 * k + 1])
-        step(s)
-    L.set_step_events()
-    torch.cuda.synchronize()
-    upd_cold = np.array([cev.ms(2 * k, 2 * k + 1) for k in range(K)])
-    cev.close()
-    del scrub
+    total_ms, upd, cycles = timed_passes(torch, stream, K, W, step, L)
+    breakdown = breakdown_pass(torch, stream, K, W, calls, step, L, cycles, one_call)
+    upd_cold, upd_clean = cold_passes(torch, K, W, step, L)
     copy_gbs = device_copy_gbs(torch, stream)
 
     # Forward gather (not part of the value): read_rows of each step's lookups.
@@ -457,84 +546,220 @@ def main() -> int:
     rr_bytes = n * (8 + 2 * 4 * Cc)
 
     U = nuniq.cpu().numpy()[W:]
-    coords = int(U.sum()) * Cc
+    coords = U * Cc
+    dormancy = w.mode == "dormancy"
+    # Lazy mode writes last_step but does not read it: 4 B less per coordinate
+    # (per row with one last_step per row)
     if per_row:
-        upd_bytes = BYTES_PER_COORD_ROW_LS * U * Cc + BYTES_PER_ROW_ROW_LS * U
+        upd_bytes = BYTES_PER_COORD_ROW_LS * U * Cc + (BYTES_PER_ROW_ROW_LS - 4 * (not dormancy)) * U
     else:
-        upd_bytes = BYTES_PER_COORD * U * Cc + BYTES_PER_ROW * U
-    one_call = not args.separate_calls and not args.two_calls
+        upd_bytes = (BYTES_PER_COORD - 4 * (not dormancy)) * U * Cc + BYTES_PER_ROW * U
     if one_call and not args.host_state:
         # the same launch also writes the CSR's row_offsets and col_indices
         # (with the state in host memory those bytes stay in HBM, off the
         # host link that bounds the launch, and are left out)
         upd_bytes = upd_bytes + (CSR_BYTES_PER_COORD * U * Cc + CSR_BYTES_PER_ROW * U
                                  + CSR_BYTES_PER_TABLE_ROW * (R + 1) + 4 * (R // 8192 + 1))
-    achieved = float((upd_bytes / (upd * 1e-3)).mean() / 1e9)
-    cold_achieved = float((upd_bytes / (upd_cold * 1e-3)).mean() / 1e9)
+    form = "one_call" if one_call else ("two_calls" if args.two_calls else "separate_calls")
     traffic = None
-    if one_call and not per_row and not args.host_state \
-            and sources_sha256() == UPDATE_TRAFFIC["sources_sha256"]:
-        traffic = UPDATE_TRAFFIC["fetch_bytes"] + UPDATE_TRAFFIC["write_bytes"]
-    # measured DRAM bytes / time beside algorithmic bytes / time, each regime
-    # (the counters read the same bytes per launch, within 0.1%, in both)
-    traffic_gbs = None if traffic is None else traffic / (upd.mean() * 1e-3) / 1e9
-    traffic_gbs_cold = None if traffic is None else traffic / (upd_cold.mean() * 1e-3) / 1e9
-    op = ("AdamOp<DormancyDecay, no decay, "
+    if not per_row and not args.host_state and not args.scrambled:
+        traffic = traffic_for(w.name, form)
+    op = (f"AdamOp<{'DormancyDecay' if dormancy else 'Lazy'}, no decay, "
           + ("last_step per row" if per_row else "last_step per coordinate") + ">")
-    kernel = (f"k_step_lookups<{op}, 32, 2> (tile combine + update + CSR blocks)" if one_call
-              else f"k_update_rows<{op}, SrcCsrTouched, 32, 2>")
+    lpr = lanes_per_row(Cc)
+    kernel = kernel_label(op, lpr, 1 if lpr == 4 else 2, one_call, "SrcCsrTouched")
 
-    result = {
-        "metric": METRIC,
-        "value": coords / (total_ms * 1e-3) / 1e9,
-        "unit": "G touched coords/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": W,
-        "ms_per_step": total_ms / K,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic",
-        "config": {"workload": w.name, "rows": R, "cols": Cc, "lookups_per_step": n,
-                   "zipf_s": w.zipf_s, "mode": w.mode,
-                   "state": "p,m,v float32 + last_step int32 per "
-                            + ("row" if per_row else "coordinate")
-                            + (", in mapped pinned host memory" if args.host_state else ", in HBM"),
-                   "mean_unique_rows": float(U.mean()),
-                   "calls": " + ".join(c for c, _ in calls)},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "traffic_GBs": traffic_gbs,
-                     "traffic_unit":
-                         "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled)",
-                     "algorithmic_bytes_per_launch": float(upd_bytes.mean()),
-                     "kernel": kernel,
-                     "mean_us": float(upd.mean() * 1e3), "us": pcts(upd),
-                     "coords_per_s_G": float((U * Cc / (upd * 1e-3)).mean() / 1e9),
-                     "device_copy_GBs": copy_gbs,
-                     "frac_of_device_copy": achieved / copy_gbs,
-                     "cold": {"achieved": cold_achieved, "frac": cold_achieved / HBM_PEAK_GBS,
-                              "traffic_GBs": traffic_gbs_cold,
-                              "mean_us": float(upd_cold.mean() * 1e3), "us": pcts(upd_cold)}},
-        "breakdown_us": breakdown,
-        "read_rows": {"us": pcts(rr), "lookups": n,
-                      "achieved_GBs": float((rr_bytes / (rr * 1e-3)).mean() / 1e9),
-                      "bytes_per_lookup": 8 + 2 * 4 * Cc},
-    }
+    metric = METRIC if cfg == 3 else METRIC.replace("10M x 128 table", f"{R // 10**6}M x {Cc} table")
+    result = result_head(w, K, W, total_ms, int(coords.sum()), metric)
+    result["config"] = {"workload": w.name, "rows": R, "cols": Cc, "lookups_per_step": n,
+                        "zipf_s": w.zipf_s, "mode": w.mode,
+                        "state": "p,m,v float32 + last_step int32 per "
+                                 + ("row" if per_row else "coordinate")
+                                 + (", in mapped pinned host memory" if args.host_state
+                                    else ", in HBM"),
+                        "mean_unique_rows": float(U.mean()),
+                        "calls": " + ".join(c for c, _ in calls)}
+    result["roofline"] = roofline_block(upd, upd_cold, upd_clean, upd_bytes, coords, copy_gbs,
+                                        traffic, kernel)
+    result["breakdown_us"] = breakdown
+    result["read_rows"] = {"us": pcts(rr), "lookups": n,
+                           "achieved_GBs": float((rr_bytes / (rr * 1e-3)).mean() / 1e9),
+                           "bytes_per_lookup": 8 + 2 * 4 * Cc}
     if args.host_state:
         # The state crosses the host link, not HBM: the roofline that bounds the
         # update is the link's, measured here with plain pinned copies.
         link = host_link_gbs(torch, stream)
-        result["roofline"]["bound"] = "host link"
-        result["roofline"]["peak"] = link["host_to_device"] + link["device_to_host"]
-        result["roofline"]["frac"] = achieved / result["roofline"]["peak"]
-        result["roofline"]["host_link_copy_GBs"] = link
-        result["roofline"]["peak_note"] = "sum of the measured pinned copy rates, each direction"
+        rf = result["roofline"]
+        rf["bound"] = "host link"
+        rf["peak"] = link["host_to_device"] + link["device_to_host"]
+        rf["frac"] = rf["achieved"] / rf["peak"]
+        rf["host_link_copy_GBs"] = link
+        rf["peak_note"] = "sum of the measured pinned copy rates, each direction"
     if args.cpu_seconds > 0:
         log("cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(w, host_p0, batches, args.cpu_seconds, per_row)
+    return result
+
+
+# Partial rows: algorithmic bytes per nonzero of the update (SGD with momentum:
+# read p, b, g and write p, b; Adam DormancyDecay: read p, m, v, last_step, g and
+# write p, m, v, last_step), plus its column index; the update kernel without a
+# touched-row list reads row_offsets over every table row (4 B per row, plus one).
+PARTIAL_BYTES_PER_NNZ = {"sgd": 20, "adam": 36}
+PARTIAL_COL_BYTES = 4
+
+
+def cpu_baseline_partial(w, kind, host_p0, entries, budget_s: float):
+    """The oracle, as it stands, on the first steps of the partial-row workload
+    (COO -> CSR, then the step) until the time budget is spent; single thread."""
+    import oracle
+
+    import numpy as np
+
+    h = w.hyper
+    zeros = lambda dt=np.float32: np.zeros((w.rows, w.cols), dt)  # pages mapped lazily
+    if kind == "sgd":
+        opt = oracle.Sgd(host_p0, lr=h["lr"], momentum=h["momentum"],
+                         weight_decay=h["weight_decay"], b=zeros())
+    else:
+        opt = oracle.Adam(host_p0, lr=h["lr"], beta1=h["beta1"], beta2=h["beta2"], eps=h["eps"],
+                          mode="dormancy", m=zeros(), v=zeros(), last_step=zeros(np.int32))
+    nnz = 0
+    steps = 0
+    t_canon = 0.0
+    t0 = time.perf_counter()
+    for er, ec, ev in entries:
+        tc = time.perf_counter()
+        lin = er * w.cols + ec
+        ro, ci, cv = oracle.csr_from_coo(lin, ev, w.rows * w.cols, 1, w.rows, w.cols)
+        t_canon += time.perf_counter() - tc
+        opt.step_csr(ro, ci, cv)
+        nnz += lin.size
+        steps += 1
+        if steps >= 2 and time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": nnz / dt / 1e9, "unit": "G touched coords/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {steps} steps of the same workload (COO -> CSR, then the step; "
+                      f"{nnz} nonzeros in {dt:.2f} s, one thread)",
+            "canonicalise_s": t_canon, "update_s": dt - t_canon,
+            "host": {"cpu": cpu_model(), "nproc": os.cpu_count()}}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            return next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:
+        return ""
+
+
+def run_partial(args, kind: str) -> dict:
+    import numpy as np
+    import torch
+
+    import lazy_optimizer_step_amd as L
+    import synth
+
+    w = synth.WORKLOADS[4] if kind == "sgd" else synth.WORKLOAD_4_ADAM
+    R, Cc = w.rows, w.cols
+    K, W = args.steps, args.warmup
+    h = w.hyper
+    log(f"initial table {R}x{Cc} float32 (N(0, {w.init_std}))")
+    host_p0 = synth.init_params(w)
+    p_d = torch.from_numpy(host_p0).to("cuda")
+    if kind == "sgd":
+        opt = L.SparseSgd(p_d, lr=h["lr"], momentum=h["momentum"], weight_decay=h["weight_decay"])
+    else:
+        opt = L.SparseAdam(p_d, lr=h["lr"], beta1=h["beta1"], beta2=h["beta2"], eps=h["eps"],
+                           mode="dormancy")
+    log(f"inputs of {W + K} steps ({w.n_rows_touched} rows of {w.col_min}-{w.col_max} columns)")
+    entries = synth.partial_rows_many(w, range(W + K))
+    lin_d = [torch.from_numpy(er * Cc + ec).to("cuda") for er, ec, _ in entries]
+    val_d = [torch.from_numpy(ev).to("cuda") for _, _, ev in entries]
+    nnz = np.array([x.numel() for x in lin_d])
+    row_offsets = torch.empty(R + 1, dtype=torch.int32, device="cuda")
+    col_indices = torch.empty(int(nnz.max()), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def to_csr(s: int):
+        coo = L.CooGradient(lin_d[s], val_d[s], dim=R * Cc, width=1)
+        return L.csr_from_coo(coo, R, Cc, row_offsets=row_offsets, col_indices=col_indices,
+                              copy_values=False, stream=stream)
+
+    def upd(g) -> None:
+        opt.step(g, stream=stream)
+
+    step_name = "sparse_sgd_step" if kind == "sgd" else "sparse_adam_step"
+    calls = [("csr_from_coo", to_csr), (step_name, upd)]
+
+    def step(s: int, ev=None, base: int = 0) -> None:
+        g = None
+        for c, (name, f) in enumerate(calls):
+            if ev is not None:
+                ev.record(base + c, stream)
+            g = f(g) if f is upd else f(s)
+        if ev is not None:
+            ev.record(base + len(calls), stream)
+
+    log(f"warmup {W} steps")
+    for s in range(W):
+        step(s)
+    torch.cuda.synchronize()
+    total_ms, upd_ms, cycles = timed_passes(torch, stream, K, W, step, L)
+    breakdown = breakdown_pass(torch, stream, K, W, calls, step, L, cycles, False)
+    upd_cold, upd_clean = cold_passes(torch, K, W, step, L)
+    copy_gbs = device_copy_gbs(torch, stream)
+
+    nz = nnz[W:]
+    upd_bytes = (PARTIAL_BYTES_PER_NNZ[kind] + PARTIAL_COL_BYTES) * nz + 4 * (R + 1)
+    op = "SgdOp<momentum>" if kind == "sgd" else "AdamOp<DormancyDecay, no decay, last_step per coordinate>"
+    kernel = f"k_update_csr_scan<{op}>"
+    metric = METRIC.replace("10M x 128 table", f"2M x {Cc} table, partial rows")
+    result = result_head(w, K, W, total_ms, int(nz.sum()), metric)
+    result["config"] = {"workload": w.name, "rows": R, "cols": Cc,
+                        "rows_per_step": w.n_rows_touched,
+                        "cols_per_row": [w.col_min, w.col_max],
+                        "optimizer": kind if kind == "sgd" else "adam dormancy",
+                        "state": ("p, momentum float32" if kind == "sgd"
+                                  else "p,m,v float32 + last_step int32 per coordinate")
+                                 + ", in HBM",
+                        "mean_nnz": float(nz.mean()),
+                        "calls": " + ".join(c for c, _ in calls)}
+    result["roofline"] = roofline_block(upd_ms, upd_cold, upd_clean, upd_bytes, nz, copy_gbs,
+                                        traffic_for(w.name, "two_calls"), kernel)
+    result["breakdown_us"] = breakdown
+    if args.cpu_seconds > 0:
+        log("cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline_partial(w, kind, host_p0, entries, args.cpu_seconds)
+    return result
+
+
+def main() -> int:
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the sparse step is built and timed on a single "
+              "MI355X; run it with --gpus 1", file=sys.stderr, flush=True)
+        return 2
+
+    import torch
+
+    if args.copy_probe:
+        copy_probe(args.warmup + args.steps)
+        return 0
+
+    cfg, kind = WORKLOAD_CHOICES[args.workload]
+    if kind is not None and (args.two_calls or args.separate_calls or args.last_step_per_row
+                             or args.scrambled or args.host_state):
+        print("the partial-row workloads take none of --two-calls, --separate-calls, "
+              "--last-step-per-row, --scrambled, --host-state", file=sys.stderr, flush=True)
+        return 2
+    torch.cuda.set_device(0)
+    if kind is not None:
+        result = run_partial(args, kind)
+    else:
+        result = run_lookups(args, cfg)
     print(json.dumps(result), flush=True)
     return 0
 

@@ -15,7 +15,7 @@
  *     step t (the number of step calls so far) and apply
  *     p -= lr * m_hat / (sqrt(v_hat) + eps).
  * Untouched coordinates are never read or written, so they stay bit-identical.
- * From the DiskSparseAdam README (page 2), where page 1 is silent: duplicate
+ * From the DiskSparseAdam README, where the optirs page is silent: duplicate
  * lookups are summed and emitted in ascending order ("Safe Duplicate
  * Aggregation & Sorted I/O"); out-of-range indices, wrong shapes and
  * non-finite gradients are errors ("Validated Inputs"; step() method).
@@ -23,10 +23,13 @@
  * Conventions for every entry point:
  *   - Pointers named d_* or documented as "device" are HIP device pointers
  *     (e.g. torch tensor data_ptr()); the caller allocates and owns all of
- *     them, including state, outputs and workspace.  The library's only
- *     device allocation is a 256-byte status block per device, made by the
- *     first SPOPT_VALIDATE call on that device and kept until the process
- *     ends; validated calls are serialised process-wide around it.
+ *     them, including state, outputs and workspace.  The library itself
+ *     allocates device memory in two places only: sparse_opt_create makes a
+ *     16 KB table of beta1^k and beta2^k (k < 1024, double) for every Adam
+ *     handle, freed by sparse_opt_destroy; and the first SPOPT_VALIDATE call
+ *     on a device makes a 256-byte status block for that device, kept until
+ *     the process ends (validated calls are serialised process-wide around
+ *     it).  Step, canonicalisation and conversion calls allocate nothing.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream) on
  *     the calling thread's current device.  All device work is enqueued on
  *     it; calls return before it finishes unless SPOPT_VALIDATE is set, in
@@ -127,8 +130,8 @@ typedef struct spopt_sgd_config {
 
 /* COO gradient over a dense (dim x width) object: entry k covers coordinates
  * indices[k]*width + j for j < width, with values[k*width + j].
- *   width == 1: P1's CooGradient (a 1-D vector, or the rows*cols flattened
- *               view of a table);
+ *   width == 1: the optirs_gpu sparse_optimizer page's CooGradient (a 1-D
+ *               vector, or the rows*cols flattened view of a table);
  *   width == cols of a table: indices are row ids and every entry is a full
  *               row (the compact form of a CSR whose touched rows are full).
  * indices strictly ascending in [0, dim).
@@ -239,7 +242,8 @@ SPOPT_API int sparse_opt_host_device_pointer(void* host_ptr, void** device_ptr);
 SPOPT_API int sparse_opt_workspace_size(int64_t n, int64_t width, int64_t key_space, size_t* bytes);
 
 /* Raw lookups -> canonical COO (DiskSparseAdam "Safe Duplicate Aggregation &
- * Sorted I/O"; P1 canonical COO).
+ * Sorted I/O"; the canonical CooGradient of the optirs_gpu sparse_optimizer
+ * page, section "Sparse gradient representations").
  *   ids        device int64 [n], each in [0, key_space)
  *   vals       device float [n * width], row i belongs to ids[i]
  *   out_keys   device int64 [n]: the U distinct ids, strictly ascending
@@ -257,13 +261,19 @@ SPOPT_API int sparse_opt_workspace_size(int64_t n, int64_t width, int64_t key_sp
  * with SPOPT_VALIDATE also SPOPT_ERANGE (an id outside [0, key_space)) and
  * SPOPT_ENONFINITE.  In trusted mode an out-of-range id is still detected on
  * the device; the call then sets *d_nunique = 0 (an empty gradient) and
- * writes no other output. */
+ * writes no other output.  The sort and segment kernels coordinate their
+ * blocks through bounded device-side waits; the blocks are numbered in the
+ * order they start, so a wait only ever waits on a block that is running,
+ * and the bound (about a second) is there to turn a library bug into an
+ * answer rather than a hang.  A wait that gives up ends the call the same
+ * way: *d_nunique = 0, no other output written (under SPOPT_VALIDATE too:
+ * the validation reads the inputs before the sort). */
 SPOPT_API int coo_from_lookups(const int64_t* ids, const float* vals, int64_t n, int64_t width,
                      int64_t key_space, int64_t* out_keys, float* out_vals, int32_t* out_counts,
                      int64_t* d_nunique, void* workspace, size_t workspace_bytes, void* stream,
                      uint32_t flags);
 
-/* ---- COO <-> CSR (P1 CsrGradient::from_coo / to_coo) -------------------- */
+/* ---- COO <-> CSR (optirs_gpu sparse_optimizer: CsrGradient::from_coo / to_coo) */
 
 /* Canonical COO -> CSR of shape rows x cols.
  *   in->width == 1:    in->dim must be rows*cols; row = idx / cols,
@@ -287,8 +297,8 @@ SPOPT_API int csr_from_coo(const spopt_coo* in, int64_t rows, int64_t cols, int3
 /* Raw lookups of full table rows -> full-row CSR gradient in one call: the
  * same outputs, bit for bit, as coo_from_lookups(ids, vals, n, cols, rows, ...)
  * followed by csr_from_coo on that COO with its values and row ids used in
- * place (DiskSparseAdam "Safe Duplicate Aggregation & Sorted I/O"; P1
- * CsrGradient::from_coo).  While it numbers the distinct ids, the segment
+ * place (DiskSparseAdam "Safe Duplicate Aggregation & Sorted I/O"; the
+ * optirs_gpu sparse_optimizer page's CsrGradient::from_coo).  While it numbers the distinct ids, the segment
  * kernel records how many lie below each block of 8192 rows, so the
  * row_offsets blocks need no search, and the combine of tile-crossing sums
  * shares one launch with them.
@@ -352,7 +362,9 @@ SPOPT_API int sparse_sgd_step(spopt_t h, const spopt_grad* g, void* stream, uint
  * NULL handle.  A step the validation rejects leaves the table and t as they
  * were; the canonical outputs are written all the same.  In trusted mode an
  * out-of-range id gives U = 0, as csr_from_lookups: no row is updated and t
- * still advances. */
+ * still advances; so does a device-side wait that gives up (see
+ * coo_from_lookups).  A caller that must tell such a step from one with no
+ * lookups reads *d_nunique after it. */
 SPOPT_API int sparse_step_from_lookups(spopt_t h, const int64_t* ids, const float* vals, int64_t n,
                                        int64_t* out_keys, float* out_vals, int32_t* out_counts,
                                        int64_t* d_nunique, int32_t* row_offsets,

@@ -2,8 +2,10 @@
 
 The functions below carry the C ABI's names (include/sparse_opt.h) and only
 marshal arguments: they check dtypes, devices and contiguity, allocate
-outputs with torch when none are given, and call the library on torch's
-current stream.  All arithmetic runs in the library's HIP kernels.
+outputs (and the canonicalisation's workspace) with torch when none are
+given, and call the library on torch's current stream, or on ``stream=``
+(then what they allocate is allocated on that stream).  All arithmetic runs
+in the library's HIP kernels.
 
 Pages followed (see the header for the full contract): the optirs_gpu
 sparse_optimizer module page (COO/CSR gradients, sparse SGD, Lazy and
@@ -12,6 +14,7 @@ the DiskSparseAdam README (duplicates summed and sorted, validated inputs).
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes as C
 from dataclasses import dataclass
 
@@ -37,6 +40,20 @@ def _stream(stream) -> int:
     if isinstance(stream, torch.cuda.Stream):
         return stream.cuda_stream
     return int(stream)
+
+
+def _alloc_on(stream):
+    """Context in which torch allocates on the stream the call's kernels run on.
+    The caching allocator then gives memory this call allocates (its internal
+    workspace, dropped on return) to no other stream until the work queued on
+    `stream` has finished with it."""
+    if stream is None:
+        return contextlib.nullcontext()
+    if not isinstance(stream, torch.cuda.Stream):
+        if int(stream) == torch.cuda.current_stream().cuda_stream:
+            return contextlib.nullcontext()
+        stream = torch.cuda.ExternalStream(int(stream))
+    return torch.cuda.stream(stream)
 
 
 class HostArray:
@@ -187,6 +204,13 @@ def coo_from_lookups(ids: torch.Tensor, vals: torch.Tensor, key_space: int, *, o
                      stream=None, validate: bool = False):
     """Raw lookups -> canonical COO.  Returns (keys, vals, counts, d_nunique), all
     sized by the lookup count n; the first U = d_nunique entries are the result."""
+    with _alloc_on(stream):
+        return _coo_from_lookups(ids, vals, key_space, out_keys, out_vals, out_counts, d_nunique,
+                                 workspace, stream, validate)
+
+
+def _coo_from_lookups(ids, vals, key_space, out_keys, out_vals, out_counts, d_nunique, workspace,
+                      stream, validate):
     n = ids.numel()
     width = vals.numel() // n if n else (vals.shape[1] if vals.dim() == 2 else 1)
     dev = ids.device
@@ -221,6 +245,13 @@ def csr_from_coo(coo: CooGradient, rows: int, cols: int, *, row_offsets=None, co
     """Canonical COO -> CSR.  Returns a CsrGradient.  For a full-row COO the touched
     rows are the COO's keys (no copy unless touched_rows is given), and values may
     alias the COO's (copy_values=False)."""
+    with _alloc_on(stream):
+        return _csr_from_coo(coo, rows, cols, row_offsets, col_indices, values, touched_rows,
+                             d_n_touched, want_col_indices, copy_values, stream, validate)
+
+
+def _csr_from_coo(coo, rows, cols, row_offsets, col_indices, values, touched_rows, d_n_touched,
+                  want_col_indices, copy_values, stream, validate):
     c = coo._c()
     dev = coo.indices.device
     total = c.nnz * coo.width
@@ -293,13 +324,14 @@ def csr_from_lookups(ids: torch.Tensor, vals: torch.Tensor, rows: int, *, out_ke
     result of coo_from_lookups then csr_from_coo(copy_values=False), bit for bit.
     vals: (n, cols).  Returns (csr, counts, d_nunique): csr.touched_rows holds the
     distinct ids and csr.values their summed rows (first U = d_nunique entries)."""
-    (n, cols, out_keys, out_vals, out_counts, d_nunique, row_offsets, col_indices,
-     workspace) = _lookup_outputs(ids, vals, rows, out_keys, out_vals, out_counts, d_nunique,
-                                  row_offsets, col_indices, want_col_indices, workspace)
-    check(_lib.lib().csr_from_lookups(_ptr(ids), _ptr(vals), n, rows, cols, _ptr(out_keys),
-                                      _ptr(out_vals), _ptr(out_counts), _ptr(d_nunique),
-                                      _ptr(row_offsets), _ptr(col_indices), _ptr(workspace),
-                                      workspace.numel(), _stream(stream), _flags(validate)))
+    with _alloc_on(stream):
+        (n, cols, out_keys, out_vals, out_counts, d_nunique, row_offsets, col_indices,
+         workspace) = _lookup_outputs(ids, vals, rows, out_keys, out_vals, out_counts, d_nunique,
+                                      row_offsets, col_indices, want_col_indices, workspace)
+        check(_lib.lib().csr_from_lookups(_ptr(ids), _ptr(vals), n, rows, cols, _ptr(out_keys),
+                                          _ptr(out_vals), _ptr(out_counts), _ptr(d_nunique),
+                                          _ptr(row_offsets), _ptr(col_indices), _ptr(workspace),
+                                          workspace.numel(), _stream(stream), _flags(validate)))
     csr = CsrGradient(row_offsets, col_indices, out_vals, rows, cols, touched_rows=out_keys,
                       n_touched=n, d_n_touched=d_nunique)
     return csr, out_counts, d_nunique
@@ -318,13 +350,16 @@ def sparse_step_from_lookups(h: "_Handle", ids: torch.Tensor, vals: torch.Tensor
         raise ValueError(f"vals: shape {tuple(vals.shape)}, the handle's table takes "
                          f"({n}, {h.cols})")
     vals = vals if vals.dim() == 2 else vals.view(n, h.cols)
-    (n, cols, out_keys, out_vals, out_counts, d_nunique, row_offsets, col_indices,
-     workspace) = _lookup_outputs(ids, vals, h.rows, out_keys, out_vals, out_counts, d_nunique,
-                                  row_offsets, col_indices, want_col_indices, workspace)
-    check(h._L.sparse_step_from_lookups(h._h, _ptr(ids), _ptr(vals), n, _ptr(out_keys),
-                                        _ptr(out_vals), _ptr(out_counts), _ptr(d_nunique),
-                                        _ptr(row_offsets), _ptr(col_indices), _ptr(workspace),
-                                        workspace.numel(), _stream(stream), _flags(validate)))
+    with _alloc_on(stream):
+        (n, cols, out_keys, out_vals, out_counts, d_nunique, row_offsets, col_indices,
+         workspace) = _lookup_outputs(ids, vals, h.rows, out_keys, out_vals, out_counts,
+                                      d_nunique, row_offsets, col_indices, want_col_indices,
+                                      workspace)
+        check(h._L.sparse_step_from_lookups(h._h, _ptr(ids), _ptr(vals), n, _ptr(out_keys),
+                                            _ptr(out_vals), _ptr(out_counts), _ptr(d_nunique),
+                                            _ptr(row_offsets), _ptr(col_indices),
+                                            _ptr(workspace), workspace.numel(), _stream(stream),
+                                            _flags(validate)))
     csr = CsrGradient(row_offsets, col_indices, out_vals, h.rows, cols, touched_rows=out_keys,
                       n_touched=n, d_n_touched=d_nunique)
     return csr, out_counts, d_nunique
@@ -338,6 +373,11 @@ def csr_to_coo(csr: CsrGradient, *, out_indices=None, out_values=None, nnz: int 
     dev = csr.row_offsets.device
     if nnz is None:
         nnz = int(csr.row_offsets[csr.rows].item())
+    with _alloc_on(stream):
+        return _csr_to_coo(csr, c, dev, out_indices, out_values, nnz, stream, validate)
+
+
+def _csr_to_coo(csr, c, dev, out_indices, out_values, nnz, stream, validate):
     if out_indices is None:
         out_indices = torch.empty(max(nnz, 1), dtype=torch.int64, device=dev)
     if out_values is None:
@@ -414,7 +454,8 @@ def read_rows(params: torch.Tensor, indices: torch.Tensor, *, out=None, stream=N
     _need(indices, torch.int64, "indices")
     n = indices.numel()
     if out is None:
-        out = torch.empty((n, cols), dtype=torch.float32, device=indices.device)
+        with _alloc_on(stream):
+            out = torch.empty((n, cols), dtype=torch.float32, device=indices.device)
     _need(out, torch.float32, "out", n * cols)
     check(_lib.lib().read_rows(_ptr(params), rows, cols, _ptr(indices), n, _ptr(out),
                                _stream(stream), _flags(validate)))

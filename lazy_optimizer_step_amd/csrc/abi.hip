@@ -1,4 +1,4 @@
-// abi.cpp - the optimizer handle, error reporting and the step entry points of
+// abi.hip - the optimizer handle, error reporting and the step entry points of
 // the C ABI declared in sparse_opt.h.
 //
 // The handle holds the configuration and the global step t (optirs_gpu

@@ -57,8 +57,10 @@ constexpr uint32_t kLbCount = (1u << 30) - 1u;
 // Tiles are numbered by an atomic ticket, in the order blocks start, so a
 // tile waits only for tiles that are already running and publish their own
 // counts before they wait on anybody; the bound only turns a bug into a
-// reported error instead of a hang.
-constexpr uint32_t kSpinLimit = 1u << 16;
+// reported error instead of a hang.  Each round of a wait is a device-scope
+// load (about a microsecond) and a short sleep, so 2^20 rounds outlast any
+// plausible descheduling of the awaited block (about a second).
+constexpr uint32_t kSpinLimit = 1u << 20;
 // The pack kernel: at most this many blocks, each counting the digits of its
 // share of the lookups into its own histograms (plain stores, nothing to zero
 // beforehand); every radix pass sums them.  kPackIpt lookups per thread are

@@ -109,7 +109,7 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 __host__ __device__ inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-// Status-word helpers implemented in abi.cpp.
+// Status-word helpers implemented in abi.hip.
 int status_to_code(uint32_t bits, const char* what);
 std::mutex& validation_mutex();
 uint32_t* device_status_block();  // 4 words per device, allocated on first use

@@ -342,3 +342,58 @@ def test_two_tables_on_two_streams():
         torch.cuda.synchronize()
         runs[mode] = [[host(x).tobytes() for x in (t.params, t.m, t.v, t.last_step)] for t in tabs]
     assert runs["sequential"] == runs["concurrent"]
+
+
+def test_stream_argument_not_current_keeps_its_workspace():
+    """stream= given without making it current: the binding allocates the call's
+    workspace and outputs on that stream, so memory the current stream allocates
+    and overwrites right after the call is never the memory the call's kernels
+    (held back behind a bounded spin on their stream) still use.  Results equal
+    the same calls on the current stream, bit for bit: the one-call step (stream
+    as a torch.cuda.Stream) and coo_from_lookups (stream as a raw handle)."""
+    import synth
+    w = synth.WORKLOADS[3].scaled(rows=300_000, n_lookups=30000)
+    batches = [synth.lookups(w, s) for s in range(4)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    torch.cuda._sleep(1 << 20)
+    e1.record()
+    torch.cuda.synchronize()
+    hold = int((1 << 20) * 3.0 / max(e0.elapsed_time(e1), 1e-3))  # about 3 ms
+    nbytes = L.sparse_opt_workspace_size(w.n_lookups, w.cols, w.rows)
+    runs = {}
+    for mode in ("current", "other"):
+        t = L.SparseAdam(dev(synth.init_params(w)), mode="dormancy")
+        side = torch.cuda.Stream()
+        outs = []
+        for ids, g in batches:
+            di, dg = dev(ids), dev(g)
+            if mode == "current":
+                csr, counts, U = t.step_lookups(di, dg)
+                keys, sums, cnt, u = L.coo_from_lookups(di, dg, w.rows)
+            else:
+                side.wait_stream(torch.cuda.current_stream())  # inputs copied
+                with torch.cuda.stream(side):
+                    torch.cuda._sleep(hold)
+                csr, counts, U = t.step_lookups(di, dg, stream=side)
+                junk = [torch.full((nbytes // 4 + 4096,), float("nan"), device="cuda")
+                        for _ in range(3)]
+                with torch.cuda.stream(side):
+                    torch.cuda._sleep(hold)
+                keys, sums, cnt, u = L.coo_from_lookups(di, dg, w.rows, stream=side.cuda_stream)
+                junk += [torch.full((nbytes // 4 + 4096,), float("nan"), device="cuda")
+                         for _ in range(3)]
+                for x in (di, dg):
+                    x.record_stream(side)
+            outs.append((csr.touched_rows, csr.values, counts, U, keys, sums, cnt, u))
+        torch.cuda.synchronize()
+        res = []
+        for o in outs:
+            n = int(host(o[3])[0])
+            assert n == int(host(o[7])[0])
+            res.append([host(o[0])[:n].tobytes(), host(o[1])[:n].tobytes(),
+                        host(o[2])[:n].tobytes(), host(o[4])[:n].tobytes(),
+                        host(o[5])[:n].tobytes(), host(o[6])[:n].tobytes()])
+        res.append([host(x).tobytes() for x in (t.params, t.m, t.v, t.last_step)])
+        runs[mode] = res
+    assert runs["current"] == runs["other"]
