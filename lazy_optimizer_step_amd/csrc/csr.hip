@@ -7,9 +7,14 @@
 //
 // row_offsets is built without a global scan: a block owns a run of
 // consecutive entries of row_offsets, finds the range of COO entries that fall
-// into its rows with one block-wide search for both ends over the sorted
-// indices, counts entries per row in LDS and scans the counts locally (the
-// full-row blocks are in csr_full.hpp).
+// into its rows, counts entries per row in LDS and scans the counts locally
+// (the full-row blocks are in csr_full.hpp).  For scalar entries (width 1)
+// the kernel that writes the column of every entry also writes the first
+// row_offsets entry of every block (the number of entries in the rows below
+// it: entry k writes it for the blocks whose first row lies after the row of
+// entry k - 1 and at or before its own), so the row blocks read their range
+// instead of searching for it; a full-row COO's blocks search its row ids
+// once each.
 #include "common.hpp"
 #include "csr_full.hpp"
 
@@ -19,9 +24,12 @@ constexpr int kRoRows = 4096;  // row_offsets entries per block
 constexpr int kRoPer = kRoRows / kRoThreads;
 constexpr int kRoBatch = 8;    // index loads in flight per thread while counting
 
+// bounds_in_place: row_offsets[r0] and row_offsets[r1] (r1 <= rows) already
+// hold the block's entry range, written by k_scalar_cols; the block writes
+// row_offsets[r0] again with the same value.
 __global__ __launch_bounds__(kRoThreads) void k_row_offsets(
     const int64_t* __restrict__ idx, const int64_t* d_nnz, int64_t nnz_host, int64_t rows,
-    int64_t cols, int64_t width, int32_t* __restrict__ row_offsets) {
+    int64_t cols, int64_t width, int32_t* __restrict__ row_offsets, int bounds_in_place) {
     __shared__ uint32_t red[kRoThreads / kWave][4];
     __shared__ uint32_t cnt[kRoRows];
     __shared__ uint32_t wt[kRoThreads / kWave];
@@ -30,8 +38,19 @@ __global__ __launch_bounds__(kRoThreads) void k_row_offsets(
     const int64_t r1 = (r0 + kRoRows < rows + 1) ? r0 + kRoRows : rows + 1;
     const int64_t scale = (width == 1) ? cols : 1;  // entries of row r have keys < (r+1)*scale
     for (int i = threadIdx.x; i < kRoRows; i += kRoThreads) cnt[i] = 0;
-    const Bounds2 bd = block_lower_bounds2(idx, nnz_host, nnz, r0 * scale, r1 * scale, red);
-    const int64_t ka = bd.b0, kb = bd.b1;
+    int64_t ka, kb;
+    if (bounds_in_place) {
+        // Clamped to [0, nnz], so malformed trusted input never reads outside idx.
+        const int64_t a = row_offsets[r0];
+        const int64_t b = r1 <= rows ? (int64_t)row_offsets[r1] : nnz;
+        ka = a < 0 ? 0 : (a > nnz ? nnz : a);
+        kb = b < ka ? ka : (b > nnz ? nnz : b);
+        __syncthreads();  // every thread has read row_offsets[r0] before it is written again
+    } else {
+        const Bounds2 bd = block_lower_bounds2(idx, nnz_host, nnz, r0 * scale, r1 * scale, red);
+        ka = bd.b0;
+        kb = bd.b1;
+    }
     // For canonical input every entry in [ka, kb) lies in rows [r0, r1); the
     // bound test only keeps malformed trusted input inside the LDS array.
     // kRoBatch loads per thread are issued before any is used: a block of the
@@ -110,15 +129,37 @@ __global__ void k_full_cols(int32_t* __restrict__ ci, const int64_t* d_nnz, int6
     }
 }
 
-// Scalar COO over the flattened view: column of every entry, values copied.
+// Scalar COO over the flattened view: column of every entry, values copied,
+// and the first row_offsets entry of every kRoRows-row block: entry k is the
+// first entry at or past row b * kRoRows for every block b whose first row
+// lies in (row of entry k - 1, row of entry k]; the blocks past the last
+// entry's row (all blocks when there is none) hold nnz and are spread over
+// every thread of the grid.
 __global__ void k_scalar_cols(const int64_t* __restrict__ idx, const float* __restrict__ vin,
-                              const int64_t* d_nnz, int64_t nnz_host, int64_t cols,
-                              int32_t* __restrict__ ci, float* __restrict__ vout) {
+                              const int64_t* d_nnz, int64_t nnz_host, int64_t rows, int64_t cols,
+                              int32_t* __restrict__ ci, float* __restrict__ vout,
+                              int32_t* __restrict__ row_offsets) {
     const int64_t nnz = d_nnz ? (*d_nnz < nnz_host ? *d_nnz : nnz_host) : nnz_host;
-    for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < nnz;
-         k += (int64_t)gridDim.x * blockDim.x) {
-        if (ci) ci[k] = (int32_t)(idx[k] % cols);
+    const int64_t nblk = rows / kRoRows;  // blocks 0..nblk start at rows <= rows
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t gstride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t xl = nnz > 0 ? idx[nnz - 1] : -1;
+    const int64_t after = xl < 0 ? 0 : (xl / cols) / kRoRows + 1;  // first block past the last row
+    for (int64_t b = after + gid; b <= nblk; b += gstride)
+        row_offsets[b * kRoRows] = (int32_t)(nnz > 0 ? nnz : 0);
+    for (int64_t k = gid; k < nnz; k += gstride) {
+        const int64_t x = idx[k];
+        const int64_t xp = k > 0 ? idx[k - 1] : -1;
+        if (ci) ci[k] = (int32_t)(x % cols);
         if (vout) vout[k] = vin[k];
+        // Rows as floor(x / cols); -1 below the first entry (or for a negative
+        // index, which a trusted caller promises not to pass).
+        const int64_t row = x < 0 ? -1 : x / cols;
+        const int64_t rowp = xp < 0 ? -1 : xp / cols;
+        int64_t b0 = rowp < 0 ? 0 : rowp / kRoRows + 1;
+        int64_t b1 = row < 0 ? -1 : row / kRoRows;
+        if (b1 > nblk) b1 = nblk;
+        for (int64_t b = b0; b <= b1; ++b) row_offsets[b * kRoRows] = (int32_t)k;
     }
 }
 
@@ -351,15 +392,25 @@ extern "C" int csr_from_coo(const spopt_coo* in, int64_t rows, int64_t cols,
             k_csr_full<false><<<(unsigned)(nblk_ci + nblk_ro), kRoThreads, 0, st>>>(
                 in->indices, in->d_nnz, in->nnz, rows, cols, row_offsets, nblk_ci, col_indices);
         SPOPT_LAUNCHED();
-    } else {
+    } else if (full) {
         k_row_offsets<<<(unsigned)ceil_div(rows + 1, kRoRows), kRoThreads, 0, st>>>(
-            in->indices, in->d_nnz, in->nnz, rows, cols, in->width, row_offsets);
+            in->indices, in->d_nnz, in->nnz, rows, cols, in->width, row_offsets, 0);
         SPOPT_LAUNCHED();
-        if (full && col_indices) {
+        if (col_indices) {
             k_full_cols<<<grid_for(in->nnz * cols / 4 + 1, 256), 256, 0, st>>>(
                 col_indices, in->d_nnz, in->nnz, cols);
             SPOPT_LAUNCHED();
         }
+    } else {
+        // Scalar entries: columns, values and the row blocks' first offsets,
+        // then the row blocks.
+        k_scalar_cols<<<grid_for(in->nnz, 256), 256, 0, st>>>(
+            in->indices, in->values, in->d_nnz, in->nnz, rows, cols, col_indices,
+            values == in->values ? nullptr : values, row_offsets);
+        SPOPT_LAUNCHED();
+        k_row_offsets<<<(unsigned)ceil_div(rows + 1, kRoRows), kRoThreads, 0, st>>>(
+            in->indices, in->d_nnz, in->nnz, rows, cols, in->width, row_offsets, 1);
+        SPOPT_LAUNCHED();
     }
     if (full) {
         if (values && values != in->values) {
@@ -374,11 +425,6 @@ extern "C" int csr_from_coo(const spopt_coo* in, int64_t rows, int64_t cols,
                 in->nnz, d_n_touched == in->d_nnz ? nullptr : d_n_touched);
             SPOPT_LAUNCHED();
         }
-    } else {
-        k_scalar_cols<<<grid_for(in->nnz, 256), 256, 0, st>>>(
-            in->indices, in->values, in->d_nnz, in->nnz, cols, col_indices,
-            values == in->values ? nullptr : values);
-        SPOPT_LAUNCHED();
     }
     return SPOPT_OK;
 }
