@@ -371,6 +371,29 @@ SPOPT_API int sparse_step_from_lookups(spopt_t h, const int64_t* ids, const floa
                                        int32_t* col_indices, void* workspace,
                                        size_t workspace_bytes, void* stream, uint32_t flags);
 
+/* The same step for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * sparse_step_from_lookups without the workspace arguments, its workspace
+ * being a fixed 16 MiB array in the library's device data (one copy per GPU,
+ * held until the process ends; about 2 MiB is needed for 65,536 lookups of
+ * 128 columns on a 10M-row table, 8.2 MiB for 262,144 lookups on 50M rows).
+ * The call allocates nothing (no hipMalloc, no allocating library routine).
+ * The caller still passes every input and output.  Every call on a GPU uses
+ * that GPU's one array, which keeps the last call's contents (the
+ * canonicalisation clears what it accumulates into, so nothing needs
+ * clearing beforehand): calls that overlap in time on one GPU, e.g. on two
+ * streams without an ordering between them, race and give wrong results.
+ * Trusted mode only.
+ * Errors: those of sparse_step_from_lookups; SPOPT_EINVAL for SPOPT_VALIDATE
+ * or a bad n; SPOPT_EWORKSPACE, before any device work, when the lookups
+ * need more scratch than the array holds (sparse_opt_workspace_size(n, cols,
+ * rows) > 16 MiB). */
+SPOPT_API int sparse_step_from_lookups_noalloc(spopt_t h, const int64_t* ids, const float* vals,
+                                               int64_t n, int64_t* out_keys, float* out_vals,
+                                               int32_t* out_counts, int64_t* d_nunique,
+                                               int32_t* row_offsets, int32_t* col_indices,
+                                               void* stream, uint32_t flags);
+
 /* ---- forward gather ----------------------------------------------------- */
 
 /* DiskSparseAdam README, API reference, read_rows(indices): the current rows of

@@ -28,6 +28,7 @@ from ._lib import (FORMAT_COO, FORMAT_CSR, KIND_ADAM, KIND_SGD, MODE_DORMANCY, M
 __all__ = ["coo_from_lookups", "csr_from_coo", "csr_from_lookups", "csr_to_coo",
            "sparse_opt_workspace_size",
            "sparse_opt_create", "sparse_adam_step", "sparse_sgd_step", "sparse_step_from_lookups",
+           "sparse_step_from_lookups_noalloc",
            "set_step_events",
            "CooGradient",
            "CsrGradient", "SparseAdam", "SparseSgd", "SparseOptError", "TRUSTED", "VALIDATE",
@@ -363,6 +364,29 @@ def sparse_step_from_lookups(h: "_Handle", ids: torch.Tensor, vals: torch.Tensor
     csr = CsrGradient(row_offsets, col_indices, out_vals, h.rows, cols, touched_rows=out_keys,
                       n_touched=n, d_n_touched=d_nunique)
     return csr, out_counts, d_nunique
+
+
+def sparse_step_from_lookups_noalloc(h: "_Handle", ids: torch.Tensor, vals: torch.Tensor, *,
+                                     out_keys, out_vals, out_counts, d_nunique, row_offsets,
+                                     col_indices=None, stream=None) -> None:
+    """sparse_step_from_lookups for callers that cannot allocate: no workspace
+    argument (the library's fixed device scratch serves instead) and nothing
+    allocated here either, so every output must be given.  Trusted mode only;
+    calls that overlap in time on one GPU race on the shared scratch."""
+    n = ids.numel()
+    _need(ids, torch.int64, "ids")
+    _need(vals, torch.float32, "vals", n * h.cols)
+    _need(out_keys, torch.int64, "out_keys", n)
+    _need(out_vals, torch.float32, "out_vals", n * h.cols)
+    _need(out_counts, torch.int32, "out_counts", n)
+    _need(d_nunique, torch.int64, "d_nunique", 1)
+    _need(row_offsets, torch.int32, "row_offsets", h.rows + 1)
+    if col_indices is not None:
+        _need(col_indices, torch.int32, "col_indices", n * h.cols)
+    check(h._L.sparse_step_from_lookups_noalloc(h._h, _ptr(ids), _ptr(vals), n, _ptr(out_keys),
+                                                _ptr(out_vals), _ptr(out_counts),
+                                                _ptr(d_nunique), _ptr(row_offsets),
+                                                _ptr(col_indices), _stream(stream), TRUSTED))
 
 
 def csr_to_coo(csr: CsrGradient, *, out_indices=None, out_values=None, nnz: int | None = None,

@@ -107,6 +107,8 @@ def lib() -> C.CDLL:
         L.sparse_step_from_lookups.argtypes = [P, P, P, I64, P, P, P, P, P, P, P, C.c_size_t, P,
                                                U32]
         L.sparse_step_from_lookups.restype = C.c_int
+        L.sparse_step_from_lookups_noalloc.argtypes = [P, P, P, I64, P, P, P, P, P, P, P, U32]
+        L.sparse_step_from_lookups_noalloc.restype = C.c_int
         L.sparse_opt_set_step_events.argtypes = [P, P]
         L.sparse_opt_set_step_events.restype = C.c_int
         _lib = L
@@ -121,5 +123,6 @@ def check(rc: int) -> None:
 EXPORTED = ("sparse_opt_create", "sparse_opt_destroy", "sparse_opt_get_step", "sparse_opt_set_step",
             "sparse_opt_last_error", "sparse_opt_workspace_size", "coo_from_lookups",
             "csr_from_coo", "csr_from_lookups", "csr_to_coo", "sparse_adam_step",
-            "sparse_sgd_step", "sparse_step_from_lookups", "sparse_opt_set_step_events", "read_rows",
+            "sparse_sgd_step", "sparse_step_from_lookups", "sparse_step_from_lookups_noalloc",
+            "sparse_opt_set_step_events", "read_rows",
             "sparse_opt_host_alloc", "sparse_opt_host_free", "sparse_opt_host_device_pointer")

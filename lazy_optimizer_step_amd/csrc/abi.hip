@@ -429,3 +429,62 @@ extern "C" int sparse_step_from_lookups(spopt_t h, const int64_t* ids, const flo
     h->t = t;
     return SPOPT_OK;
 }
+
+// ---- the step from raw lookups without a workspace argument ---------------
+
+// The canonicalisation workspace of sparse_step_from_lookups_noalloc: a
+// file-scope device array, one copy on every GPU the library runs on, held
+// until the process ends.  Host code never uses this name as an address: the
+// device address of each GPU's copy is looked up once, with that GPU current,
+// and kept (scratch_address).
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+static int scratch_address(void** out) {
+    static std::mutex mu;
+    static std::vector<void*> addr;
+    int dev = -1;
+    SPOPT_HIP(hipGetDevice(&dev));
+    if (dev < 0) return fail(SPOPT_EDEVICE, "sparse_step_from_lookups_noalloc: no current device");
+    std::lock_guard<std::mutex> guard(mu);
+    if ((size_t)dev >= addr.size()) addr.resize((size_t)dev + 1, nullptr);
+    if (addr[(size_t)dev] == nullptr) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr)
+            return fail(SPOPT_EDEVICE,
+                        "sparse_step_from_lookups_noalloc: device address of the scratch array: %s",
+                        hipGetErrorString(e));
+        addr[(size_t)dev] = p;
+    }
+    *out = addr[(size_t)dev];
+    return SPOPT_OK;
+}
+
+extern "C" int sparse_step_from_lookups_noalloc(spopt_t h, const int64_t* ids, const float* vals,
+                                                int64_t n, int64_t* out_keys, float* out_vals,
+                                                int32_t* out_counts, int64_t* d_nunique,
+                                                int32_t* row_offsets, int32_t* col_indices,
+                                                void* stream, uint32_t flags) {
+    const char* what = "sparse_step_from_lookups_noalloc";
+    if (h == nullptr) return fail(SPOPT_EINVAL, "%s: NULL handle", what);
+    if (flags & SPOPT_VALIDATE)
+        return fail(SPOPT_EINVAL, "%s: trusted calls only (validation allocates a status block)",
+                    what);
+    size_t need = 0;
+    if (sparse_opt_workspace_size(n, h->cols, h->rows, &need) != SPOPT_OK)
+        return fail(SPOPT_EINVAL, "%s: bad n=%lld for a %lld x %lld table", what, (long long)n,
+                    (long long)h->rows, (long long)h->cols);
+    if (need > kNoAllocScratchBytes)
+        return fail(SPOPT_EWORKSPACE,
+                    "%s: %lld lookups on a %lld x %lld table need %zu bytes of scratch; the "
+                    "fixed scratch holds %zu (use sparse_step_from_lookups with a workspace)",
+                    what, (long long)n, (long long)h->rows, (long long)h->cols, need,
+                    kNoAllocScratchBytes);
+    void* ws = nullptr;
+    const int rc = scratch_address(&ws);
+    if (rc) return rc;
+    return sparse_step_from_lookups(h, ids, vals, n, out_keys, out_vals, out_counts, d_nunique,
+                                    row_offsets, col_indices, ws, kNoAllocScratchBytes, stream,
+                                    flags);
+}

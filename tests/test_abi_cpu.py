@@ -145,6 +145,32 @@ def test_step_from_lookups_host_errors():
     assert ev(None, None) == _lib.OK
 
 
+def test_step_from_lookups_noalloc_host_errors():
+    """The allocation-free step refuses, before any device work: a NULL handle,
+    validated calls, and lookups whose workspace exceeds its fixed 16 MiB."""
+    L_ = _lib.lib()
+    f = L_.sparse_step_from_lookups_noalloc
+    assert f(None, FAKE, FAKE, 10, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0) == _lib.EINVAL
+    h = C.c_void_p()
+    cfg = _lib.SgdConfig(0.1, 0.0, 0.0)
+    rows, cols = 1000, 1024
+    assert L_.sparse_opt_create(C.byref(h), _lib.KIND_SGD, C.byref(cfg), rows, cols, FAKE, None,
+                                None, None) == 0
+    try:
+        args = lambda n, flags=0: (h, FAKE, FAKE, n, FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
+                                   flags)
+        assert f(*args(10, _lib.VALIDATE)) == _lib.EINVAL
+        assert b"trusted" in L_.sparse_opt_last_error()
+        assert f(*args(-1)) == _lib.EINVAL
+        big = 200_000
+        assert L.sparse_opt_workspace_size(big, cols, rows) > 16 << 20
+        assert f(*args(big)) == _lib.EWORKSPACE
+        assert b"16777216" in L_.sparse_opt_last_error()
+        assert L_.sparse_opt_get_step(h) == 0
+    finally:
+        L_.sparse_opt_destroy(h)
+
+
 def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True)
