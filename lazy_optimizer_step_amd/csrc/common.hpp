@@ -91,6 +91,34 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Division of unsigned 64-bit integers by a divisor fixed for a launch,
+// without the GPU's long software division: with s = floor(log2 d) and
+// m = floor((2^(64+s) - 1) / d), formed on the host, the estimate
+// q = high64(n * m) >> s falls short of floor(n / d) by at most 1 for every
+// n < 2^64 (m * 2^-(64+s) undershoots 1/d by less than 2^-(64+s)), so one
+// correction step gives the exact quotient.
+struct FastDiv {
+    uint64_t d, m;
+    int s;
+    static FastDiv make(uint64_t d) {
+        FastDiv f;
+        f.d = d;
+        f.s = 63 - __builtin_clzll(d);
+        f.m = (uint64_t)((((unsigned __int128)1 << (64 + f.s)) - 1) / d);
+        return f;
+    }
+    __device__ __forceinline__ uint64_t div(uint64_t n, uint64_t* rem = nullptr) const {
+        uint64_t q = __umul64hi(n, m) >> s;
+        uint64_t r = n - q * d;
+        if (r >= d) {
+            ++q;
+            r -= d;
+        }
+        if (rem) *rem = r;
+        return q;
+    }
+};
+
 // ------------------------------------------------------------------ host ---
 
 void set_error(const char* fmt, ...);

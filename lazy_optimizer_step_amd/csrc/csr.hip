@@ -29,7 +29,8 @@ constexpr int kRoBatch = 8;    // index loads in flight per thread while countin
 // row_offsets[r0] again with the same value.
 __global__ __launch_bounds__(kRoThreads) void k_row_offsets(
     const int64_t* __restrict__ idx, const int64_t* d_nnz, int64_t nnz_host, int64_t rows,
-    int64_t cols, int64_t width, int32_t* __restrict__ row_offsets, int bounds_in_place) {
+    int64_t cols, int64_t width, int32_t* __restrict__ row_offsets, int bounds_in_place,
+    FastDiv by_cols) {
     __shared__ uint32_t red[kRoThreads / kWave][4];
     __shared__ uint32_t cnt[kRoRows];
     __shared__ uint32_t wt[kRoThreads / kWave];
@@ -69,7 +70,7 @@ __global__ __launch_bounds__(kRoThreads) void k_row_offsets(
                 const int64_t o = x[j] - r0;
                 if (live && (uint64_t)o < (uint64_t)kRoRows) cnt[o] = 1u;
             } else {
-                const int64_t o = (x[j] < 0 ? -1 : x[j] / scale - r0);
+                const int64_t o = (x[j] < 0 ? -1 : (int64_t)by_cols.div((uint64_t)x[j]) - r0);
                 if (live && (uint64_t)o < (uint64_t)kRoRows) atomicAdd(&cnt[o], 1u);
             }
         }
@@ -136,7 +137,7 @@ __global__ void k_full_cols(int32_t* __restrict__ ci, const int64_t* d_nnz, int6
 // entry's row (all blocks when there is none) hold nnz and are spread over
 // every thread of the grid.
 __global__ void k_scalar_cols(const int64_t* __restrict__ idx, const float* __restrict__ vin,
-                              const int64_t* d_nnz, int64_t nnz_host, int64_t rows, int64_t cols,
+                              const int64_t* d_nnz, int64_t nnz_host, int64_t rows, FastDiv by_cols,
                               int32_t* __restrict__ ci, float* __restrict__ vout,
                               int32_t* __restrict__ row_offsets) {
     const int64_t nnz = d_nnz ? (*d_nnz < nnz_host ? *d_nnz : nnz_host) : nnz_host;
@@ -144,18 +145,20 @@ __global__ void k_scalar_cols(const int64_t* __restrict__ idx, const float* __re
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t gstride = (int64_t)gridDim.x * blockDim.x;
     const int64_t xl = nnz > 0 ? idx[nnz - 1] : -1;
-    const int64_t after = xl < 0 ? 0 : (xl / cols) / kRoRows + 1;  // first block past the last row
+    // first block past the last row
+    const int64_t after = xl < 0 ? 0 : (int64_t)by_cols.div((uint64_t)xl) / kRoRows + 1;
     for (int64_t b = after + gid; b <= nblk; b += gstride)
         row_offsets[b * kRoRows] = (int32_t)(nnz > 0 ? nnz : 0);
     for (int64_t k = gid; k < nnz; k += gstride) {
         const int64_t x = idx[k];
         const int64_t xp = k > 0 ? idx[k - 1] : -1;
-        if (ci) ci[k] = (int32_t)(x % cols);
-        if (vout) vout[k] = vin[k];
         // Rows as floor(x / cols); -1 below the first entry (or for a negative
         // index, which a trusted caller promises not to pass).
-        const int64_t row = x < 0 ? -1 : x / cols;
-        const int64_t rowp = xp < 0 ? -1 : xp / cols;
+        uint64_t col = 0;
+        const int64_t row = x < 0 ? -1 : (int64_t)by_cols.div((uint64_t)x, &col);
+        const int64_t rowp = xp < 0 ? -1 : (int64_t)by_cols.div((uint64_t)xp);
+        if (ci) ci[k] = x < 0 ? -1 : (int32_t)col;
+        if (vout) vout[k] = vin[k];
         int64_t b0 = rowp < 0 ? 0 : rowp / kRoRows + 1;
         int64_t b1 = row < 0 ? -1 : row / kRoRows;
         if (b1 > nblk) b1 = nblk;
@@ -394,7 +397,8 @@ extern "C" int csr_from_coo(const spopt_coo* in, int64_t rows, int64_t cols,
         SPOPT_LAUNCHED();
     } else if (full) {
         k_row_offsets<<<(unsigned)ceil_div(rows + 1, kRoRows), kRoThreads, 0, st>>>(
-            in->indices, in->d_nnz, in->nnz, rows, cols, in->width, row_offsets, 0);
+            in->indices, in->d_nnz, in->nnz, rows, cols, in->width, row_offsets, 0,
+            FastDiv::make(1));
         SPOPT_LAUNCHED();
         if (col_indices) {
             k_full_cols<<<grid_for(in->nnz * cols / 4 + 1, 256), 256, 0, st>>>(
@@ -404,12 +408,13 @@ extern "C" int csr_from_coo(const spopt_coo* in, int64_t rows, int64_t cols,
     } else {
         // Scalar entries: columns, values and the row blocks' first offsets,
         // then the row blocks.
+        const FastDiv by_cols = FastDiv::make((uint64_t)cols);
         k_scalar_cols<<<grid_for(in->nnz, 256), 256, 0, st>>>(
-            in->indices, in->values, in->d_nnz, in->nnz, rows, cols, col_indices,
+            in->indices, in->values, in->d_nnz, in->nnz, rows, by_cols, col_indices,
             values == in->values ? nullptr : values, row_offsets);
         SPOPT_LAUNCHED();
         k_row_offsets<<<(unsigned)ceil_div(rows + 1, kRoRows), kRoThreads, 0, st>>>(
-            in->indices, in->d_nnz, in->nnz, rows, cols, in->width, row_offsets, 1);
+            in->indices, in->d_nnz, in->nnz, rows, cols, in->width, row_offsets, 1, by_cols);
         SPOPT_LAUNCHED();
     }
     if (full) {

@@ -138,3 +138,19 @@ def test_flat_update_full_rows_without_columns():
     assert_state_close(host(gpu.params), ora.p, "params")
     assert_state_close(host(gpu.m), ora.m, "m")
     assert_state_close(host(gpu.v), ora.v, "v")
+
+
+@pytest.mark.parametrize("pattern", ["gaps", "last_row", "first_row", "one_row"])
+def test_csr_from_flat_coo_indices_beyond_32_bits(pattern):
+    """A 40M x 128 view: linear indices up to 5.1e9, so row and column come
+    from 64-bit division by the column count."""
+    rows, cols = 40_000_001, 128
+    rng = np.random.default_rng(11)
+    lin = _entries(rng, rows, cols, pattern)
+    lin = np.unique(np.r_[lin, (rows - 3) * cols + 5, 2**32 + 7]).astype(np.int64)
+    vals = rng.standard_normal(lin.size).astype(np.float32)
+    ro, ci, cv = oracle.csr_from_coo(lin, vals, rows * cols, 1, rows, cols)
+    csr = L.csr_from_coo(L.CooGradient(dev(lin), dev(vals), dim=rows * cols, width=1), rows, cols)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(csr.row_offsets), ro)
+    assert np.array_equal(host(csr.col_indices)[:lin.size], ci)
