@@ -717,7 +717,7 @@ def run_partial(args, kind: str) -> dict:
     nz = nnz[W:]
     upd_bytes = (PARTIAL_BYTES_PER_NNZ[kind] + PARTIAL_COL_BYTES) * nz + 4 * (R + 1)
     op = "SgdOp<momentum>" if kind == "sgd" else "AdamOp<DormancyDecay, no decay, last_step per coordinate>"
-    kernel = f"k_update_csr_flat<{op}>"
+    kernel = f"k_update_csr_scan<{op}>"
     metric = METRIC.replace("10M x 128 table", f"2M x {Cc} table, partial rows")
     result = result_head(w, K, W, total_ms, int(nz.sum()), metric)
     result["config"] = {"workload": w.name, "rows": R, "cols": Cc,

@@ -82,15 +82,6 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, uint32_t* warp_t
 
 __device__ __forceinline__ bool finite_f(float x) { return __builtin_isfinite(x); }
 
-// Orders one wave's LDS writes before its later LDS reads by other lanes of the
-// same wave (no block barrier: the waves of a block may run different numbers
-// of iterations).
-__device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 // Division of unsigned 64-bit integers by a divisor fixed for a launch,
 // without the GPU's long software division: with s = floor(log2 d) and
 // m = floor((2^(64+s) - 1) / d), formed on the host, the estimate

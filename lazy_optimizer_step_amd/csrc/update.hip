@@ -24,11 +24,10 @@
 // a batch of ITERS such groups per wave.  A full row (all cols entries
 // present) is moved with 16-byte loads and stores of p, m, v, last_step and g;
 // a partial row uses one lane per entry.  Rows come from a touched-row list
-// (CSR) or the keys of a full-row COO; without a list the CSR kernel takes
-// runs of rows from row_offsets and one lane per entry (k_update_csr_flat).
-// The step from raw lookups takes its rows from the canonicalisation's
-// segments and shares one launch with the tile combine and the CSR blocks
-// (k_step_lookups).
+// (CSR) or the keys of a full-row COO; without a list the CSR kernel scans
+// row_offsets 64 rows per wave.  The step from raw lookups takes its rows from
+// the canonicalisation's segments and shares one launch with the tile combine
+// and the CSR blocks (k_step_lookups).
 #include <hip/hip_ext.h>
 
 #include "common.hpp"
@@ -167,36 +166,6 @@ struct AdamOp {
         v[i] = vv;
         if (!LSROW) ls[i] = a.t;
     }
-    // scalar() in phases, so that a lane's loads for several coordinates can be
-    // in flight together: sload (state), sprep (beta^gap from the table), then
-    // sfinish (the same arithmetic, and the stores).
-    struct S {
-        float p, m, v;
-        int32_t last;
-        double t1, t2;
-    };
-    __device__ __forceinline__ void sload(int64_t i, int32_t rl, S& x) const {
-        x.p = p[i];
-        x.m = m[i];
-        x.v = v[i];
-        x.last = (MODE != SPOPT_MODE_DORMANCY) ? 0 : (LSROW ? rl : ls[i]);
-    }
-    __device__ __forceinline__ void sprep(S& x) const {
-        x.t1 = 1.0;
-        x.t2 = 1.0;
-        if (MODE == SPOPT_MODE_DORMANCY) {
-            const int k = table_index(x.last);
-            x.t1 = a.pow1[k];
-            x.t2 = a.pow2[k];
-        }
-    }
-    __device__ __forceinline__ void sfinish(int64_t i, S& x, float g) const {
-        coord(x.p, x.m, x.v, x.last, x.t1, x.t2, g);
-        p[i] = x.p;
-        m[i] = x.m;
-        v[i] = x.v;
-        if (!LSROW) ls[i] = a.t;
-    }
 };
 
 template <bool MOM>
@@ -248,19 +217,6 @@ struct SgdOp {
         coord(pp, bb, g);
         p[i] = pp;
         if (MOM) b[i] = bb;
-    }
-    struct S {
-        float p, b;
-    };
-    __device__ __forceinline__ void sload(int64_t i, int32_t, S& x) const {
-        x.p = p[i];
-        x.b = MOM ? b[i] : 0.f;
-    }
-    __device__ __forceinline__ void sprep(S&) const {}
-    __device__ __forceinline__ void sfinish(int64_t i, S& x, float g) const {
-        coord(x.p, x.b, g);
-        p[i] = x.p;
-        if (MOM) b[i] = x.b;
     }
 };
 
@@ -487,107 +443,37 @@ __global__ __launch_bounds__(256) void k_step_lookups(Op op, FusedCsr f, int64_t
     csr_row_block<true>(b - f.nblk_ci, f.keys, f.n, nnz, f.rows, f.cols, f.row_offsets, f.bnd);
 }
 
-// CSR without a touched-row list, one lane per entry.  A wave takes kFlatRows
-// consecutive rows (kFlatRPL per lane) and loads their row_offsets at once;
-// the rows' entries are then one contiguous run of the CSR, which the wave
-// works through kFlatQ entries per lane at a time: each lane finds its
-// entry's row by a binary search of the row starts (kept in LDS), and the
-// loads of all the round's entries (column and value, then state, then
-// beta^gap) are in flight together.  With one last_step per row, the row's
-// value is read once, before any of its entries, and written once, after.
-constexpr int kFlatRPL = 4;
-constexpr int kFlatRows = kWave * kFlatRPL;
-constexpr int kFlatQ = 2;
-constexpr int kFlatWaves = 4;  // waves per block
-
+// CSR without a touched-row list: one wave per 64 rows of row_offsets.
 template <class Op>
-__global__ __launch_bounds__(kFlatWaves * kWave) void k_update_csr_flat(
-    Op op, const int32_t* __restrict__ ro, const int32_t* __restrict__ ci, int64_t rows,
-    int64_t cols, const float* __restrict__ g) {
-    __shared__ int32_t s_start[kFlatWaves][kFlatRows + 1];
-    __shared__ int32_t s_last[kFlatWaves][Op::kLsRow ? kFlatRows : 1];
-    const int w = (int)(threadIdx.x >> 6);
+__global__ __launch_bounds__(256) void k_update_csr_scan(Op op, const int32_t* __restrict__ ro,
+                                                         const int32_t* __restrict__ ci,
+                                                         int64_t rows, int64_t cols,
+                                                         const float* __restrict__ g) {
     const int lane = lane_id();
-    const int32_t nnz = ro[rows];  // entries stay inside [0, nnz) even for malformed offsets
     const int64_t nw = ((int64_t)gridDim.x * blockDim.x) >> 6;
-    for (int64_t wv = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6; wv * kFlatRows < rows;
-         wv += nw) {
-        const int64_t r0 = wv * kFlatRows;
-        const int64_t rend = r0 + kFlatRows < rows ? r0 + kFlatRows : rows;
-        int32_t st[kFlatRPL];
-#pragma unroll
-        for (int j = 0; j < kFlatRPL; ++j) {
-            const int64_t r = r0 + j * kWave + lane;
-            st[j] = ro[r < rend ? r : rend];
+    const int nnz = ro[rows];  // entries stay inside [0, nnz) even for malformed offsets
+    for (int64_t tile = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+         tile * kWave < rows; tile += nw) {
+        const int64_t r = tile * kWave + lane;
+        int a = 0, b = 0;
+        if (r < rows) {
+            a = ro[r];
+            b = ro[r + 1];
         }
-        const int32_t e_end = ro[rend];
-#pragma unroll
-        for (int j = 0; j < kFlatRPL; ++j) s_start[w][j * kWave + lane] = st[j];
-        if (lane == 0) s_start[w][kFlatRows] = e_end;
-        wave_lds_sync();
-        if constexpr (Op::kLsRow) {
-            // The row's last_step before the step, for the rows that have entries.
-#pragma unroll
-            for (int j = 0; j < kFlatRPL; ++j) {
-                const int k = j * kWave + lane;
-                const bool has = r0 + k < rend && s_start[w][k + 1] > st[j];
-                s_last[w][k] = has ? op.row_last(r0 + k) : 0;
+        uint64_t mask = ballot(b > a && a >= 0 && b <= nnz);
+        while (mask) {
+            const int bit = __builtin_ctzll(mask);
+            mask &= mask - 1;
+            const int st = read_lane(a, bit), en = read_lane(b, bit);
+            const int64_t row = tile * kWave + bit;
+            const int64_t base = row * cols;
+            const int32_t rl = op.row_last(row);
+            for (int j = st + lane; j < en && j - st < cols; j += kWave) {
+                const int64_t c = ci ? (int64_t)ci[j] : (int64_t)(j - st);
+                if ((uint64_t)c < (uint64_t)cols) op.scalar(base + c, rl, g[j]);
             }
-            wave_lds_sync();
+            op.row_done(row);
         }
-        const int32_t e_begin = __builtin_amdgcn_readfirstlane(st[0]);
-        const int32_t e0 = e_begin < 0 ? 0 : e_begin;
-        const int32_t e1 = e_end > nnz ? nnz : e_end;
-        for (int32_t eb = e0; eb < e1; eb += kFlatQ * kWave) {
-            int32_t e[kFlatQ], k[kFlatQ];
-            bool ok[kFlatQ];
-#pragma unroll
-            for (int q = 0; q < kFlatQ; ++q) {
-                e[q] = eb + q * kWave + lane;
-                ok[q] = e[q] < e1;
-                if (!ok[q]) e[q] = e0;
-                // the last row whose start is at or before the entry
-                int lo = 0, hi = kFlatRows;  // s_start[lo] <= e < s_start[hi]
-                while (hi - lo > 1) {
-                    const int mid = (lo + hi) >> 1;
-                    if (s_start[w][mid] <= e[q])
-                        lo = mid;
-                    else
-                        hi = mid;
-                }
-                k[q] = lo;
-            }
-            int64_t col[kFlatQ];
-            float gv[kFlatQ];
-#pragma unroll
-            for (int q = 0; q < kFlatQ; ++q) {
-                col[q] = ci ? (int64_t)ci[e[q]] : (int64_t)(e[q] - s_start[w][k[q]]);
-                gv[q] = g[e[q]];
-            }
-            int64_t at[kFlatQ];
-            typename Op::S x[kFlatQ];
-#pragma unroll
-            for (int q = 0; q < kFlatQ; ++q) {
-                ok[q] = ok[q] && r0 + k[q] < rend && (uint64_t)col[q] < (uint64_t)cols;
-                at[q] = ok[q] ? (r0 + k[q]) * cols + col[q] : 0;
-                int32_t rl = 0;
-                if constexpr (Op::kLsRow) rl = s_last[w][k[q]];
-                op.sload(at[q], rl, x[q]);
-            }
-#pragma unroll
-            for (int q = 0; q < kFlatQ; ++q) op.sprep(x[q]);
-#pragma unroll
-            for (int q = 0; q < kFlatQ; ++q)
-                if (ok[q]) op.sfinish(at[q], x[q], gv[q]);
-        }
-        if constexpr (Op::kLsRow) {
-#pragma unroll
-            for (int j = 0; j < kFlatRPL; ++j) {
-                const int kk = j * kWave + lane;
-                if (r0 + kk < rend && s_start[w][kk + 1] > st[j]) op.row_done(r0 + kk);
-            }
-        }
-        wave_lds_sync();  // the LDS rows are rewritten for the next run of rows
     }
 }
 
@@ -714,8 +600,8 @@ static int launch_update(const Op& op, bool state_aligned, const spopt_grad* gr,
         return launch_rows(op, SrcCsrTouched{c.touched_rows, c.row_offsets, c.col_indices, rows},
                            c.d_n_touched, c.n_touched, rows, cols, c.values, vec_ok, s);
     }
-    const unsigned grid = grid_cap(ceil_div(ceil_div(rows, kFlatRows), kFlatWaves));
-    launch_update_kernel(k_update_csr_flat<Op>, grid, s, op, c.row_offsets, c.col_indices, rows,
+    const unsigned grid = grid_cap(ceil_div(ceil_div(rows, kWave), 4));
+    launch_update_kernel(k_update_csr_scan<Op>, grid, s, op, c.row_offsets, c.col_indices, rows,
                          cols, c.values);
     SPOPT_LAUNCHED();
     return SPOPT_OK;

@@ -10,8 +10,8 @@ last_step and untouched coordinates bit-exact.
 
 The CSR build writes the first offset of every 4096-row block from the entry
 that crosses into it, then fills each block from its two bounds; the update
-takes 256 rows per wave and works through their entries 128 at a time.  The
-shapes below put block and wave edges where they can go wrong.
+scans row_offsets 64 rows per wave, one lane per entry.  The shapes below put
+block and wave edges where they can go wrong.
 """
 import numpy as np
 import pytest
