@@ -75,21 +75,31 @@ CSR_BYTES_PER_COORD = 4
 CSR_BYTES_PER_ROW = 8
 CSR_BYTES_PER_TABLE_ROW = 4
 
-# HBM bytes per launch of the one-call step's last kernel (k_step_lookups) on
-# this workload, from two rocprofv3 --pmc passes of this command (FETCH_SIZE
-# scaled by 2.0 and WRITE_SIZE by 1.0: a plain 1 GiB device copy reads 512 MiB
-# by FETCH_SIZE and writes 1 GiB by WRITE_SIZE).  Valid only for the kernel
-# sources they were taken with; reported as null once those sources change.
+# HBM bytes per launch of the kernel that updates the table, from two
+# rocprofv3 --pmc passes of this command (FETCH_SIZE scaled by 2.0 and
+# WRITE_SIZE by 1.0: a plain 1 GiB device copy reads 512 MiB by FETCH_SIZE and
+# writes 1 GiB by WRITE_SIZE), keyed by (workload, step form): the one-call
+# step's k_step_lookups, the two-call step's k_update_rows, and the partial-row
+# step's k_update_csr_scan.  Valid only for the kernel sources they were taken
+# with; reported as null once those sources change.
 UPDATE_SOURCES = ("lazy_optimizer_step_amd/csrc/update.hip",
                   "lazy_optimizer_step_amd/csrc/common.hpp",
                   "lazy_optimizer_step_amd/csrc/csr_full.hpp",
                   "lazy_optimizer_step_amd/csrc/seg_combine.hpp")
-# Keyed by (workload, step form); the default line's entry is the one-call step
-# on the 10M x 128 workload.
+_SHA = "287c4ff8dc6c13aaa1d6b9356fd0ad408a4b1dd22e984540e14f3d34c3905d0f"
 TRAFFIC = {
     ("table10Mx128_zipf1.05_dormancy", "one_call"): {
-        "sources_sha256": "ec49f6071ccd114523f0160d63a848d6ddae0ae8c5bfe4f2323dfdcae4314128",
-        "fetch_bytes": 2.0 * 33446.1 * 1024, "write_bytes": 1.0 * 104296.8 * 1024},
+        "sources_sha256": _SHA, "fetch_bytes": 2.0 * 33422.9 * 1024,
+        "write_bytes": 1.0 * 104262.6 * 1024},
+    ("table10Mx128_zipf1.05_dormancy", "two_calls"): {
+        "sources_sha256": _SHA, "fetch_bytes": 2.0 * 33775.5 * 1024,
+        "write_bytes": 1.0 * 59017.2 * 1024},
+    ("table2Mx256_csr16-64_sgd", "two_calls"): {
+        "sources_sha256": _SHA, "fetch_bytes": 2.0 * 23941.2 * 1024,
+        "write_bytes": 1.0 * 23465.3 * 1024},
+    ("table2Mx256_csr16-64_dormancy", "two_calls"): {
+        "sources_sha256": _SHA, "fetch_bytes": 2.0 * 40151.7 * 1024,
+        "write_bytes": 1.0 * 46930.6 * 1024},
 }
 
 
@@ -415,7 +425,8 @@ def roofline_block(upd, upd_cold, upd_clean, upd_bytes, coords, copy_gbs, traffi
 
 
 def traffic_for(name: str, form: str):
-    t = TRAFFIC.get((name, form))
+    # the three-call step's update launch is the two-call step's, on the same CSR
+    t = TRAFFIC.get((name, "two_calls" if form == "separate_calls" else form))
     if t is None or sources_sha256() != t["sources_sha256"]:
         return None
     return t["fetch_bytes"] + t["write_bytes"]
@@ -593,6 +604,8 @@ def run_lookups(args, cfg: int) -> dict:
         rf["bound"] = "host link"
         rf["peak"] = link["host_to_device"] + link["device_to_host"]
         rf["frac"] = rf["achieved"] / rf["peak"]
+        for regime in ("cold", "cold_clean"):
+            rf[regime]["frac"] = rf[regime]["achieved"] / rf["peak"]
         rf["host_link_copy_GBs"] = link
         rf["peak_note"] = "sum of the measured pinned copy rates, each direction"
     if args.cpu_seconds > 0:
