@@ -22,12 +22,12 @@
 //
 // Work mapping: LPR lanes per touched row, 64/LPR rows per wave at a time and
 // a batch of ITERS such groups per wave.  A full row (all cols entries
-// present) is moved with 16-byte loads and stores of p, m, v, last_step and g;
-// a partial row uses one lane per entry.  Rows come from a touched-row list
-// (CSR) or the keys of a full-row COO; without a list the CSR kernel scans
-// row_offsets 64 rows per wave.  The step from raw lookups takes its rows from
-// the canonicalisation's segments and shares one launch with the tile combine
-// and the CSR blocks (k_step_lookups).
+// present) is moved with 16-byte loads and stores of p, m, v, last_step and g
+// (nontemporal for the Adam state); a partial row uses one lane per entry.
+// Rows come from a touched-row list (CSR) or the keys of a full-row COO;
+// without a list the CSR kernel scans row_offsets 64 rows per wave.  The step
+// from raw lookups takes its rows from the canonicalisation's segments and
+// shares one launch with the tile combine and the CSR blocks (k_step_lookups).
 #include <hip/hip_ext.h>
 
 #include "common.hpp"
@@ -36,6 +36,22 @@
 
 namespace spopt {
 
+// Nontemporal 16-byte accesses.  An Adam step reads each touched state row once
+// and writes it once; with the nontemporal hint those rows do not displace the
+// lines that the canonicalisation of the next step (and any other work) reads,
+// and their write-back does not fall into that next step.
+typedef float nt_f32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t nt_i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 load_nt(const float* q) {
+    const nt_f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const nt_f32x4*>(q));
+    return make_float4(t.x, t.y, t.z, t.w);
+}
+__device__ __forceinline__ void store_nt(float* q, const float4 x) {
+    __builtin_nontemporal_store((nt_f32x4){x.x, x.y, x.z, x.w}, reinterpret_cast<nt_f32x4*>(q));
+}
+__device__ __forceinline__ void store_nt4(int32_t* q, int32_t x) {
+    __builtin_nontemporal_store((nt_i32x4){x, x, x, x}, reinterpret_cast<nt_i32x4*>(q));
+}
 
 // Per-coordinate ops.  A vector step is split into phases so that a kernel can
 // issue every load of a batch as straight-line code before it computes:
@@ -103,9 +119,9 @@ struct AdamOp {
     }
 
     __device__ __forceinline__ void load(int64_t i, int64_t row, Vec& r) const {
-        r.p = *reinterpret_cast<const float4*>(p + i);
-        r.m = *reinterpret_cast<const float4*>(m + i);
-        r.v = *reinterpret_cast<const float4*>(v + i);
+        r.p = load_nt(p + i);
+        r.m = load_nt(m + i);
+        r.v = load_nt(v + i);
         if (MODE == SPOPT_MODE_DORMANCY && LSROW) {
             const int32_t l = ls[row];  // one address per row: a broadcast
             r.ls = make_int4(l, l, l, l);
@@ -137,13 +153,13 @@ struct AdamOp {
         coord(r.p.w, r.m.w, r.v.w, r.ls.w, x.d1[3], x.d2[3], g.w);
     }
     __device__ __forceinline__ void store(int64_t i, int64_t row, const Vec& r) const {
-        *reinterpret_cast<float4*>(p + i) = r.p;
-        *reinterpret_cast<float4*>(m + i) = r.m;
-        *reinterpret_cast<float4*>(v + i) = r.v;
+        store_nt(p + i, r.p);
+        store_nt(m + i, r.m);
+        store_nt(v + i, r.v);
         if (LSROW)
             ls[row] = a.t;  // every lane of the row stores the same value
         else
-            *reinterpret_cast<int4*>(ls + i) = make_int4(a.t, a.t, a.t, a.t);
+            store_nt4(ls + i, a.t);
     }
     __device__ __forceinline__ int32_t row_last(int64_t row) const {
         return LSROW ? ls[row] : 0;
