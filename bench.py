@@ -86,19 +86,19 @@ UPDATE_SOURCES = ("lazy_optimizer_step_amd/csrc/update.hip",
                   "lazy_optimizer_step_amd/csrc/common.hpp",
                   "lazy_optimizer_step_amd/csrc/csr_full.hpp",
                   "lazy_optimizer_step_amd/csrc/seg_combine.hpp")
-_SHA = "eabbefc0bd05862d4928aec39840bdfc079a5790360997c94a199a0e3183a669"
+_SHA = "fb924673ee4e4dd63f645161355a1fed2c1b8a51e099d49dd4dd835d4bfeee81"
 TRAFFIC = {
     ("table10Mx128_zipf1.05_dormancy", "one_call"): {
-        "sources_sha256": _SHA, "fetch_bytes": 2.0 * 33404.5 * 1024,
-        "write_bytes": 1.0 * 104262.9 * 1024},
+        "sources_sha256": _SHA, "fetch_bytes": 2.0 * 33410.2 * 1024,
+        "write_bytes": 1.0 * 104258.0 * 1024},
     ("table10Mx128_zipf1.05_dormancy", "two_calls"): {
-        "sources_sha256": _SHA, "fetch_bytes": 2.0 * 33770.0 * 1024,
-        "write_bytes": 1.0 * 58425.3 * 1024},
+        "sources_sha256": _SHA, "fetch_bytes": 2.0 * 33767.0 * 1024,
+        "write_bytes": 1.0 * 52105.9 * 1024},
     ("table2Mx256_csr16-64_sgd", "two_calls"): {
-        "sources_sha256": _SHA, "fetch_bytes": 2.0 * 23928.4 * 1024,
+        "sources_sha256": _SHA, "fetch_bytes": 2.0 * 23934.7 * 1024,
         "write_bytes": 1.0 * 23465.3 * 1024},
     ("table2Mx256_csr16-64_dormancy", "two_calls"): {
-        "sources_sha256": _SHA, "fetch_bytes": 2.0 * 40152.5 * 1024,
+        "sources_sha256": _SHA, "fetch_bytes": 2.0 * 40150.2 * 1024,
         "write_bytes": 1.0 * 46930.6 * 1024},
 }
 

@@ -273,14 +273,13 @@ struct SrcCsrTouched {
     int64_t rows;
     __device__ __forceinline__ void get(int64_t k, int64_t& row, int64_t& st, int64_t& len) const {
         row = touched[k];
-        if ((uint64_t)row >= (uint64_t)rows) {
-            len = 0;
-            st = 0;
-            return;
-        }
-        st = ro[row];
-        len = (int64_t)ro[row + 1] - st;
-        if (st < 0 || st + len > (int64_t)ro[rows]) len = 0;  // entries stay in [0, nnz)
+        // Selects rather than an early return, so st and len stay in registers
+        // (an out-of-range id reads ro[0] and ro[1]: a table has at least one row).
+        const bool in = (uint64_t)row < (uint64_t)rows;
+        const int64_t r = in ? row : 0;
+        const int64_t a = ro[r], b = ro[r + 1], nnz = ro[rows];
+        st = in ? a : 0;
+        len = (in && a >= 0 && b <= nnz) ? b - a : 0;  // entries stay in [0, nnz)
     }
     __device__ __forceinline__ int64_t col(int64_t st, int64_t j) const {
         return ci ? (int64_t)ci[st + j] : j;
