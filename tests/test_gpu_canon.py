@@ -165,6 +165,49 @@ def test_out_of_range_in_a_later_pack_chunk(validate):
         assert _run(ids, vals, 1000)[3] == 0
 
 
+@pytest.mark.parametrize("n,key_space,pattern", [
+    (8192, 1_000_000, "one_id"), (8192, 1_000_000, "random"), (8191, 2, "random"),
+    (8193, 1_000_000, "random"), (8192, 1 << 40, "random"), (257, 5000, "sorted_desc"),
+    (4096, 3, "random")])
+def test_lookup_counts_around_four_radix_tiles(n, key_space, pattern):
+    """Lookup counts at and around four 2048-lookup radix tiles (one id only,
+    1-bit and 40-bit keys, ids in descending order): the oracle's keys and
+    counts bit for bit."""
+    rng = np.random.default_rng(n + key_space % 97)
+    if pattern == "one_id":
+        ids = np.full(n, key_space // 3, np.int64)
+    elif pattern == "sorted_desc":
+        ids = np.sort(rng.integers(0, key_space, size=n, dtype=np.int64))[::-1].copy()
+    else:
+        ids = rng.integers(0, key_space, size=n, dtype=np.int64)
+    vals = rng.standard_normal((n, 8)).astype(np.float32)
+    gk, gv, gc, u = _run(ids, vals, key_space)
+    ok, ov, oc = oracle.coo_from_lookups(ids, vals, key_space)
+    assert u == ok.size
+    assert np.array_equal(gk, ok) and np.array_equal(gc, oc)
+    assert_sums_close(gv, ov, ids, ok, oc, vals)
+
+
+@pytest.mark.parametrize("validate", [False, True])
+@pytest.mark.parametrize("where", [0, 4095, 8191])
+def test_out_of_range_within_8192_lookups(validate, where):
+    n = 8192
+    ids = np.arange(n, dtype=np.int64) % 700
+    ids[where] = -5 if where == 4095 else 700
+    vals = np.ones((n, 2), np.float32)
+    if validate:
+        with pytest.raises(L.SparseOptError) as e:
+            _run(ids, vals, 700, validate=True)
+        assert e.value.code == oracle.ERANGE
+    else:
+        assert _run(ids, vals, 700)[3] == 0
+    # the next call on fresh inputs is unaffected
+    ids[where] = 3
+    gk, gv, gc, u = _run(ids, vals, 700)
+    ok, ov, oc = oracle.coo_from_lookups(ids, vals, 700)
+    assert u == ok.size and np.array_equal(gk, ok) and np.array_equal(gc, oc)
+
+
 def test_a_million_lookups():
     """A million lookups: 977 sort tiles and 3907 segment tiles, more than the
     device runs at once, and about 15 chunks of 2048 lookups per pack block."""
