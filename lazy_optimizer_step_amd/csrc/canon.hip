@@ -541,10 +541,6 @@ __device__ __forceinline__ void store_part(double* dst, const double (&r)[V], in
 // Destination of the running sum when lookup j of a chunk closes it.
 enum : int { kFlushNone = 0, kFlushOut = 1, kFlushFirst = 2, kFlushLast = 3 };
 
-// Waits until every vector memory operation this wave issued has completed
-// (vmcnt 0; the export and LDS/scalar counters are left at their maximum).
-__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
 
 // Head count of every segment tile of kSumTile sorted lookups: the lookups
 // whose id differs from their predecessor's, stored with a plain store.  When
@@ -582,9 +578,9 @@ __global__ __launch_bounds__(kSumTile) void k_head_count(const uint64_t* __restr
 //     the distinct id and the segment's first position.
 //  2. Value rows: LPR lanes cover LPR*V consecutive columns of one row
 //     (16-byte loads when V = 4), so one load instruction fetches 64/LPR rows;
-//     all 16 rows of the wave are loaded, the wave waits once (stores share the
-//     vector memory counter, so none is issued before the wait), then adds
-//     them in sorted (= lookup) order: row j to the accumulator of lane group
+//     all 16 rows of the wave are requested before any is used, then added in
+//     sorted (= lookup) order as they arrive (the compiler waits for each load
+//     instruction's rows in turn): row j to the accumulator of lane group
 //     j % (64/LPR); a segment that ends at row j is closed by adding the group
 //     accumulators pairwise across lanes (one fixed order, the same bits on
 //     every lane) unless row j is its only row in the wave.  A segment inside
@@ -749,7 +745,6 @@ __global__ __launch_bounds__(kSumThreads) void k_seg_sum(
             const uint32_t p = (uint32_t)__shfl((int)pos, src, kWave);
             load_row<V>(row[u], vals + (int64_t)p * width, col, width);
         }
-        wait_vmem_all();
         double acc[V];
 #pragma unroll
         for (int v = 0; v < V; ++v) acc[v] = 0.0;
