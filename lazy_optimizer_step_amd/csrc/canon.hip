@@ -541,7 +541,6 @@ __device__ __forceinline__ void store_part(double* dst, const double (&r)[V], in
 // Destination of the running sum when lookup j of a chunk closes it.
 enum : int { kFlushNone = 0, kFlushOut = 1, kFlushFirst = 2, kFlushLast = 3 };
 
-
 // Head count of every segment tile of kSumTile sorted lookups: the lookups
 // whose id differs from their predecessor's, stored with a plain store.  When
 // the tiles are few, k_seg_sum sums the counts of the tiles before its own in
