@@ -209,6 +209,35 @@ def test_against_oracle(kind, cfg):
         assert_state_close(host(a.momentum_buf), o.b, "momentum")
 
 
+@pytest.mark.parametrize("n", [65536, 70001])
+def test_every_lookup_on_one_row(n):
+    """All lookups hit one row: one segment across every segment tile (256 and
+    274 tiles), summed by the combine in 16 runs, then one row updated; against
+    the oracle, and bit for bit against the two calls."""
+    rows, cols = 5000, 128
+    cfg = dict(mode="dormancy")
+    a, b, p0 = _make("adam", rows, cols, 21, cfg)
+    o = oracle.Adam(p0.copy(), **cfg)
+    rng = np.random.default_rng(22)
+    for s in range(2):
+        ids = np.full(n, 1234 + s, np.int64)
+        vals = rng.standard_normal((n, cols)).astype(np.float32)
+        di, dv = dev(ids), dev(vals)
+        got = a.step_lookups(di, dv)
+        csr, counts, U = L.csr_from_lookups(di, dv, rows)
+        b.step(csr)
+        ok, ov, oc = oracle.coo_from_lookups(ids, vals, rows)
+        o.step_coo(ok, ov, width=cols)
+        torch.cuda.synchronize()
+        assert int(host(got[2])[0]) == 1 and int(host(got[1])[0]) == n
+        assert _outputs(*got, cols) == _outputs(csr, counts, U, cols)
+        assert _state(a) == _state(b)
+    assert_state_close(host(a.params), o.p, "params")
+    assert_state_close(host(a.m), o.m, "m")
+    assert_state_close(host(a.v), o.v, "v")
+    assert np.array_equal(host(a.last_step), o.ls)
+
+
 def test_binding_checks_shapes_against_the_handle():
     """The binding sizes and checks every array from the handle's rows and cols,
     so vals of another width are refused before the library is called."""
