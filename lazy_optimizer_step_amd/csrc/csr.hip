@@ -92,8 +92,22 @@ __global__ __launch_bounds__(kRoThreads) void k_row_offsets(
     }
     __syncthreads();
     const int64_t per_entry = (width == 1) ? 1 : cols;
-    for (int64_t r = r0 + threadIdx.x; r < r1; r += kRoThreads)
-        row_offsets[r] = (int32_t)((ka + (int64_t)cnt[r - r0]) * per_entry);
+    // Four offsets per 16-byte store where the block's offsets allow it.  Plain
+    // stores, not nontemporal ones: the update that follows scans these offsets.
+    if ((((uintptr_t)(row_offsets + r0)) & 15u) == 0 && ((r1 - r0) & 3) == 0) {
+        typedef int32_t rx4 __attribute__((ext_vector_type(4)));
+        const int nq = (int)((r1 - r0) >> 2);
+        for (int q = threadIdx.x; q < nq; q += kRoThreads) {
+            const rx4 v = {(int32_t)((ka + (int64_t)cnt[4 * q]) * per_entry),
+                           (int32_t)((ka + (int64_t)cnt[4 * q + 1]) * per_entry),
+                           (int32_t)((ka + (int64_t)cnt[4 * q + 2]) * per_entry),
+                           (int32_t)((ka + (int64_t)cnt[4 * q + 3]) * per_entry)};
+            reinterpret_cast<rx4*>(row_offsets + r0)[q] = v;
+        }
+    } else {
+        for (int64_t r = r0 + threadIdx.x; r < r1; r += kRoThreads)
+            row_offsets[r] = (int32_t)((ka + (int64_t)cnt[r - r0]) * per_entry);
+    }
 }
 
 // Full-row COO -> row_offsets and col_indices in one launch: the first nblk_ci
