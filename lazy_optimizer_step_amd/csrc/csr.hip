@@ -163,20 +163,51 @@ __global__ void k_scalar_cols(const int64_t* __restrict__ idx, const float* __re
     const int64_t after = xl < 0 ? 0 : (int64_t)by_cols.div((uint64_t)xl) / kRoRows + 1;
     for (int64_t b = after + gid; b <= nblk; b += gstride)
         row_offsets[b * kRoRows] = (int32_t)(nnz > 0 ? nnz : 0);
-    for (int64_t k = gid; k < nnz; k += gstride) {
-        const int64_t x = idx[k];
-        const int64_t xp = k > 0 ? idx[k - 1] : -1;
-        // Rows as floor(x / cols); -1 below the first entry (or for a negative
-        // index, which a trusted caller promises not to pass).
-        uint64_t col = 0;
-        const int64_t row = x < 0 ? -1 : (int64_t)by_cols.div((uint64_t)x, &col);
-        const int64_t rowp = xp < 0 ? -1 : (int64_t)by_cols.div((uint64_t)xp);
-        if (ci) ci[k] = x < 0 ? -1 : (int32_t)col;
-        if (vout) vout[k] = vin[k];
-        int64_t b0 = rowp < 0 ? 0 : rowp / kRoRows + 1;
-        int64_t b1 = row < 0 ? -1 : row / kRoRows;
-        if (b1 > nblk) b1 = nblk;
-        for (int64_t b = b0; b <= b1; ++b) row_offsets[b * kRoRows] = (int32_t)k;
+    // Four entries per thread: two 16-byte index loads and one 16-byte column
+    // store where the arrays allow it.
+    const bool vec = ci != nullptr && ((((uintptr_t)idx) | ((uintptr_t)ci)) & 15u) == 0;
+    const int64_t nq = (nnz + 3) / 4;
+    for (int64_t q = gid; q < nq; q += gstride) {
+        const int64_t k0 = 4 * q;
+        int64_t xs[5];
+        xs[0] = k0 > 0 ? idx[k0 - 1] : -1;
+        if (vec && k0 + 4 <= nnz) {
+            const longlong2 a = reinterpret_cast<const longlong2*>(idx + k0)[0];
+            const longlong2 b = reinterpret_cast<const longlong2*>(idx + k0)[1];
+            xs[1] = a.x; xs[2] = a.y; xs[3] = b.x; xs[4] = b.y;
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) xs[j + 1] = k0 + j < nnz ? idx[k0 + j] : -1;
+        }
+        int32_t cs[4];
+        int64_t rowp = xs[0] < 0 ? -1 : (int64_t)by_cols.div((uint64_t)xs[0]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t k = k0 + j;
+            const int64_t x = xs[j + 1];
+            // Rows as floor(x / cols); -1 below the first entry (or for a negative
+            // index, which a trusted caller promises not to pass).
+            uint64_t col = 0;
+            const int64_t row = x < 0 ? -1 : (int64_t)by_cols.div((uint64_t)x, &col);
+            cs[j] = x < 0 ? -1 : (int32_t)col;
+            if (k < nnz) {
+                if (vout) vout[k] = vin[k];
+                int64_t b0 = rowp < 0 ? 0 : rowp / kRoRows + 1;
+                int64_t b1 = row < 0 ? -1 : row / kRoRows;
+                if (b1 > nblk) b1 = nblk;
+                for (int64_t b = b0; b <= b1; ++b) row_offsets[b * kRoRows] = (int32_t)k;
+            }
+            rowp = row;
+        }
+        if (ci) {
+            if (vec && k0 + 4 <= nnz) {
+                reinterpret_cast<int4*>(ci + k0)[0] = make_int4(cs[0], cs[1], cs[2], cs[3]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (k0 + j < nnz) ci[k0 + j] = cs[j];
+            }
+        }
     }
 }
 
@@ -423,7 +454,7 @@ extern "C" int csr_from_coo(const spopt_coo* in, int64_t rows, int64_t cols,
         // Scalar entries: columns, values and the row blocks' first offsets,
         // then the row blocks.
         const FastDiv by_cols = FastDiv::make((uint64_t)cols);
-        k_scalar_cols<<<grid_for(in->nnz, 256), 256, 0, st>>>(
+        k_scalar_cols<<<grid_for((in->nnz + 3) / 4, 256), 256, 0, st>>>(
             in->indices, in->values, in->d_nnz, in->nnz, rows, by_cols, col_indices,
             values == in->values ? nullptr : values, row_offsets);
         SPOPT_LAUNCHED();
