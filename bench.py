@@ -95,7 +95,7 @@ TRAFFIC = {
         "sources_sha256": _SHA, "fetch_bytes": 2.0 * 33767.0 * 1024,
         "write_bytes": 1.0 * 52105.9 * 1024},
     ("table2Mx256_csr16-64_sgd", "two_calls"): {
-        "sources_sha256": _SHA, "fetch_bytes": 2.0 * 23941.2 * 1024,
+        "sources_sha256": _SHA, "fetch_bytes": 2.0 * 23934.0 * 1024,
         "write_bytes": 1.0 * 23465.3 * 1024},
     ("table2Mx256_csr16-64_dormancy", "two_calls"): {
         "sources_sha256": _SHA, "fetch_bytes": 2.0 * 40149.6 * 1024,
