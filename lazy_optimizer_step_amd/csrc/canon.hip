@@ -498,14 +498,17 @@ __device__ __forceinline__ bool tile_exclusive_prefix(uint32_t* words, int64_t t
 // width is a multiple of V and the arrays are V*4-byte aligned, so a lane
 // whose first column is inside the row owns all V of its columns.
 // Straight-line: a lane past the end of the row loads the row's first V
-// columns instead and zeroes them, so loads are never behind a branch.
+// columns instead and zeroes them, so loads are never behind a branch.  The
+// 16-byte form is a nontemporal load: each lookup's row is read once a step,
+// and the hint keeps those rows from displacing lines that are read again.
 template <int V>
 __device__ __forceinline__ void load_row(float (&r)[V], const float* row, int64_t col,
                                          int64_t width) {
     const bool in = col < width;
     const float* src = row + (in ? col : 0);
     if constexpr (V == 4) {
-        const float4 x = *reinterpret_cast<const float4*>(src);
+        typedef float g4 __attribute__((ext_vector_type(4)));
+        const g4 x = __builtin_nontemporal_load(reinterpret_cast<const g4*>(src));
         r[0] = in ? x.x : 0.f; r[1] = in ? x.y : 0.f; r[2] = in ? x.z : 0.f; r[3] = in ? x.w : 0.f;
     } else if constexpr (V == 2) {
         const float2 x = *reinterpret_cast<const float2*>(src);
