@@ -89,16 +89,16 @@ UPDATE_SOURCES = ("lazy_optimizer_step_amd/csrc/update.hip",
 _SHA = "fb924673ee4e4dd63f645161355a1fed2c1b8a51e099d49dd4dd835d4bfeee81"
 TRAFFIC = {
     ("table10Mx128_zipf1.05_dormancy", "one_call"): {
-        "sources_sha256": _SHA, "fetch_bytes": 2.0 * 33409.3 * 1024,
-        "write_bytes": 1.0 * 104261.1 * 1024},
+        "sources_sha256": _SHA, "fetch_bytes": 2.0 * 33409.7 * 1024,
+        "write_bytes": 1.0 * 104262.0 * 1024},
     ("table10Mx128_zipf1.05_dormancy", "two_calls"): {
-        "sources_sha256": _SHA, "fetch_bytes": 2.0 * 33767.0 * 1024,
+        "sources_sha256": _SHA, "fetch_bytes": 2.0 * 33768.9 * 1024,
         "write_bytes": 1.0 * 52105.9 * 1024},
     ("table2Mx256_csr16-64_sgd", "two_calls"): {
-        "sources_sha256": _SHA, "fetch_bytes": 2.0 * 23934.0 * 1024,
+        "sources_sha256": _SHA, "fetch_bytes": 2.0 * 23935.2 * 1024,
         "write_bytes": 1.0 * 23465.3 * 1024},
     ("table2Mx256_csr16-64_dormancy", "two_calls"): {
-        "sources_sha256": _SHA, "fetch_bytes": 2.0 * 40149.6 * 1024,
+        "sources_sha256": _SHA, "fetch_bytes": 2.0 * 40161.6 * 1024,
         "write_bytes": 1.0 * 46930.6 * 1024},
 }
 
